@@ -1,0 +1,224 @@
+/*
+ * libtreeverify -- target-side verification of a speculative draft tree on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The target model checks a whole draft tree in one forward pass ("SpecBlock:
+ * Block-Iterative Speculative Decoding with Dynamic Tree Drafting", Abstract
+ * and App. A.5).  This library implements the data-parallel part of that
+ * pass for one attention layer plus the acceptance step:
+ *
+ *   tv_build_tree_mask   parent array -> packed ancestor-or-self bitmask
+ *   tv_tree_attention    tree-masked GQA attention over the verified-prefix KV
+ *                        (full, or a listed subset of KV blocks) and the tree
+ *   tv_greedy_accept     per-node vocabulary argmax, longest accepted path,
+ *                        accepted length and bonus token
+ *   tv_commit_kv         copy the accepted nodes' K/V rows into the cache
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Tree: n_nodes nodes per sequence, node 0 is the root (the last committed
+ *   token, whose K/V is not yet in the cache), nodes are topologically
+ *   ordered: parents[0] == -1 and 0 <= parents[i] < i.  1 <= n_nodes <= 256.
+ * - Every pointer argument is a device pointer unless stated otherwise.  The
+ *   caller owns every buffer; the library allocates nothing, keeps no state
+ *   between calls (apart from cached device properties) and never
+ *   synchronises the host.  All work is enqueued on `stream` in order.
+ * - Host-checkable problems (null pointers, unsupported sizes, misaligned
+ *   buffers, a workspace that is too small) return a non-zero tv_status and
+ *   enqueue nothing.
+ * - Problems that live in device memory (a malformed parent array, a block id
+ *   outside the prefix, a prefix length outside the cache, a commit that would
+ *   overflow the cache) cannot be seen by the host: the kernels take the
+ *   defined fallback documented with each call and OR the matching TV_DERR_*
+ *   bit into *dev_err when dev_err is not NULL.  The caller clears *dev_err.
+ * - bf16 tensors hold IEEE bfloat16 values; int32/uint32 are little endian.
+ *   Tensor layouts are C-contiguous in the order given.  Every bf16 tensor
+ *   and the cache base pointers must be 16-byte aligned.
+ */
+#ifndef TREEVERIFY_H
+#define TREEVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TV_OK = 0,
+  TV_ERR_NULL = 1,         /* a required pointer is NULL */
+  TV_ERR_SHAPE = 2,        /* a size is out of range or inconsistent */
+  TV_ERR_UNSUPPORTED = 3,  /* head_dim, dtype or alignment not supported */
+  TV_ERR_WORKSPACE = 4,    /* workspace too small or misaligned */
+  TV_ERR_LAUNCH = 5,       /* the HIP runtime refused a launch */
+  TV_ERR_DEVICE = 6        /* no usable HIP device */
+} tv_status;
+
+typedef enum { TV_BF16 = 0, TV_F32 = 1 } tv_dtype;
+
+/* device-side data-error bits, OR-ed into *dev_err */
+#define TV_DERR_BAD_PARENT 1  /* parents[0] != -1 or parents[i] not in [0, i) */
+#define TV_DERR_BAD_BLOCK 2   /* a listed block id < 0, starting at/after prefix_len,
+                                 or n_blocks outside [0, max_blocks] */
+#define TV_DERR_CAPACITY 4    /* prefix_len + accept_len + 1 > cache_capacity */
+#define TV_DERR_BAD_PREFIX 8  /* prefix_len < 0, > cache_capacity or > max_prefix_len */
+#define TV_DERR_BAD_PATH 16   /* accept_len or an accept_path entry out of range */
+
+#define TV_MAX_NODES 256
+
+/*
+ * tv_build_tree_mask -- ancestor-or-self visibility of every tree node.
+ *
+ * Source: SpecBlock App. A.2 "Attention Mask for SpecBlock": a position sees
+ * its on-path ancestors and itself, never positions on other branches (the
+ * verified prefix is visible to all and is handled by tv_tree_attention).
+ *
+ * parents  int32  [batch][n_nodes]
+ * mask     uint32 [batch][n_nodes][W], W = ceil(n_nodes / 32): bit (j % 32) of
+ *          word (j / 32) of row i is set iff node j is node i or an ancestor
+ *          of i.  Bits for j >= n_nodes are zero.
+ * depth    int32  [batch][n_nodes] or NULL: number of edges from the root.
+ * Fallback: a sequence with any malformed parent entry gets self-only rows
+ * and depth 0 everywhere, and TV_DERR_BAD_PARENT is raised.
+ */
+tv_status tv_build_tree_mask(const int32_t* parents, int32_t batch, int32_t n_nodes,
+                             uint32_t* mask, int32_t* depth, int32_t* dev_err,
+                             hipStream_t stream);
+
+/*
+ * tv_tree_attention -- one layer's attention for all tree nodes.
+ *
+ * Sources: SpecBlock App. A.2 (visibility: the verified prefix, the node's
+ * ancestors and itself); SpecPV Sec. 3.2 "Partial Verification" (a selected
+ * subset of KV blocks is attended as one continuous segment).
+ *
+ * For sequence b, node i and query head h (kv head g = h / (Hq / Hkv)) the
+ * visible keys are
+ *   full mode (max_blocks == 0): cache rows 0 .. prefix_len[b]-1;
+ *   partial mode: for t < n_blocks[b], block blk = block_idx[b][t] covers rows
+ *     blk*block_size .. min((blk+1)*block_size, prefix_len[b]) - 1, in list
+ *     order (a block listed twice counts twice);
+ * followed by the tree nodes j whose bit is set in mask[b][i].
+ * out = softmax(scale * q k^T) v over those keys, accumulated in fp32 and
+ * rounded to bf16 (nearest even); lse = natural-log sum of exp(scale q.k).
+ *
+ * Layouts:
+ *   q        bf16 [batch][n_nodes][n_q_heads][head_dim]
+ *   k_tree   bf16 [batch][n_nodes][n_kv_heads][head_dim]    (v_tree the same)
+ *   k_cache  bf16, sequence b at k_cache + b * cache_seq_stride elements, then
+ *            [n_kv_heads][cache_capacity][head_dim]          (v_cache the same)
+ *   prefix_len int32 [batch]; mask as produced by tv_build_tree_mask
+ *   block_idx int32 [batch][max_blocks], n_blocks int32 [batch] (partial mode)
+ *   out      bf16 [batch][n_nodes][n_q_heads][head_dim]
+ *   lse      fp32 [batch][n_nodes][n_q_heads] or NULL
+ * Supported: head_dim 64 or 128, n_q_heads % n_kv_heads == 0,
+ *   n_nodes * (n_q_heads / n_kv_heads) <= 1024.
+ * Fallbacks: a block that is invalid is skipped (TV_DERR_BAD_BLOCK); a
+ *   prefix_len outside [0, min(cache_capacity, max_prefix_len)] is clamped to
+ *   that range (TV_DERR_BAD_PREFIX); a row that sees no key at all (possible
+ *   only with a hand-made mask) gets out = 0 and lse = -inf.
+ * Workspace: at least tv_tree_attention_workspace_size(desc) bytes, 256-byte
+ *   aligned, contents undefined on entry and on exit.
+ */
+typedef struct {
+  int32_t batch, n_nodes, n_q_heads, n_kv_heads, head_dim;
+  int32_t cache_capacity;   /* rows per (sequence, kv head) in the cache */
+  int32_t max_prefix_len;   /* host-side upper bound of prefix_len[] (grid sizing) */
+  int32_t block_size;       /* partial mode: tokens per KV block (>= 1) */
+  int32_t max_blocks;       /* partial mode: columns of block_idx; 0 = full mode */
+  float softmax_scale;      /* <= 0 means 1 / sqrt(head_dim) */
+  int32_t num_splits;       /* prefix splits per (sequence, kv head); 0 = automatic */
+  int64_t cache_seq_stride; /* elements between sequences; 0 = n_kv_heads*capacity*head_dim */
+} tv_attn_desc;
+
+typedef struct {
+  const void* q;
+  const void* k_tree;
+  const void* v_tree;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* prefix_len;
+  const uint32_t* mask;
+  const int32_t* block_idx; /* NULL in full mode */
+  const int32_t* n_blocks;  /* NULL in full mode */
+  void* out;
+  float* lse;               /* may be NULL */
+} tv_attn_ptrs;
+
+size_t tv_tree_attention_workspace_size(const tv_attn_desc* desc);
+/* number of prefix splits the call will use for this descriptor (>= 1) */
+int32_t tv_tree_attention_num_splits(const tv_attn_desc* desc);
+tv_status tv_tree_attention(const tv_attn_desc* desc, const tv_attn_ptrs* ptrs, void* workspace,
+                            size_t workspace_bytes, int32_t* dev_err, hipStream_t stream);
+
+/*
+ * tv_greedy_accept -- temperature-0 acceptance of a verified tree.
+ *
+ * Sources: SpecBlock Sec. 4 (greedy decoding at T = 0), App. A.5 (the longest
+ * accepted prefix is committed), App. E (the target adds one bonus token);
+ * papernotes on SpecBlock, key design 3 (the valid-prefix recurrence, whose
+ * tree form is the acceptance rule below).
+ *
+ * logits        [batch][n_nodes] rows of `vocab` values (bf16 or fp32), row
+ *               r = b*n_nodes + i starting at element r*row_stride
+ *               (row_stride >= vocab)
+ * parents       int32 [batch][n_nodes]
+ * draft_tokens  int32 [batch][n_nodes] (entry 0 of each sequence is ignored;
+ *               ids outside [0, vocab) never match)
+ * target_argmax int32 [batch][n_nodes]: lowest index of the largest logit
+ *               (values compare as reals: -0 == +0)
+ * accept_len    int32 [batch]: depth of the path's last node (drafts accepted)
+ * accept_path   int32 [batch][n_nodes]: node ids root first, -1 padded
+ * bonus_token   int32 [batch]: target_argmax of the path's last node
+ * Rule: node i >= 1 is accepted iff its parent is accepted and
+ *   draft_tokens[i] == target_argmax[parent]; the root is accepted; the path
+ *   ends at the deepest accepted node, the lowest index among equal depths.
+ * Fallback: a malformed parent array gives accept_len 0, path [0, -1, ...],
+ *   bonus = target_argmax of the root, and TV_DERR_BAD_PARENT.
+ * NaN logits are outside the contract (result unspecified).
+ * Workspace: tv_greedy_accept_workspace_size(...) bytes, 256-byte aligned.
+ */
+size_t tv_greedy_accept_workspace_size(int32_t batch, int32_t n_nodes, int64_t vocab);
+tv_status tv_greedy_accept(const void* logits, tv_dtype dtype, int64_t vocab, int64_t row_stride,
+                           const int32_t* parents, const int32_t* draft_tokens, int32_t batch,
+                           int32_t n_nodes, int32_t* target_argmax, int32_t* accept_len,
+                           int32_t* accept_path, int32_t* bonus_token, void* workspace,
+                           size_t workspace_bytes, int32_t* dev_err, hipStream_t stream);
+
+/*
+ * tv_commit_kv -- append the accepted path's K/V to the cache.
+ *
+ * Source: SpecBlock App. A.5 (commit the longest accepted prefix before the
+ * next iteration) and App. A.2 (the prefix holds previously committed
+ * positions).
+ *
+ * For r = 0 .. accept_len[b] and every kv head h:
+ *   k_cache[b][h][prefix_len[b] + r] = k_tree[b][accept_path[b][r]][h]  (same for v)
+ * then new_prefix_len[b] = prefix_len[b] + accept_len[b] + 1.  Rows are copied
+ * bit for bit; no other cache row is touched.  new_prefix_len may alias
+ * prefix_len.  Layouts as for tv_tree_attention.
+ * Fallback: if the commit would overflow cache_capacity (TV_DERR_CAPACITY),
+ *   prefix_len is out of range (TV_DERR_BAD_PREFIX), or accept_len / a path
+ *   entry is out of range (TV_DERR_BAD_PATH), nothing is written for that
+ *   sequence and new_prefix_len[b] = prefix_len[b].
+ */
+tv_status tv_commit_kv(const void* k_tree, const void* v_tree, const int32_t* accept_path,
+                       const int32_t* accept_len, const int32_t* prefix_len,
+                       int32_t* new_prefix_len, void* k_cache, void* v_cache,
+                       int64_t cache_seq_stride, int32_t cache_capacity, int32_t batch,
+                       int32_t n_nodes, int32_t n_kv_heads, int32_t head_dim, int32_t* dev_err,
+                       hipStream_t stream);
+
+/* human-readable name of a status code (static storage) */
+const char* tv_status_string(tv_status status);
+/* library version: major * 10000 + minor * 100 + patch */
+int32_t tv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREEVERIFY_H */

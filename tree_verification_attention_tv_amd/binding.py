@@ -1,0 +1,278 @@
+"""ctypes binding of libtreeverify for torch tensors.
+
+Argument marshalling only: every step runs in the HIP library.  torch
+supplies device memory (outputs and workspaces are allocated with torch) and
+the current stream.  If the library is missing or a tensor is not on a GPU
+the call raises -- there is no CPU fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtreeverify.so")
+_lock = threading.Lock()
+_lib = None
+
+TV_BF16, TV_F32 = 0, 1
+DERR_BAD_PARENT, DERR_BAD_BLOCK, DERR_CAPACITY, DERR_BAD_PREFIX, DERR_BAD_PATH = 1, 2, 4, 8, 16
+MAX_NODES = 256
+
+
+class TVError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {status_string(status)}")
+        self.status = status
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_nodes", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("cache_capacity", ctypes.c_int32), ("max_prefix_len", ctypes.c_int32),
+        ("block_size", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float), ("num_splits", ctypes.c_int32),
+        ("cache_seq_stride", ctypes.c_int64),
+    ]
+
+
+class AttnPtrs(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k_tree", ctypes.c_void_p), ("v_tree", ctypes.c_void_p),
+        ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("prefix_len", ctypes.c_void_p), ("mask", ctypes.c_void_p),
+        ("block_idx", ctypes.c_void_p), ("n_blocks", ctypes.c_void_p),
+        ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+    ]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtreeverify.so (built in-tree); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise RuntimeError(
+                    f"{_LIB_PATH} is not built; run `python -m "
+                    "tree_verification_attention_tv_amd.build` (hipcc, gfx950)")
+            L = ctypes.CDLL(_LIB_PATH)
+            vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+            L.tv_build_tree_mask.argtypes = [vp, i32, i32, vp, vp, vp, vp]
+            L.tv_build_tree_mask.restype = i32
+            L.tv_tree_attention_workspace_size.argtypes = [ctypes.POINTER(AttnDesc)]
+            L.tv_tree_attention_workspace_size.restype = sz
+            L.tv_tree_attention_num_splits.argtypes = [ctypes.POINTER(AttnDesc)]
+            L.tv_tree_attention_num_splits.restype = i32
+            L.tv_tree_attention.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(AttnPtrs),
+                                            vp, sz, vp, vp]
+            L.tv_tree_attention.restype = i32
+            L.tv_greedy_accept_workspace_size.argtypes = [i32, i32, i64]
+            L.tv_greedy_accept_workspace_size.restype = sz
+            L.tv_greedy_accept.argtypes = [vp, i32, i64, i64, vp, vp, i32, i32, vp, vp, vp, vp,
+                                           vp, sz, vp, vp]
+            L.tv_greedy_accept.restype = i32
+            L.tv_commit_kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32,
+                                       i32, vp, vp]
+            L.tv_commit_kv.restype = i32
+            L.tv_status_string.argtypes = [i32]
+            L.tv_status_string.restype = ctypes.c_char_p
+            L.tv_version.argtypes = []
+            L.tv_version.restype = i32
+            _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().tv_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(lib().tv_version())
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _on_gpu(name, t, dtype=None, contiguous=True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device}); there is no CPU path")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _check(fn, status):
+    if status != 0:
+        raise TVError(fn, status)
+
+
+def _err_ptr(dev_err):
+    if dev_err is None:
+        return None
+    _on_gpu("dev_err", dev_err, torch.int32)
+    return _ptr(dev_err)
+
+
+# ---------------------------------------------------------------------------
+# public calls
+# ---------------------------------------------------------------------------
+
+def build_tree_mask(parents: torch.Tensor, *, dev_err=None, with_depth=True):
+    """parents int32 [B][N] -> (mask int32 [B][N][W] holding uint32 bit
+    patterns, depth int32 [B][N] or None)."""
+    _on_gpu("parents", parents, torch.int32)
+    bsz, n = parents.shape
+    w = (n + 31) // 32
+    mask = torch.empty((bsz, n, w), dtype=torch.int32, device=parents.device)
+    depth = torch.empty((bsz, n), dtype=torch.int32, device=parents.device) if with_depth else None
+    _check("tv_build_tree_mask", lib().tv_build_tree_mask(
+        _ptr(parents), bsz, n, _ptr(mask), _ptr(depth), _err_ptr(dev_err), _stream(parents.device)))
+    return mask, depth
+
+
+def attn_desc(q, k_cache, *, max_prefix_len, block_size=0, max_blocks=0, scale=0.0,
+              num_splits=0) -> AttnDesc:
+    bsz, n, hq, d = q.shape
+    _, hkv, cap, d2 = k_cache.shape
+    if d2 != d:
+        raise ValueError("head_dim of q and the cache differ")
+    return AttnDesc(batch=bsz, n_nodes=n, n_q_heads=hq, n_kv_heads=hkv, head_dim=d,
+                    cache_capacity=cap, max_prefix_len=int(max_prefix_len),
+                    block_size=int(block_size), max_blocks=int(max_blocks),
+                    softmax_scale=float(scale), num_splits=int(num_splits),
+                    cache_seq_stride=int(k_cache.stride(0)))
+
+
+def attention_workspace_size(desc: AttnDesc) -> int:
+    return int(lib().tv_tree_attention_workspace_size(ctypes.byref(desc)))
+
+
+def attention_num_splits(desc: AttnDesc) -> int:
+    return int(lib().tv_tree_attention_num_splits(ctypes.byref(desc)))
+
+
+def tree_attention(q, k_cache, v_cache, k_tree, v_tree, prefix_len, mask, *, max_prefix_len,
+                   block_idx=None, n_blocks=None, block_size=0, scale=0.0, num_splits=0,
+                   want_lse=False, out=None, lse=None, workspace=None, dev_err=None):
+    """bf16 tree-masked GQA attention.  Returns out (and lse if asked)."""
+    bf = torch.bfloat16
+    _on_gpu("q", q, bf)
+    _on_gpu("k_cache", k_cache, bf)
+    _on_gpu("v_cache", v_cache, bf)
+    _on_gpu("k_tree", k_tree, bf)
+    _on_gpu("v_tree", v_tree, bf)
+    _on_gpu("prefix_len", prefix_len, torch.int32)
+    _on_gpu("mask", mask, torch.int32)
+    if v_cache.shape != k_cache.shape or v_cache.stride() != k_cache.stride():
+        raise ValueError("k_cache and v_cache must have the same shape and strides")
+    partial = block_idx is not None
+    if partial:
+        _on_gpu("block_idx", block_idx, torch.int32)
+        _on_gpu("n_blocks", n_blocks, torch.int32)
+    desc = attn_desc(q, k_cache, max_prefix_len=max_prefix_len,
+                     block_size=block_size if partial else 0,
+                     max_blocks=block_idx.shape[1] if partial else 0,
+                     scale=scale, num_splits=num_splits)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    ws_bytes = attention_workspace_size(desc)
+    if ws_bytes == 0:
+        raise TVError("tv_tree_attention_workspace_size", 2)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ptrs = AttnPtrs(q=q.data_ptr(), k_tree=k_tree.data_ptr(), v_tree=v_tree.data_ptr(),
+                    k_cache=k_cache.data_ptr(), v_cache=v_cache.data_ptr(),
+                    prefix_len=prefix_len.data_ptr(), mask=mask.data_ptr(),
+                    block_idx=block_idx.data_ptr() if partial else None,
+                    n_blocks=n_blocks.data_ptr() if partial else None,
+                    out=out.data_ptr(), lse=lse.data_ptr() if lse is not None else None)
+    _check("tv_tree_attention", lib().tv_tree_attention(
+        ctypes.byref(desc), ctypes.byref(ptrs), _ptr(workspace), workspace.numel(),
+        _err_ptr(dev_err), _stream(q.device)))
+    return (out, lse) if want_lse else out
+
+
+def accept_workspace_size(batch, n_nodes, vocab) -> int:
+    return int(lib().tv_greedy_accept_workspace_size(int(batch), int(n_nodes), int(vocab)))
+
+
+def greedy_accept(logits, parents, draft_tokens, *, vocab=None, workspace=None, dev_err=None,
+                  outputs=None):
+    """logits [B][N][V] (bf16 or fp32; rows may be strided) ->
+    (target_argmax [B][N], accept_len [B], accept_path [B][N], bonus [B]), int32."""
+    _on_gpu("logits", logits, (torch.bfloat16, torch.float32), contiguous=False)
+    _on_gpu("parents", parents, torch.int32)
+    _on_gpu("draft_tokens", draft_tokens, torch.int32)
+    bsz, n = parents.shape
+    if logits.shape[:2] != (bsz, n) or logits.stride(2) != 1 or \
+            logits.stride(0) != n * logits.stride(1):
+        raise ValueError("logits must be [B][N][V] with unit vocab stride and uniform row stride")
+    v = logits.shape[2] if vocab is None else int(vocab)
+    dt = TV_BF16 if logits.dtype == torch.bfloat16 else TV_F32
+    dev = parents.device
+    if outputs is None:
+        outputs = (torch.empty((bsz, n), dtype=torch.int32, device=dev),
+                   torch.empty((bsz,), dtype=torch.int32, device=dev),
+                   torch.empty((bsz, n), dtype=torch.int32, device=dev),
+                   torch.empty((bsz,), dtype=torch.int32, device=dev))
+    amax, alen, path, bonus = outputs
+    ws_bytes = accept_workspace_size(bsz, n, v)
+    if ws_bytes == 0:
+        raise TVError("tv_greedy_accept_workspace_size", 2)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    _check("tv_greedy_accept", lib().tv_greedy_accept(
+        _ptr(logits), dt, v, int(logits.stride(1)), _ptr(parents), _ptr(draft_tokens), bsz, n,
+        _ptr(amax), _ptr(alen), _ptr(path), _ptr(bonus), _ptr(workspace), workspace.numel(),
+        _err_ptr(dev_err), _stream(dev)))
+    return amax, alen, path, bonus
+
+
+def commit_kv(k_tree, v_tree, accept_path, accept_len, prefix_len, k_cache, v_cache, *,
+              new_prefix_len=None, dev_err=None):
+    """Append the accepted rows to the caches in place; returns new_prefix_len
+    (a fresh tensor unless one is given -- it may be prefix_len itself)."""
+    bf = torch.bfloat16
+    for name, t in (("k_tree", k_tree), ("v_tree", v_tree)):
+        _on_gpu(name, t, bf)
+    _on_gpu("k_cache", k_cache, bf, contiguous=False)
+    _on_gpu("v_cache", v_cache, bf, contiguous=False)
+    for name, t in (("accept_path", accept_path), ("accept_len", accept_len),
+                    ("prefix_len", prefix_len)):
+        _on_gpu(name, t, torch.int32)
+    bsz, hkv, cap, d = k_cache.shape
+    if k_cache.stride()[1:] != (cap * d, d, 1) or v_cache.stride() != k_cache.stride():
+        raise ValueError("caches must be [B][Hkv][cap][D] with contiguous rows per sequence")
+    n = k_tree.shape[1]
+    if new_prefix_len is None:
+        new_prefix_len = torch.empty_like(prefix_len)
+    _check("tv_commit_kv", lib().tv_commit_kv(
+        _ptr(k_tree), _ptr(v_tree), _ptr(accept_path), _ptr(accept_len), _ptr(prefix_len),
+        _ptr(new_prefix_len), _ptr(k_cache), _ptr(v_cache), int(k_cache.stride(0)), cap, bsz,
+        n, hkv, d, _err_ptr(dev_err), _stream(k_cache.device)))
+    return new_prefix_len

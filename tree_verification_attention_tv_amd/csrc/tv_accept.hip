@@ -1,0 +1,271 @@
+// Greedy (temperature-0) acceptance of a verified draft tree.
+//
+// Sources: SpecBlock Sec. 4 (greedy decoding), App. A.5 (longest accepted
+// prefix is committed), App. E (one bonus token from the target); papernotes
+// on SpecBlock, key design 3 (valid-prefix recurrence: a position stays
+// valid only while every earlier prediction matched the target's argmax).
+//
+// Two kernels:
+//  1. vocab_argmax_kernel: one workgroup per (row chunk, logits row).  Each
+//     thread streams 16-byte vectors of its chunk, keeps the first index of
+//     its running maximum, and the workgroup reduces (value, index) pairs
+//     with "larger value, then smaller index" -- a total order, so the
+//     result does not depend on the reduction order.  Partials go to the
+//     workspace.  This is the HBM-bound part (B*N*V logits).
+//  2. path_walk_kernel: one workgroup per sequence.  Thread i finishes row
+//     i's argmax from the partials, then walks from node i to the root
+//     checking draft[j] == argmax[parent(j)] on every edge; the deepest
+//     accepted node (lowest index on ties) is found with one max-reduction
+//     of depth * 65536 + (65535 - i), and its root path is written out.
+#include "tv_internal.h"
+
+#include <float.h>
+
+namespace tv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;  // 16-byte vectors per thread per chunk
+
+struct ValIdx {
+  float v;
+  int i;
+};
+
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+__device__ __forceinline__ ValIdx wave_argmax(ValIdx a) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(a.v, off);
+    const int oi = __shfl_xor(a.i, off);
+    if (better(ov, oi, a.v, a.i)) {
+      a.v = ov;
+      a.i = oi;
+    }
+  }
+  return a;
+}
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T x);
+template <>
+__device__ __forceinline__ float to_f32<bf16>(bf16 x) {
+  return (float)x;
+}
+template <>
+__device__ __forceinline__ float to_f32<float>(float x) {
+  return x;
+}
+
+// VEC elements of T per 16-byte load
+template <typename T, bool kVector>
+__global__ __launch_bounds__(kThreads) void vocab_argmax_kernel(const T* __restrict__ logits,
+                                                               int64_t vocab, int64_t row_stride,
+                                                               int64_t chunk_len, int chunks,
+                                                               float* __restrict__ part_v,
+                                                               int* __restrict__ part_i) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int chunk = blockIdx.x;
+  const int64_t row = blockIdx.y;
+  const T* src = logits + row * row_stride;
+  const int64_t begin = (int64_t)chunk * chunk_len;
+  int64_t end = begin + chunk_len;
+  if (end > vocab) end = vocab;
+
+  float bv = -INFINITY;
+  int bi = INT32_MAX;
+  if (kVector) {
+    typedef T vec_t __attribute__((ext_vector_type(VEC)));
+    // chunk_len is a multiple of kThreads * VEC; only the last chunk is ragged
+    for (int64_t base = begin + (int64_t)threadIdx.x * VEC; base < end;
+         base += (int64_t)kThreads * VEC) {
+      if (base + VEC <= end) {
+        const vec_t x = *reinterpret_cast<const vec_t*>(src + base);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float f = to_f32<T>(x[e]);
+          if (f > bv || bi == INT32_MAX) {
+            bv = f;
+            bi = (int)(base + e);
+          }
+        }
+      } else {
+        for (int64_t k = base; k < end; ++k) {
+          const float f = to_f32<T>(src[k]);
+          if (f > bv || bi == INT32_MAX) {
+            bv = f;
+            bi = (int)k;
+          }
+        }
+      }
+    }
+  } else {
+    for (int64_t k = begin + threadIdx.x; k < end; k += kThreads) {
+      const float f = to_f32<T>(src[k]);
+      if (f > bv || bi == INT32_MAX) {
+        bv = f;
+        bi = (int)k;
+      }
+    }
+  }
+
+  ValIdx a = wave_argmax(ValIdx{bv, bi});
+  __shared__ float sv[kThreads / kWave];
+  __shared__ int si[kThreads / kWave];
+  const int wave = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    sv[wave] = a.v;
+    si[wave] = a.i;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kThreads / kWave; ++w)
+      if (better(sv[w], si[w], a.v, a.i)) {
+        a.v = sv[w];
+        a.i = si[w];
+      }
+    part_v[row * chunks + chunk] = a.v;
+    part_i[row * chunks + chunk] = a.i;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void path_walk_kernel(
+    const float* __restrict__ part_v, const int* __restrict__ part_i, int chunks,
+    const int32_t* __restrict__ parents, const int32_t* __restrict__ draft, int n,
+    int32_t* __restrict__ target_argmax, int32_t* __restrict__ accept_len,
+    int32_t* __restrict__ accept_path, int32_t* __restrict__ bonus, int32_t* __restrict__ dev_err) {
+  __shared__ int par[TV_MAX_NODES];
+  __shared__ int amax[TV_MAX_NODES];
+  __shared__ int dtok[TV_MAX_NODES];
+  __shared__ int bad;
+  __shared__ unsigned red[kThreads / kWave];
+
+  const int b = blockIdx.x;
+  const int i = threadIdx.x;
+  if (i == 0) bad = 0;
+  __syncthreads();
+  if (i < n) {
+    const int64_t row = (int64_t)b * n + i;
+    float bv = part_v[row * chunks];
+    int bi = part_i[row * chunks];
+    for (int c = 1; c < chunks; ++c) {
+      const float v = part_v[row * chunks + c];
+      const int k = part_i[row * chunks + c];
+      if (better(v, k, bv, bi)) {
+        bv = v;
+        bi = k;
+      }
+    }
+    amax[i] = bi;
+    target_argmax[row] = bi;
+    const int p = parents[row];
+    par[i] = p;
+    dtok[i] = draft[row];
+    const bool ok = (i == 0) ? (p == -1) : (p >= 0 && p < i);
+    if (!ok) bad = 1;
+  }
+  __syncthreads();
+
+  // key = depth << 16 | (0xFFFF - i) for accepted nodes, 0 otherwise; the
+  // root is always accepted so the maximum is never 0.
+  unsigned key = 0;
+  if (i < n) {
+    if (bad) {
+      key = (i == 0) ? 0xFFFFu : 0u;
+    } else {
+      bool acc = true;
+      int d = 0;
+      for (int j = i; par[j] >= 0; j = par[j]) {
+        acc = acc && (dtok[j] == amax[par[j]]);
+        ++d;
+      }
+      if (acc) key = ((unsigned)d << 16) | (unsigned)(0xFFFF - i);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const unsigned o = __shfl_xor(key, off);
+    key = o > key ? o : key;
+  }
+  if ((i & (kWave - 1)) == 0) red[i / kWave] = key;
+  __syncthreads();
+  unsigned best = red[0];
+  for (int w = 1; w < kThreads / kWave; ++w) best = red[w] > best ? red[w] : best;
+  const int end_node = 0xFFFF - (int)(best & 0xFFFFu);
+  const int depth = (int)(best >> 16);
+
+  int32_t* path = accept_path + (int64_t)b * n;
+  if (i < n && i > depth) path[i] = -1;
+  if (i == 0) {
+    int j = end_node;
+    for (int k = depth; k >= 0; --k) {
+      path[k] = j;
+      j = par[j];
+    }
+    accept_len[b] = depth;
+    bonus[b] = amax[end_node];
+    if (bad) raise_err(dev_err, TV_DERR_BAD_PARENT);
+  }
+}
+
+}  // namespace
+
+AcceptPlan plan_accept(int batch, int n, int64_t vocab) {
+  AcceptPlan p;
+  // ~32 KB of bf16 per workgroup: enough bytes in flight per CU without
+  // starving rows with few chunks.
+  const int64_t per_pass = (int64_t)kThreads * 8;
+  int64_t chunk = per_pass * kUnroll;
+  if (chunk > vocab) chunk = ((vocab + per_pass - 1) / per_pass) * per_pass;
+  if (chunk < per_pass) chunk = per_pass;
+  p.chunk_len = chunk;
+  p.chunks = (int)((vocab + chunk - 1) / chunk);
+  const size_t rows = (size_t)batch * n;
+  p.ws_bytes = rows * p.chunks * (sizeof(float) + sizeof(int)) + 256;
+  return p;
+}
+
+hipError_t launch_accept(const void* logits, tv_dtype dt, int64_t vocab, int64_t row_stride,
+                         const int32_t* parents, const int32_t* draft, int batch, int n,
+                         int32_t* target_argmax, int32_t* accept_len, int32_t* accept_path,
+                         int32_t* bonus, void* workspace, const AcceptPlan& plan,
+                         int32_t* dev_err, hipStream_t stream) {
+  const size_t rows = (size_t)batch * n;
+  float* part_v = reinterpret_cast<float*>(workspace);
+  int* part_i = reinterpret_cast<int*>(
+      reinterpret_cast<char*>(workspace) + ((rows * plan.chunks * sizeof(float) + 255) / 256) * 256);
+  const dim3 grid(plan.chunks, (unsigned)rows);
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(logits);
+  if (dt == TV_BF16) {
+    const bool vec = (addr % 16 == 0) && (row_stride % 8 == 0);
+    if (vec)
+      hipLaunchKernelGGL((vocab_argmax_kernel<bf16, true>), grid, dim3(kThreads), 0, stream,
+                         (const bf16*)logits, vocab, row_stride, plan.chunk_len, plan.chunks,
+                         part_v, part_i);
+    else
+      hipLaunchKernelGGL((vocab_argmax_kernel<bf16, false>), grid, dim3(kThreads), 0, stream,
+                         (const bf16*)logits, vocab, row_stride, plan.chunk_len, plan.chunks,
+                         part_v, part_i);
+  } else {
+    const bool vec = (addr % 16 == 0) && (row_stride % 4 == 0);
+    if (vec)
+      hipLaunchKernelGGL((vocab_argmax_kernel<float, true>), grid, dim3(kThreads), 0, stream,
+                         (const float*)logits, vocab, row_stride, plan.chunk_len, plan.chunks,
+                         part_v, part_i);
+    else
+      hipLaunchKernelGGL((vocab_argmax_kernel<float, false>), grid, dim3(kThreads), 0, stream,
+                         (const float*)logits, vocab, row_stride, plan.chunk_len, plan.chunks,
+                         part_v, part_i);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(path_walk_kernel, dim3(batch), dim3(kThreads), 0, stream, part_v, part_i,
+                     plan.chunks, parents, draft, n, target_argmax, accept_len, accept_path, bonus,
+                     dev_err);
+  return hipGetLastError();
+}
+
+}  // namespace tv

@@ -1,0 +1,91 @@
+// Commit of the accepted path's K/V rows into the cache (SpecBlock App. A.5:
+// the longest accepted prefix is committed before the next iteration).
+//
+// One workgroup per sequence copies (accept_len + 1) * Hkv * 2 rows with
+// 16-byte vector moves.  The sequence's prefix length is read once by
+// thread 0 before any write, and the new length is written by the same
+// thread after the copy, so new_prefix_len may alias prefix_len.
+#include "tv_internal.h"
+
+namespace tv {
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void commit_kernel(
+    const uint4* __restrict__ k_tree, const uint4* __restrict__ v_tree,
+    const int32_t* __restrict__ path, const int32_t* __restrict__ accept_len,
+    const int32_t* prefix_len, int32_t* new_prefix_len, uint4* __restrict__ k_cache,
+    uint4* __restrict__ v_cache, int64_t seq_stride_vec, int cap, int n, int hkv, int vec_per_row,
+    int32_t* __restrict__ dev_err) {
+  __shared__ int s_prefix, s_len, s_ok;
+  __shared__ int s_node[TV_MAX_NODES];
+  const int b = blockIdx.x;
+  const int t = threadIdx.x;
+  if (t == 0) {
+    const int p = prefix_len[b];
+    const int a = accept_len[b];
+    int ok = 1;
+    if (p < 0 || p > cap) {
+      raise_err(dev_err, TV_DERR_BAD_PREFIX);
+      ok = 0;
+    } else if (a < 0 || a >= n) {
+      raise_err(dev_err, TV_DERR_BAD_PATH);
+      ok = 0;
+    } else if ((int64_t)p + a + 1 > cap) {
+      raise_err(dev_err, TV_DERR_CAPACITY);
+      ok = 0;
+    }
+    s_prefix = p;
+    s_len = a;
+    s_ok = ok;
+  }
+  __syncthreads();
+  const int a = s_len;
+  if (s_ok && t <= a) {
+    const int node = path[(int64_t)b * n + t];
+    s_node[t] = node;
+    if (node < 0 || node >= n) {
+      raise_err(dev_err, TV_DERR_BAD_PATH);
+      s_ok = 0;  // benign race: every writer stores 0
+    }
+  }
+  __syncthreads();
+  if (s_ok) {
+    const int p = s_prefix;
+    const int per_row = vec_per_row;
+    const int items = (a + 1) * hkv * per_row;
+    const uint4* kt = k_tree + (int64_t)b * n * hkv * per_row;
+    const uint4* vt = v_tree + (int64_t)b * n * hkv * per_row;
+    uint4* kc = k_cache + b * seq_stride_vec;
+    uint4* vc = v_cache + b * seq_stride_vec;
+    for (int it = t; it < items; it += kThreads) {
+      const int c = it % per_row;
+      const int rh = it / per_row;
+      const int h = rh % hkv;
+      const int r = rh / hkv;
+      const int64_t src = ((int64_t)s_node[r] * hkv + h) * per_row + c;
+      const int64_t dst = ((int64_t)h * cap + p + r) * per_row + c;
+      kc[dst] = kt[src];
+      vc[dst] = vt[src];
+    }
+  }
+  if (t == 0) new_prefix_len[b] = s_ok ? s_prefix + a + 1 : s_prefix;
+}
+
+}  // namespace
+
+hipError_t launch_commit(const void* k_tree, const void* v_tree, const int32_t* path,
+                         const int32_t* accept_len, const int32_t* prefix_len,
+                         int32_t* new_prefix_len, void* k_cache, void* v_cache,
+                         int64_t seq_stride, int cap, int batch, int n, int hkv, int d,
+                         int32_t* dev_err, hipStream_t stream) {
+  const int vec_per_row = d / 8;  // 8 bf16 per 16-byte vector
+  hipLaunchKernelGGL(commit_kernel, dim3(batch), dim3(kThreads), 0, stream,
+                     (const uint4*)k_tree, (const uint4*)v_tree, path, accept_len, prefix_len,
+                     new_prefix_len, (uint4*)k_cache, (uint4*)v_cache, seq_stride / 8, cap, n, hkv,
+                     vec_per_row, dev_err);
+  return hipGetLastError();
+}
+
+}  // namespace tv

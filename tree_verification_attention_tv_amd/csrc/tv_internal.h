@@ -1,0 +1,69 @@
+// Internal declarations shared by the libtreeverify HIP sources (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "treeverify.h"
+
+namespace tv {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// launch wrappers implemented in the kernel sources; each returns the HIP
+// launch status.  Arguments have been validated by the API layer.
+// ---------------------------------------------------------------------------
+
+hipError_t launch_build_mask(const int32_t* parents, int batch, int n, uint32_t* mask,
+                             int32_t* depth, int32_t* dev_err, hipStream_t stream);
+
+struct AttnPlan {
+  int rows;          // query rows per (sequence, kv head) = n_nodes * group
+  int row_blocks;    // 16-row MFMA blocks per wave (1..4)
+  int row_groups;    // workgroups sharing one (sequence, kv head, split) in rows
+  int splits;        // prefix splits (the tree block is one more split)
+  int chunk;         // prefix slots per split (multiple of the 32-token tile)
+  int prefix_slots;  // upper bound of prefix slots per sequence
+  size_t ws_o_bytes, ws_ml_bytes;
+};
+
+AttnPlan plan_attention(const tv_attn_desc& d, int cu_count);
+
+hipError_t launch_attention(const tv_attn_desc& d, const AttnPlan& plan, const tv_attn_ptrs& p,
+                            void* workspace, int32_t* dev_err, hipStream_t stream);
+
+struct AcceptPlan {
+  int chunks;        // vocabulary chunks per row
+  int64_t chunk_len; // elements per chunk
+  size_t ws_bytes;
+};
+
+AcceptPlan plan_accept(int batch, int n, int64_t vocab);
+
+hipError_t launch_accept(const void* logits, tv_dtype dt, int64_t vocab, int64_t row_stride,
+                         const int32_t* parents, const int32_t* draft, int batch, int n,
+                         int32_t* target_argmax, int32_t* accept_len, int32_t* accept_path,
+                         int32_t* bonus, void* workspace, const AcceptPlan& plan,
+                         int32_t* dev_err, hipStream_t stream);
+
+hipError_t launch_commit(const void* k_tree, const void* v_tree, const int32_t* path,
+                         const int32_t* accept_len, const int32_t* prefix_len,
+                         int32_t* new_prefix_len, void* k_cache, void* v_cache,
+                         int64_t seq_stride, int cap, int batch, int n, int hkv, int d,
+                         int32_t* dev_err, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// small device helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void raise_err(int32_t* dev_err, int bits) {
+  if (dev_err) atomicOr(dev_err, bits);
+}
+
+}  // namespace tv
