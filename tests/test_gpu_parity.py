@@ -336,3 +336,35 @@ def test_full_step_8b(workloads):
     rk, rv, rp = oracle.commit_kv(wl.k_tree, wl.v_tree, r_path, r_alen, wl.prefix_len,
                                   wl.k_cache, wl.v_cache)
     assert np.array_equal(bf16_host(kc), rk) and np.array_equal(newp.cpu().numpy(), rp)
+
+
+def test_attention_large_score_jump_recomputes():
+    """A later tile scores far above the first tile of its split (a row sum
+    far beyond 2^100 relative to the first reference): the split must fall
+    back to the exact two-pass computation and still match the oracle."""
+    _say("[attention] score jump")
+    wl = W.make_random_case(51, batch=1, n_nodes=5, hq=8, hkv=2, d=128, prefix_lens=[300])
+    big = W.f32_to_bf16_bits(np.full(128, 6.0, dtype=np.float32))
+    wl.q[:] = big                      # q.k = 128*36 at the boosted keys
+    wl.k_cache[0, :, 200:230] = big    # inside a later tile of the same split
+    _run_attention_case(DevWorkload(wl), label="score-jump", num_splits=1)
+
+
+def test_attention_first_block_invalid_then_valid():
+    _say("[attention] first listed block invalid")
+    wl = W.make_random_case(52, batch=1, n_nodes=7, hq=8, hkv=2, d=128, prefix_lens=[400],
+                            block_size=32, blocks_per_seq=5)
+    good_idx, good_n = wl.block_idx.copy(), wl.n_blocks.copy()
+    dw = DevWorkload(wl)
+    bad = np.concatenate([np.array([[1000]], dtype=np.int32), good_idx], axis=1)
+    dw.block_idx = dev_i32(bad)
+    dw.n_blocks = dev_i32(good_n + 1)
+    wl.block_idx = bad
+    mask, _ = binding.build_tree_mask(dw.parents)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = dw.attention(mask, partial=True, dev_err=err, num_splits=1)
+    torch.cuda.synchronize()
+    wl.block_idx, wl.n_blocks = good_idx, good_n
+    ref, _ = oracle_attention(wl, partial=True)
+    check_attention_close(out, ref, "first-block-invalid")
+    assert int(err.item()) & binding.DERR_BAD_BLOCK

@@ -9,31 +9,48 @@
 // Design (gfx950):
 //  * One workgroup (4 waves) per (sequence, kv head, row group, split).  It
 //    holds every query row of its kv head -- n_nodes x group rows -- so each
-//    K/V tile is read from HBM once and reused by all rows (AI = rows
-//    FLOP/byte).  Each wave owns RB blocks of 16 rows.
+//    K/V tile is read from HBM once and reused by all rows (rows FLOP/byte).
+//    Each wave owns RB blocks of 16 rows.
 //  * The prefix (full rows, or the listed blocks) is cut into `splits`
 //    contiguous ranges; the tree block is one more split whose tiles are
 //    masked with the packed ancestor bits.  A combine kernel merges the
-//    (max, sum, unnormalised output) partials in fixed order.
-//  * K/V tiles of 32 tokens are staged in LDS (double buffered, padded rows
-//    against bank conflicts).  S^T = K Q^T and O^T += V^T P^T run on
-//    v_mfma_f32_16x16x32_bf16: the S^T accumulator layout puts one query row
-//    per lane column, so the softmax row statistics are mostly in-register
-//    and need two cross-lane steps; P^T is re-packed to bf16 straight from
-//    the accumulator registers as the B operand of the PV product.
-//  * Online softmax in fp32 in the log2 domain (scale * log2 e folded into
-//    one FMA before v_exp_f32); masked scores are -inf; rescaling of the
-//    output accumulators is skipped when no row maximum moved.
+//    (max, sum, unnormalised output) partials in a fixed order.
+//  * 32-token K/V tiles flow HBM -> registers -> LDS through a 3-slot LDS
+//    ring with two register stages, so two tiles are in flight per CU.  LDS
+//    rows are padded (K: D+8, V: D+16 elements) so that the 16-byte K reads
+//    and the 8-byte transposing V reads below are free of bank conflicts,
+//    and every operand address is a per-lane base plus an immediate.
+//  * S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_16x16x32_bf16.  The
+//    S^T accumulator gives every lane one query row and four tokens, so row
+//    statistics need two cross-lane steps; P^T is packed to bf16 straight
+//    from those registers as the B operand of the PV product, and the V^T
+//    A operand comes from ds_read_b64_tr_b16 (two per operand).
+//  * Software pipeline: QK of tile i+1 is issued before the softmax of tile
+//    i, so MFMA work overlaps the VALU softmax.
+//  * Softmax in fp32, log2 domain (scale * log2 e folded into one FMA
+//    before v_exp_f32).  Each row's reference max is fixed at the first tile
+//    in which the row sees a key, so the hot loop never rescales the output
+//    accumulators: later scores above the reference only make p > 1, which
+//    fp32 accumulates exactly enough (p is also exact in bf16's 8-bit
+//    exponent).  If a row's sum leaves [1, 2^100] or an output is not
+//    finite, the split is recomputed with the exact row max from a QK-only
+//    pre-pass (p <= 1 then).  Masked scores are -inf.
 #include "tv_internal.h"
 
 #include <math.h>
+
+#include <type_traits>
 
 namespace tv {
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTile = 32;        // tokens per KV tile
-constexpr int kMinChunk = 64;    // minimum prefix slots per split
+constexpr int kSlots = 3;        // LDS ring slots
+constexpr int kMinChunk = 128;   // minimum prefix slots per split
+constexpr float kSumMax = 1.2676506e30f;  // 2^100: largest accepted row sum
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 struct AttnArgs {
   const bf16* q;
@@ -52,7 +69,7 @@ struct AttnArgs {
   float* lse;
   int64_t seq_stride;
   int batch, n, hq, hkv, grp, cap, words;
-  int block_size, max_blocks, max_prefix;
+  int block_size, block_shift, max_blocks, max_prefix;  // block_shift < 0: not a power of 2
   int chunk, splits, row_groups, rows;
   float c;  // softmax scale * log2(e)
 };
@@ -80,44 +97,46 @@ __device__ __forceinline__ int prefix_slots(const AttnArgs& a, int b, int p, int
   return nb * a.block_size;
 }
 
-// Cache row behind prefix slot u (< slots), or -1 when the slot is empty
-// (past the prefix, or in an invalid / clipped block).
-__device__ __forceinline__ int slot_row(const AttnArgs& a, int b, int p, int u, int* err) {
-  if (a.max_blocks == 0) return u < p ? u : -1;
-  const int blk = a.block_idx[(int64_t)b * a.max_blocks + u / a.block_size];
-  if (blk < 0 || (int64_t)blk * a.block_size >= p) {
-    *err |= TV_DERR_BAD_BLOCK;
-    return -1;
-  }
-  const int row = blk * a.block_size + u % a.block_size;
-  return row < p ? row : -1;
+// Hide a per-tile LDS base from loop-invariant code motion so operand
+// addresses stay "base + immediate" instead of one register each.
+#define LDSP(T) __attribute__((address_space(3))) T*
+template <typename T>
+__device__ __forceinline__ void opaque(__attribute__((address_space(3))) T*& p) {
+  asm volatile("" : "+v"(p));
 }
 
-__device__ __forceinline__ float wave_max_cols(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+// Reductions over the four 16-lane groups (lanes l, l^16, l^32, l^48) with
+// the gfx950 row-swap permutes: after swapping, the two results of each
+// swap hold the value of a lane and of its partner.
+__device__ __forceinline__ float xmax16_32(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-__device__ __forceinline__ float wave_sum_cols(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+__device__ __forceinline__ float xsum16_32(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <int D, int RB>
+template <int D, int RB, bool PARTIAL>
 __global__ __launch_bounds__(kThreads, 1) void attn_split_kernel(AttnArgs a) {
-  constexpr int DC = D / 32;               // k-steps of the QK^T product
-  constexpr int DB = D / 16;               // 16-wide output blocks of PV
-  constexpr int KSTR = D + 8;              // LDS row stride (elements), K
-  constexpr int VSTR = D + 16;             // LDS row stride (elements), V
-  constexpr int VPR = D / 8;               // 16-byte vectors per row
-  constexpr int LOADS = kTile * VPR / kThreads;
-  static_assert(LOADS >= 1 && kTile * VPR % kThreads == 0, "tile / thread mismatch");
+  constexpr int CH = D / 8;                 // 16-byte chunks per row
+  constexpr int DC = D / 32;                // k-steps of the QK^T product
+  constexpr int DB = D / 16;                // 16-wide output blocks of PV
+  constexpr int KSTR = D + 8;               // LDS row stride of K (elements)
+  constexpr int VSTR = D + 16;              // LDS row stride of V (elements)
+  constexpr int RSTEP = kThreads / CH;      // rows covered by one load step
+  constexpr int LOADS = kTile / RSTEP;      // 16-byte loads per thread per tensor per tile
+  static_assert(LOADS >= 1 && kTile % RSTEP == 0, "tile / thread mismatch");
 
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][kTile * KSTR];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][kTile * VSTR];
-  __shared__ uint32_t svalid[2];
+  __shared__ __attribute__((aligned(16))) bf16 Ks[kSlots][kTile * KSTR];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[kSlots][kTile * VSTR];
+  __shared__ uint32_t svalid[kSlots];
+  __shared__ uint32_t smask[TV_MAX_NODES * (TV_MAX_NODES / 32)];  // tree rows of this WG
 
   const int s = blockIdx.x;
   const int g = blockIdx.y / a.row_groups;
@@ -145,198 +164,303 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_kernel(AttnArgs a) {
   err = 0;
   if (begin >= end) return;  // uniform over the workgroup
 
-  const int row0 = rg * (64 * RB) + wave * (16 * RB);
+  const int wg_row0 = rg * (64 * RB);
+  const int row0 = wg_row0 + wave * (16 * RB);
   const bool active = row0 < a.rows;
 
-  // Q^T fragments (B operand of S^T = K Q^T): column = query row, 8 d per lane
+  // ---- tree rows' mask words staged in LDS -------------------------------
+  const int node0 = wg_row0 / a.grp;
+  if (tree) {
+    const int node1 = min(a.n, (wg_row0 + 64 * RB + a.grp - 1) / a.grp);
+    const int cnt = (node1 - node0) * a.words;
+    const uint32_t* src = a.mask + ((int64_t)b * a.n + node0) * a.words;
+    for (int k = tid; k < cnt; k += kThreads) smask[k] = src[k];
+  }
+
+  // ---- Q^T fragments (B operand of S^T = K Q^T) ----------------------------
   bf16x8 qf[RB][DC];
 #pragma unroll
   for (int mb = 0; mb < RB; ++mb) {
     const int m = row0 + 16 * mb + col;
+    const bool real = m < a.rows;
+    const int i = real ? m / a.grp : 0;
+    const int h = g * a.grp + (real ? m - i * a.grp : 0);
+    const bf16* qrow = a.q + (((int64_t)b * a.n + i) * a.hq + h) * D + 8 * grp4;
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
-      if (m < a.rows) {
-        const int i = m / a.grp;
-        const int h = g * a.grp + m % a.grp;
-        qf[mb][dc] = *reinterpret_cast<const bf16x8*>(
-            a.q + (((int64_t)b * a.n + i) * a.hq + h) * D + 32 * dc + 8 * grp4);
-      } else {
-        qf[mb][dc] = bf16x8{};
-      }
-    }
+    for (int dc = 0; dc < DC; ++dc)
+      qf[mb][dc] = real ? *reinterpret_cast<const bf16x8*>(qrow + 32 * dc) : bf16x8{};
   }
 
-  f32x4 o[RB][DB];
-  float mrun[RB], lrun[RB];
-#pragma unroll
-  for (int mb = 0; mb < RB; ++mb) {
-    mrun[mb] = -INFINITY;
-    lrun[mb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) o[mb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
+  // ---- source rows --------------------------------------------------------
   const bf16* kbase;
   const bf16* vbase;
-  int64_t row_elems;  // elements between consecutive tokens in the source
+  int row_elems;
   if (tree) {
     kbase = a.k_tree + ((int64_t)b * a.n * a.hkv + g) * D;
     vbase = a.v_tree + ((int64_t)b * a.n * a.hkv + g) * D;
-    row_elems = (int64_t)a.hkv * D;
+    row_elems = a.hkv * D;
   } else {
     kbase = a.k_cache + b * a.seq_stride + (int64_t)g * a.cap * D;
     vbase = a.v_cache + b * a.seq_stride + (int64_t)g * a.cap * D;
     row_elems = D;
   }
+  const int lrow = tid / CH;         // first tile row this thread loads
+  const int lcol = (tid % CH) * 8;   // its column (elements)
+  const int32_t* blist = PARTIAL ? a.block_idx + (int64_t)b * a.max_blocks : nullptr;
 
-  uint4 kreg[LOADS], vreg[LOADS];
-  uint32_t vbits_next = 0;
-
-  auto token_row = [&](int u) -> int {  // source row of slot/token u, -1 if empty
-    if (u >= end) return -1;
-    return tree ? u : slot_row(a, b, p_len, u, &err);
+  // source row of slot u (caller guarantees u < end), -1 when empty
+  auto partial_row = [&](int u) -> int {
+    const int bi = a.block_shift >= 0 ? (u >> a.block_shift) : (u / a.block_size);
+    const int blk = blist[bi];
+    if (blk < 0 || (int64_t)blk * a.block_size >= p_len) {
+      err |= TV_DERR_BAD_BLOCK;
+      return -1;
+    }
+    const int row = blk * a.block_size + (u - bi * a.block_size);
+    return row < p_len ? row : -1;
   };
 
-  auto load_tile = [&](int t0) {
+  // ---- staging: registers -> LDS ring --------------------------------------
+  uint4 kreg[2][LOADS], vreg[2][LOADS];
+  uint32_t vb_reg[2] = {0u, 0u};
+
+  auto load_tile = [&](int st, int t0) {
 #pragma unroll
     for (int ld = 0; ld < LOADS; ++ld) {
-      const int idx = tid + ld * kThreads;
-      const int r = idx / VPR;
-      const int cv = idx % VPR;
-      const int row = token_row(t0 + r);
+      const int u = t0 + lrow + ld * RSTEP;
+      int row = u < end ? u : -1;
+      if (PARTIAL && !tree && row >= 0) row = partial_row(u);
       if (row >= 0) {
-        kreg[ld] = *reinterpret_cast<const uint4*>(kbase + row * row_elems + cv * 8);
-        vreg[ld] = *reinterpret_cast<const uint4*>(vbase + row * row_elems + cv * 8);
+        const int64_t off = (int64_t)row * row_elems + lcol;
+        kreg[st][ld] = *reinterpret_cast<const uint4*>(kbase + off);
+        vreg[st][ld] = *reinterpret_cast<const uint4*>(vbase + off);
       } else {
-        kreg[ld] = uint4{0u, 0u, 0u, 0u};
-        vreg[ld] = uint4{0u, 0u, 0u, 0u};
+        kreg[st][ld] = uint4{0u, 0u, 0u, 0u};
+        vreg[st][ld] = uint4{0u, 0u, 0u, 0u};
       }
     }
-    const bool v = lane < kTile && token_row(t0 + lane) >= 0;
-    vbits_next = (uint32_t)__ballot(v);
+    uint32_t vb;
+    if (PARTIAL && !tree) {
+      const int u = t0 + lane;
+      const bool v = lane < kTile && u < end && partial_row(u) >= 0;
+      vb = (uint32_t)__ballot(v);
+    } else {
+      const int cnt = end - t0;
+      vb = cnt >= kTile ? 0xFFFFFFFFu : ((1u << cnt) - 1u);
+    }
+    vb_reg[st] = vb;
   };
 
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int st, int slot) {
 #pragma unroll
     for (int ld = 0; ld < LOADS; ++ld) {
-      const int idx = tid + ld * kThreads;
-      const int r = idx / VPR;
-      const int cv = idx % VPR;
-      *reinterpret_cast<uint4*>(&Ks[buf][r * KSTR + cv * 8]) = kreg[ld];
-      *reinterpret_cast<uint4*>(&Vs[buf][r * VSTR + cv * 8]) = vreg[ld];
+      const int r = lrow + ld * RSTEP;
+      *reinterpret_cast<uint4*>(&Ks[slot][r * KSTR + lcol]) = kreg[st][ld];
+      *reinterpret_cast<uint4*>(&Vs[slot][r * VSTR + lcol]) = vreg[st][ld];
     }
-    if (tid == 0) svalid[buf] = vbits_next;
+    if (tid == 0) svalid[slot] = vb_reg[st];
   };
 
-  const int ntiles = (end - begin + kTile - 1) / kTile;
-  load_tile(begin);
-  store_tile(0);
-  __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    const int t0 = begin + it * kTile;
-    if (it + 1 < ntiles) load_tile(t0 + kTile);
-
-    if (active) {
-      // ---- S^T = K Q^T for 32 tokens x RB*16 rows -------------------------
-      f32x4 sacc[2][RB];
+  // ---- per-tile math --------------------------------------------------------
+  // S^T for one tile: sacc[tb][mb][r] = score of token tb*16 + 4*grp4 + r,
+  // row row0 + 16*mb + col.  Masked entries are -inf.
+  auto qk_tile = [&](int slot, int tile_idx, f32x4 (&sacc)[2][RB]) {
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
+    for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int mb = 0; mb < RB; ++mb) sacc[tb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int mb = 0; mb < RB; ++mb) sacc[tb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    LDSP(const bf16) kt = (LDSP(const bf16))&Ks[slot][col * KSTR + 8 * grp4];
+    opaque(kt);
 #pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
+    for (int dc = 0; dc < DC; ++dc) {
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-              &Ks[buf][(tb * 16 + col) * KSTR + 32 * dc + 8 * grp4]);
+      for (int tb = 0; tb < 2; ++tb) {
+        const bf16x8 kf = *(LDSP(const bf16x8))(kt + tb * 16 * KSTR + 32 * dc);
 #pragma unroll
-          for (int mb = 0; mb < RB; ++mb)
-            sacc[tb][mb] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[mb][dc], sacc[tb][mb], 0, 0, 0);
-        }
+        for (int mb = 0; mb < RB; ++mb)
+          sacc[tb][mb] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[mb][dc], sacc[tb][mb], 0, 0, 0);
       }
+    }
+    const uint32_t vbits = svalid[slot];
+    if (tree || vbits != 0xFFFFFFFFu) {
+#pragma unroll
+      for (int mb = 0; mb < RB; ++mb) {
+        uint32_t allow = vbits;
+        if (tree) {
+          const int m = row0 + 16 * mb + col;
+          allow &= m < a.rows ? smask[(m / a.grp - node0) * a.words + tile_idx] : 0u;
+        }
+        allow >>= 4 * grp4;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (!((allow >> (16 * tb + r)) & 1u)) sacc[tb][mb][r] = -INFINITY;
+      }
+    }
+  };
 
-      // ---- masking --------------------------------------------------------
-      const uint32_t vbits = svalid[buf];
-      if (tree || vbits != 0xFFFFFFFFu) {
+  f32x4 o[RB][DB];
+  float mref[RB], lrun[RB];
+  bool mset = false;  // wave-uniform: every real row of the wave has a reference
+
+  // p = 2^(s*c - mref) of one tile for row block mb, packed as the PV B
+  // operand.  The reference is taken from the first tile with a finite max.
+  auto softmax_block = [&](f32x4 (&sacc)[2][RB], int mb) -> bf16x8 {
+    if (!mset) {
+      float mx = fmaxf(fmaxf(fmaxf(sacc[0][mb][0], sacc[0][mb][1]), fmaxf(sacc[0][mb][2], sacc[0][mb][3])),
+                       fmaxf(fmaxf(sacc[1][mb][0], sacc[1][mb][1]), fmaxf(sacc[1][mb][2], sacc[1][mb][3])));
+      mx = xmax16_32(mx) * a.c;
+      mref[mb] = mref[mb] == -INFINITY ? mx : mref[mb];
+    }
+    const float muse = (mref[mb] == -INFINITY) ? 0.f : mref[mb];
+    bf16x8 pb;
+    float psum = 0.f;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[tb][mb][r], a.c, -muse));
+        psum += pv;
+        pb[tb * 4 + r] = (bf16)pv;
+      }
+    lrun[mb] += psum;
+    return pb;
+  };
+
+  auto update_mset = [&]() {
+    bool missing = false;
+#pragma unroll
+    for (int mb = 0; mb < RB; ++mb) missing |= (row0 + 16 * mb + col < a.rows) && mref[mb] == -INFINITY;
+    mset = !__ballot(missing);
+  };
+
+  // O^T += V^T P^T for one tile.  k-slot j of lane group q is token 4q+j
+  // (j<4) or 16+4q+(j-4): the tokens the lane holds in the S^T registers.
+  // ds_read_b64_tr_b16: in each 16-lane group, lane i receives element i%4
+  // of the 8-byte chunks addressed by lanes 4k + i/4 (k = 0..3); lane
+  // 4k + qq therefore addresses token (base + k), columns 4qq..4qq+3.
+  auto pv_tile = [&](int slot, const bf16x8 (&pb)[RB]) {
+    LDSP(bf16) vlo = (LDSP(bf16))&Vs[slot][(4 * grp4 + (col >> 2)) * VSTR + 4 * (col & 3)];
+    opaque(vlo);
+    LDSP(bf16) vhi = vlo + 16 * VSTR;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP(i16x4))(vlo + 16 * db));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP(i16x4))(vhi + 16 * db));
+      typedef short i16x8 __attribute__((ext_vector_type(8)));
+      const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, both);
+#pragma unroll
+      for (int mb = 0; mb < RB; ++mb)
+        o[mb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[mb], o[mb][db], 0, 0, 0);
+    }
+  };
+
+  // ---- pipeline -------------------------------------------------------------
+  // tile t lives in LDS slot t % 3; register stage (t & 1) carries tile t from
+  // its global load (two iterations ahead) to its LDS store (one ahead).
+  const int ntiles = (end - begin + kTile - 1) / kTile;
+
+  auto run = [&]() {
+#pragma unroll
+    for (int mb = 0; mb < RB; ++mb) {
+      lrun[mb] = 0.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[mb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    load_tile(0, begin);
+    if (ntiles > 1) load_tile(1, begin + kTile);
+    store_tile(0, 0);
+    if (ntiles > 1) store_tile(1, 1);
+    if (ntiles > 2) load_tile(0, begin + 2 * kTile);
+    if (ntiles > 3) load_tile(1, begin + 3 * kTile);
+    __syncthreads();
+
+    f32x4 sA[2][RB], sB[2][RB];
+    if (active) qk_tile(0, 0, sA);
+
+    // one pipeline step; ST = register stage of tile it+2; scores of tile
+    // it are in `cur`, tile it+1's go to `nxt`
+    auto step = [&](auto st_tag, int it, f32x4 (&cur)[2][RB], f32x4 (&nxt)[2][RB]) {
+      constexpr int ST = decltype(st_tag)::value;
+      if (it + 2 < ntiles) {
+        store_tile(ST, (it + 2) % kSlots);
+        if (it + 4 < ntiles) load_tile(ST, begin + (it + 4) * kTile);
+      }
+      if (active) {
+        if (it + 1 < ntiles) qk_tile((it + 1) % kSlots, it + 1, nxt);
+        bf16x8 pb[RB];
+#pragma unroll
+        for (int mb = 0; mb < RB; ++mb) pb[mb] = softmax_block(cur, mb);
+        if (!mset) update_mset();
+        pv_tile(it % kSlots, pb);
+      }
+      __syncthreads();
+    };
+    for (int it = 0; it < ntiles; it += 2) {
+      step(std::integral_constant<int, 0>{}, it, sA, sB);
+      if (it + 1 < ntiles) step(std::integral_constant<int, 1>{}, it + 1, sB, sA);
+    }
+  };
+
+#pragma unroll
+  for (int mb = 0; mb < RB; ++mb) mref[mb] = -INFINITY;
+  run();
+
+  // ---- overflow check; exact two-pass recompute when needed --------------
+  __shared__ int s_redo;
+  if (tid == 0) s_redo = 0;
+  __syncthreads();
+  if (active) {
+    bool bad = false;
+#pragma unroll
+    for (int mb = 0; mb < RB; ++mb) {
+      const float l = xsum16_32(lrun[mb]);
+      bool fin = true;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) fin = fin && __builtin_isfinite(o[mb][db][e]);
+      const bool real = row0 + 16 * mb + col < a.rows;
+      bad |= real && mref[mb] != -INFINITY && !(l <= kSumMax && fin);
+    }
+    if (__ballot(bad) && lane == 0) s_redo = 1;
+  }
+  __syncthreads();
+  if (s_redo) {
+    // QK-only pre-pass for the exact row max (single-buffered, rare path)
+#pragma unroll
+    for (int mb = 0; mb < RB; ++mb) mref[mb] = -INFINITY;
+    for (int it = 0; it < ntiles; ++it) {
+      load_tile(0, begin + it * kTile);
+      store_tile(0, 0);
+      __syncthreads();
+      if (active) {
+        f32x4 sc[2][RB];
+        qk_tile(0, it, sc);
 #pragma unroll
         for (int mb = 0; mb < RB; ++mb) {
-          uint32_t allow = vbits;
-          if (tree) {
-            const int m = row0 + 16 * mb + col;
-            const uint32_t w =
-                m < a.rows ? a.mask[((int64_t)b * a.n + m / a.grp) * a.words + t0 / kTile] : 0u;
-            allow &= w;
-          }
+          float mx = -INFINITY;
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int t = tb * 16 + 4 * grp4 + r;
-              if (!((allow >> t) & 1u)) sacc[tb][mb][r] = -INFINITY;
-            }
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[tb][mb][r]);
+          mref[mb] = fmaxf(mref[mb], xmax16_32(mx) * a.c);
         }
       }
-
-      // ---- online softmax, P^T packed to bf16 -----------------------------
-      bf16x8 pb[RB];
-#pragma unroll
-      for (int mb = 0; mb < RB; ++mb) {
-        float mx = sacc[0][mb][0];
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[tb][mb][r]);
-        mx = wave_max_cols(mx);
-        const float mnew = fmaxf(mrun[mb], mx * a.c);
-        const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-        const float alpha = __builtin_amdgcn_exp2f(mrun[mb] - muse);
-        float psum = 0.f;
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[tb][mb][r], a.c, -muse));
-            psum += pv;
-            pb[mb][tb * 4 + r] = (bf16)pv;
-          }
-        lrun[mb] = lrun[mb] * alpha + psum;
-        mrun[mb] = mnew;
-        if (__ballot(alpha != 1.f)) {
-#pragma unroll
-          for (int db = 0; db < DB; ++db) o[mb][db] *= alpha;
-        }
-      }
-
-      // ---- O^T += V^T P^T ---------------------------------------------------
-      // k-slot j of lane group q holds token 4q+j (j<4) or 16+4q+(j-4): the
-      // tokens this lane already owns in the S^T accumulators.
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const bf16* vcol = &Vs[buf][16 * db + col];
-        bf16x8 vf;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          vf[j] = vcol[(4 * grp4 + j) * VSTR];
-          vf[4 + j] = vcol[(16 + 4 * grp4 + j) * VSTR];
-        }
-#pragma unroll
-        for (int mb = 0; mb < RB; ++mb)
-          o[mb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[mb], o[mb][db], 0, 0, 0);
-      }
+      __syncthreads();
     }
-
-    if (it + 1 < ntiles) store_tile(buf ^ 1);
-    __syncthreads();
+    mset = true;
+    run();
   }
   if (err) raise_err(a.dev_err, err);
 
   if (!active) return;
 #pragma unroll
   for (int mb = 0; mb < RB; ++mb) {
-    const float l = wave_sum_cols(lrun[mb]);
+    const float l = xsum16_32(lrun[mb]);
     const int m = row0 + 16 * mb + col;
     if (m < a.rows) {
       const int i = m / a.grp;
@@ -345,7 +469,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_kernel(AttnArgs a) {
       float* dst = a.part_o + pi * D + 4 * grp4;
 #pragma unroll
       for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db) = o[mb][db];
-      if (grp4 == 0) a.part_ml[pi] = make_float2(mrun[mb], l);
+      if (grp4 == 0) a.part_ml[pi] = make_float2(mref[mb], l);
     }
   }
 }
@@ -355,6 +479,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_kernel(AttnArgs a) {
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
   constexpr int Q4 = D / 4;
+  constexpr int U = 8;
   const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const int64_t total = (int64_t)a.batch * a.n * a.hq * Q4;
   if (gid >= total) return;
@@ -370,10 +495,21 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
   const int slots = prefix_slots(a, b, p_len, &err);
   const int ns = (slots + a.chunk - 1) / a.chunk;
   const int64_t base = (int64_t)b * (a.splits + 1);
-  auto pidx = [&](int s) { return ((base + s) * a.n + i) * a.hq + h; };
+  const int64_t stride = (int64_t)a.n * a.hq;  // partial rows between splits
+  const int64_t p0 = (base * a.n + i) * a.hq + h;
 
-  float m = a.part_ml[pidx(a.splits)].x;
-  for (int s = 0; s < ns; ++s) m = fmaxf(m, a.part_ml[pidx(s)].x);
+  // splits 0..ns-1 then the tree split
+  auto split_of = [&](int k) { return k < ns ? k : a.splits; };
+  const int cnt = ns + 1;
+  float m = -INFINITY;
+  for (int k0 = 0; k0 < cnt; k0 += U) {
+    float mv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      mv[u] = (k0 + u < cnt) ? a.part_ml[p0 + split_of(k0 + u) * stride].x : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) m = fmaxf(m, mv[u]);
+  }
 
   bf16x4 res;
   float lse_v;
@@ -383,14 +519,26 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
   } else {
     float l = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s <= ns; ++s) {
-      const int ss = (s == ns) ? a.splits : s;
-      const int64_t pi = pidx(ss);
-      const float2 ml = a.part_ml[pi];
-      const float w = __builtin_amdgcn_exp2f(ml.x - m);
-      l += w * ml.y;
-      const f32x4 ov = *reinterpret_cast<const f32x4*>(a.part_o + pi * D + 4 * dq);
-      acc += w * ov;
+    for (int k0 = 0; k0 < cnt; k0 += U) {
+      float2 ml[U];
+      f32x4 ov[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (k0 + u < cnt) {
+          const int64_t pi = p0 + split_of(k0 + u) * stride;
+          ml[u] = a.part_ml[pi];
+          ov[u] = *reinterpret_cast<const f32x4*>(a.part_o + pi * D + 4 * dq);
+        } else {
+          ml[u] = make_float2(-INFINITY, 0.f);
+          ov[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float w = __builtin_amdgcn_exp2f(ml[u].x - m);
+        l += w * ml[u].y;
+        acc += w * ov[u];
+      }
     }
     const float inv = 1.f / l;
 #pragma unroll
@@ -403,7 +551,10 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
 
 template <int D, int RB>
 void launch_split(const AttnArgs& args, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_split_kernel<D, RB>), grid, dim3(kThreads), 0, stream, args);
+  if (args.max_blocks)
+    hipLaunchKernelGGL((attn_split_kernel<D, RB, true>), grid, dim3(kThreads), 0, stream, args);
+  else
+    hipLaunchKernelGGL((attn_split_kernel<D, RB, false>), grid, dim3(kThreads), 0, stream, args);
 }
 
 template <int D>
@@ -474,6 +625,9 @@ hipError_t launch_attention(const tv_attn_desc& d, const AttnPlan& plan, const t
   a.cap = d.cache_capacity;
   a.words = (d.n_nodes + 31) / 32;
   a.block_size = d.max_blocks ? d.block_size : 1;
+  a.block_shift = -1;
+  for (int sh = 0; sh < 31; ++sh)
+    if ((1 << sh) == a.block_size) a.block_shift = sh;
   a.max_blocks = d.max_blocks;
   a.max_prefix = d.max_prefix_len;
   a.chunk = plan.chunk;
