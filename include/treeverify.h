@@ -130,7 +130,9 @@ typedef struct {
   int32_t block_size;       /* partial mode: tokens per KV block (>= 1) */
   int32_t max_blocks;       /* partial mode: columns of block_idx; 0 = full mode */
   float softmax_scale;      /* <= 0 means 1 / sqrt(head_dim) */
-  int32_t num_splits;       /* prefix splits per (sequence, kv head); 0 = automatic */
+  int32_t num_splits;       /* prefix splits per (sequence, kv head); 0 = automatic.  A hint:
+                               partial mode raises it so that one split spans at most
+                               1022 blocks; tv_tree_attention_num_splits gives the count */
   int64_t cache_seq_stride; /* elements between sequences; 0 = n_kv_heads*capacity*head_dim */
 } tv_attn_desc;
 

@@ -7,10 +7,12 @@
 // proposed tokens multiplies the arithmetic intensity by N).
 //
 // Design (gfx950):
-//  * One workgroup (4 waves) per (sequence, kv head, row group, split).  It
-//    holds every query row of its kv head -- n_nodes x group rows -- so each
-//    K/V tile is read from HBM once and reused by all rows (rows FLOP/byte).
-//    Each wave owns RB blocks of 16 rows.
+//  * One workgroup (8 waves, two per SIMD) per (sequence, kv head, row
+//    group, split).  It holds up to 256 query rows of its kv head -- the
+//    n_nodes x group rows -- so each K/V tile is read from HBM once and
+//    reused by all rows (rows FLOP/byte).  Each wave owns RB (1 or 2) blocks
+//    of 16 rows.  Two waves per SIMD are needed to keep the matrix core
+//    busy: a single wave issues dependent-free MFMAs at well under peak.
 //  * The prefix (full rows, or the listed blocks) is cut into `splits`
 //    contiguous ranges; the tree block is one more split whose tiles are
 //    masked with the packed ancestor bits.  A combine kernel merges the
@@ -39,14 +41,16 @@
 
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 namespace tv {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;      // combine kernel
+constexpr int kWaves = 8;          // split kernel: 8 waves, two per SIMD
+constexpr int kSplitThreads = kWaves * 64;
 constexpr int kTile = 32;        // tokens per KV tile
-constexpr int kSlots = 3;        // LDS ring slots
 constexpr int kMinChunk = 128;   // minimum prefix slots per split
 constexpr float kSumMax = 1.2676506e30f;  // 2^100: largest accepted row sum
 
@@ -97,12 +101,17 @@ __device__ __forceinline__ int prefix_slots(const AttnArgs& a, int b, int p, int
   return nb * a.block_size;
 }
 
-// Hide a per-tile LDS base from loop-invariant code motion so operand
-// addresses stay "base + immediate" instead of one register each.
-#define LDSP(T) __attribute__((address_space(3))) T*
-template <typename T>
-__device__ __forceinline__ void opaque(__attribute__((address_space(3))) T*& p) {
-  asm volatile("" : "+v"(p));
+
+// Workgroup barrier for LDS hand-off only.  __syncthreads() would also wait
+// for every outstanding global load of the wave (vmcnt(0)), which would
+// drain the tile prefetches the pipeline keeps in flight across barriers.
+// Here each wave only waits for its own LDS accesses (lgkmcnt(0)); the
+// signal fences keep the compiler from moving memory operations across.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // gfx9 encoding: lgkmcnt(0), vmcnt/expcnt unconstrained
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // Reductions over the four 16-lane groups (lanes l, l^16, l^32, l^48) with
@@ -115,28 +124,52 @@ __device__ __forceinline__ float xmax16_32(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-__device__ __forceinline__ float xsum16_32(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+// ---- LDS DMA -----------------------------------------------------------------
+// global_load_lds_dwordx4: each lane loads 16 bytes from its own address and
+// the wave's 64 results land contiguously in LDS at M0 (lane i at M0 + 16 i).
+// Issued through inline asm so that the compiler neither reorders it nor
+// inserts its own (conservative) waits; completion is tracked by hand with
+// vmcnt, which counts these loads like any other vector-memory load.
+__device__ __forceinline__ void dma16(uint32_t lds_addr, const void* gptr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_addr), "v"(gptr)
+               : "memory");
 }
 
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// XOR swizzle of the 16-byte chunks of tile row t (CH chunks per row): keeps
+// the 16-byte K fragment reads and the 8-byte transposing V reads free of
+// bank conflicts on unpadded 256-byte rows.
+template <int CH>
+__device__ __forceinline__ int swz(int t) {
+  return (2 * t + (t >> 2)) & (CH - 1);
+}
+
+constexpr int kRing = 4;        // LDS ring slots (tiles)
+constexpr int kBlkCache = 1024; // block ids of one split staged in LDS
+
 template <int D, int RB, bool PARTIAL>
-__global__ __launch_bounds__(kThreads, 1) void attn_split_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a) {
   constexpr int CH = D / 8;                 // 16-byte chunks per row
+  constexpr int ROWB = D * 2;               // bytes per row
   constexpr int DC = D / 32;                // k-steps of the QK^T product
   constexpr int DB = D / 16;                // 16-wide output blocks of PV
-  constexpr int KSTR = D + 8;               // LDS row stride of K (elements)
-  constexpr int VSTR = D + 16;              // LDS row stride of V (elements)
-  constexpr int RSTEP = kThreads / CH;      // rows covered by one load step
-  constexpr int LOADS = kTile / RSTEP;      // 16-byte loads per thread per tensor per tile
-  static_assert(LOADS >= 1 && kTile % RSTEP == 0, "tile / thread mismatch");
+  constexpr int TILE_B = kTile * ROWB;      // bytes of one K (or V) tile
+  constexpr int SLOT_B = 2 * TILE_B;        // K tile then V tile
+  constexpr int RPI = 64 / CH;              // tile rows per DMA instruction
+  constexpr int IPT = kTile / RPI;          // DMA instructions per tensor per tile
+  constexpr int DPT = 2 * IPT / kWaves;     // DMA instructions per wave per tile
+  static_assert(DPT == 1 || DPT == 2, "DMA split across waves");
 
-  __shared__ __attribute__((aligned(16))) bf16 Ks[kSlots][kTile * KSTR];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[kSlots][kTile * VSTR];
-  __shared__ uint32_t svalid[kSlots];
+  __shared__ __attribute__((aligned(1024))) char ring[kRing * SLOT_B];
   __shared__ uint32_t smask[TV_MAX_NODES * (TV_MAX_NODES / 32)];  // tree rows of this WG
+  __shared__ int sblk[kBlkCache];                                 // partial: block ids
+  __shared__ int s_first;
 
   const int s = blockIdx.x;
   const int g = blockIdx.y / a.row_groups;
@@ -148,6 +181,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_kernel(AttnArgs a) {
   const int col = lane & 15;   // MFMA column (query row within a block)
   const int grp4 = lane >> 4;  // lane group 0..3
   const bool tree = (s == a.splits);
+  const bool part = PARTIAL && !tree;
 
   int err = 0;
   const int p_len = clamped_prefix(a, b, &err);
@@ -164,18 +198,118 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_kernel(AttnArgs a) {
   err = 0;
   if (begin >= end) return;  // uniform over the workgroup
 
-  const int wg_row0 = rg * (64 * RB);
+  const int wg_row0 = rg * (16 * kWaves * RB);
   const int row0 = wg_row0 + wave * (16 * RB);
   const bool active = row0 < a.rows;
-
-  // ---- tree rows' mask words staged in LDS -------------------------------
   const int node0 = wg_row0 / a.grp;
+
+  // ---- source rows --------------------------------------------------------
+  const char* kbytes;
+  const char* vbytes;
+  int src_rowb;  // bytes between consecutive tokens in the source
   if (tree) {
-    const int node1 = min(a.n, (wg_row0 + 64 * RB + a.grp - 1) / a.grp);
+    kbytes = reinterpret_cast<const char*>(a.k_tree + ((int64_t)b * a.n * a.hkv + g) * D);
+    vbytes = reinterpret_cast<const char*>(a.v_tree + ((int64_t)b * a.n * a.hkv + g) * D);
+    src_rowb = a.hkv * ROWB;
+  } else {
+    kbytes = reinterpret_cast<const char*>(a.k_cache + b * a.seq_stride + (int64_t)g * a.cap * D);
+    vbytes = reinterpret_cast<const char*>(a.v_cache + b * a.seq_stride + (int64_t)g * a.cap * D);
+    src_rowb = ROWB;
+  }
+
+  // ---- per-split tables staged in LDS --------------------------------------
+  int bi0 = 0;      // partial: first block index of the split
+  int fb_row = begin;  // a row of this split that is valid (stands in for empty slots)
+  if (tree) {
+    const int node1 = min(a.n, (wg_row0 + 16 * kWaves * RB + a.grp - 1) / a.grp);
     const int cnt = (node1 - node0) * a.words;
     const uint32_t* src = a.mask + ((int64_t)b * a.n + node0) * a.words;
-    for (int k = tid; k < cnt; k += kThreads) smask[k] = src[k];
+    for (int k = tid; k < cnt; k += kSplitThreads) smask[k] = src[k];
   }
+  if (part) {
+    const int32_t* blist = a.block_idx + (int64_t)b * a.max_blocks;
+    bi0 = begin / a.block_size;
+    const int bi1 = (end - 1) / a.block_size;
+    // the plan keeps a split within kBlkCache blocks
+    if (tid == 0) s_first = INT32_MAX;
+    __syncthreads();
+    for (int k = tid; k < bi1 - bi0 + 1; k += kSplitThreads) {
+      const int blk = blist[bi0 + k];
+      sblk[k] = blk;
+      if (blk >= 0 && (int64_t)blk * a.block_size < p_len) atomicMin(&s_first, k);
+      else err |= TV_DERR_BAD_BLOCK;
+    }
+    __syncthreads();
+    const int first = s_first;
+    if (first == INT32_MAX) {
+      // no valid slot in this split: an empty partial
+      if (err) raise_err(a.dev_err, err);
+      for (int mb = 0; mb < RB; ++mb) {
+        const int m = row0 + 16 * mb + col;
+        if (active && m < a.rows && grp4 == 0) {
+          const int i = m / a.grp;
+          const int h = g * a.grp + m % a.grp;
+          const int64_t pi = (((int64_t)b * (a.splits + 1) + s) * a.n + i) * a.hq + h;
+          a.part_ml[pi] = make_float2(-INFINITY, 0.f);
+        }
+      }
+      return;
+    }
+    fb_row = blist[bi0 + first] * a.block_size;
+  }
+  // cache row of slot u of this split, fb_row when the slot is empty
+  auto slot_row = [&](int u, bool& valid) -> int {
+    if (u >= end) {
+      valid = false;
+      return fb_row;
+    }
+    if (!part) {
+      valid = true;
+      return u;
+    }
+    const int bi = a.block_shift >= 0 ? (u >> a.block_shift) : (u / a.block_size);
+    const int blk = sblk[bi - bi0];
+    const int row = blk * a.block_size + (u - bi * a.block_size);
+    valid = blk >= 0 && (int64_t)blk * a.block_size < p_len && row < p_len;
+    return valid ? row : fb_row;
+  };
+
+  // ---- DMA of one tile into a ring slot ------------------------------------
+  // DMA instruction q of a tensor covers tile rows RPI*q .. RPI*q+RPI-1; lane
+  // i fills physical chunk (i % CH) of row RPI*q + i/CH, i.e. the logical
+  // chunk (i % CH) ^ swz(row).
+  const uint32_t ring_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)ring;
+  int dq[DPT], dt[DPT];       // instruction index and tensor (0 = K, 1 = V)
+  int dr[DPT];                // tile row of this lane
+  uint32_t dcol[DPT];         // byte offset of this lane's logical chunk
+#pragma unroll
+  for (int k = 0; k < DPT; ++k) {
+    const int inst = wave * DPT + k;  // 0 .. 2*IPT-1
+    dt[k] = inst / IPT;
+    dq[k] = inst % IPT;
+    dr[k] = RPI * dq[k] + lane / CH;
+    dcol[k] = 16u * (uint32_t)((lane % CH) ^ swz<CH>(dr[k]));
+  }
+  auto dma_tile = [&](int slot, int t0) {
+#pragma unroll
+    for (int k = 0; k < DPT; ++k) {
+      bool valid;
+      const int row = slot_row(t0 + dr[k], valid);
+      const char* src = (dt[k] ? vbytes : kbytes) + (uint32_t)row * (uint32_t)src_rowb + dcol[k];
+      const uint32_t dst = ring_base + slot * SLOT_B + dt[k] * TILE_B + dq[k] * 1024;
+      dma16(__builtin_amdgcn_readfirstlane(dst), src);
+    }
+  };
+  // validity bits of the 32 slots of the tile starting at t0 (wave-uniform)
+  auto tile_bits = [&](int t0) -> uint32_t {
+    if (!part) {
+      const int cnt = end - t0;
+      return cnt >= kTile ? 0xFFFFFFFFu : (cnt <= 0 ? 0u : ((1u << cnt) - 1u));
+    }
+    bool valid = false;
+    if (lane < kTile) slot_row(t0 + lane, valid);
+    return (uint32_t)__ballot(valid);
+  };
 
   // ---- Q^T fragments (B operand of S^T = K Q^T) ----------------------------
   bf16x8 qf[RB][DC];
@@ -190,125 +324,93 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_kernel(AttnArgs a) {
     for (int dc = 0; dc < DC; ++dc)
       qf[mb][dc] = real ? *reinterpret_cast<const bf16x8*>(qrow + 32 * dc) : bf16x8{};
   }
+  // Wait for Q here, on every path: the compiler's own wait would otherwise
+  // be placed inside the loop (vmcnt(0), draining the tile DMA each step).
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // gfx9 encoding: vmcnt(0)
 
-  // ---- source rows --------------------------------------------------------
-  const bf16* kbase;
-  const bf16* vbase;
-  int row_elems;
-  if (tree) {
-    kbase = a.k_tree + ((int64_t)b * a.n * a.hkv + g) * D;
-    vbase = a.v_tree + ((int64_t)b * a.n * a.hkv + g) * D;
-    row_elems = a.hkv * D;
-  } else {
-    kbase = a.k_cache + b * a.seq_stride + (int64_t)g * a.cap * D;
-    vbase = a.v_cache + b * a.seq_stride + (int64_t)g * a.cap * D;
-    row_elems = D;
-  }
-  const int lrow = tid / CH;         // first tile row this thread loads
-  const int lcol = (tid % CH) * 8;   // its column (elements)
-  const int32_t* blist = PARTIAL ? a.block_idx + (int64_t)b * a.max_blocks : nullptr;
-
-  // source row of slot u (caller guarantees u < end), -1 when empty
-  auto partial_row = [&](int u) -> int {
-    const int bi = a.block_shift >= 0 ? (u >> a.block_shift) : (u / a.block_size);
-    const int blk = blist[bi];
-    if (blk < 0 || (int64_t)blk * a.block_size >= p_len) {
-      err |= TV_DERR_BAD_BLOCK;
-      return -1;
-    }
-    const int row = blk * a.block_size + (u - bi * a.block_size);
-    return row < p_len ? row : -1;
-  };
-
-  // ---- staging: registers -> LDS ring --------------------------------------
-  uint4 kreg[2][LOADS], vreg[2][LOADS];
-  uint32_t vb_reg[2] = {0u, 0u};
-
-  auto load_tile = [&](int st, int t0) {
+  // ---- LDS operand offsets (per lane, slot relative) -----------------------
+  // K fragment (tb, dc): row tb*16 + col, logical chunk 4*dc + grp4.
+  uint32_t koff[2][DC];
 #pragma unroll
-    for (int ld = 0; ld < LOADS; ++ld) {
-      const int u = t0 + lrow + ld * RSTEP;
-      int row = u < end ? u : -1;
-      if (PARTIAL && !tree && row >= 0) row = partial_row(u);
-      if (row >= 0) {
-        const int64_t off = (int64_t)row * row_elems + lcol;
-        kreg[st][ld] = *reinterpret_cast<const uint4*>(kbase + off);
-        vreg[st][ld] = *reinterpret_cast<const uint4*>(vbase + off);
-      } else {
-        kreg[st][ld] = uint4{0u, 0u, 0u, 0u};
-        vreg[st][ld] = uint4{0u, 0u, 0u, 0u};
-      }
-    }
-    uint32_t vb;
-    if (PARTIAL && !tree) {
-      const int u = t0 + lane;
-      const bool v = lane < kTile && u < end && partial_row(u) >= 0;
-      vb = (uint32_t)__ballot(v);
-    } else {
-      const int cnt = end - t0;
-      vb = cnt >= kTile ? 0xFFFFFFFFu : ((1u << cnt) - 1u);
-    }
-    vb_reg[st] = vb;
-  };
-
-  auto store_tile = [&](int st, int slot) {
+  for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-    for (int ld = 0; ld < LOADS; ++ld) {
-      const int r = lrow + ld * RSTEP;
-      *reinterpret_cast<uint4*>(&Ks[slot][r * KSTR + lcol]) = kreg[st][ld];
-      *reinterpret_cast<uint4*>(&Vs[slot][r * VSTR + lcol]) = vreg[st][ld];
+    for (int dc = 0; dc < DC; ++dc) {
+      const int t = tb * 16 + col;
+      koff[tb][dc] = t * ROWB + 16 * ((4 * dc + grp4) ^ swz<CH>(t));
     }
-    if (tid == 0) svalid[slot] = vb_reg[st];
-  };
+  // V^T fragment (db, half): ds_read_b64_tr_b16 gives, in each 16-lane group,
+  // lane i element i%4 of the 8-byte chunks addressed by lanes 4k + i/4
+  // (k = 0..3); lane 4k + qq addresses token base + k, columns 4qq..4qq+3.
+  // k-slot j of lane group q is token 4q+j (j<4) or 16+4q+(j-4): the tokens
+  // the lane holds in the S^T accumulators.
+  uint32_t voff[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int t = 16 * hf + 4 * grp4 + (col >> 2);
+      const int c = 2 * db + ((col & 3) >> 1);
+      voff[db][hf] = TILE_B + t * ROWB + 16 * (c ^ swz<CH>(t)) + 8 * (col & 1);
+    }
+
+  typedef __attribute__((address_space(3))) char lds_char;
+  auto lds_at = [&](uint32_t addr) { return (lds_char*)(uintptr_t)addr; };
 
   // ---- per-tile math --------------------------------------------------------
   // S^T for one tile: sacc[tb][mb][r] = score of token tb*16 + 4*grp4 + r,
-  // row row0 + 16*mb + col.  Masked entries are -inf.
-  auto qk_tile = [&](int slot, int tile_idx, f32x4 (&sacc)[2][RB]) {
+  // row row0 + 16*mb + col.  The first k-step starts from a zero accumulator.
+  auto qk_tile = [&](int slot, f32x4 (&sacc)[2][RB]) {
+    const uint32_t base = ring_base + slot * SLOT_B;
+    bf16x8 kf[2][2];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-      for (int mb = 0; mb < RB; ++mb) sacc[tb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    LDSP(const bf16) kt = (LDSP(const bf16))&Ks[slot][col * KSTR + 8 * grp4];
-    opaque(kt);
+      kf[0][tb] = *(__attribute__((address_space(3))) const bf16x8*)lds_at(base + koff[tb][0]);
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        const bf16x8 kf = *(LDSP(const bf16x8))(kt + tb * 16 * KSTR + 32 * dc);
-#pragma unroll
-        for (int mb = 0; mb < RB; ++mb)
-          sacc[tb][mb] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[mb][dc], sacc[tb][mb], 0, 0, 0);
-      }
-    }
-    const uint32_t vbits = svalid[slot];
-    if (tree || vbits != 0xFFFFFFFFu) {
-#pragma unroll
-      for (int mb = 0; mb < RB; ++mb) {
-        uint32_t allow = vbits;
-        if (tree) {
-          const int m = row0 + 16 * mb + col;
-          allow &= m < a.rows ? smask[(m / a.grp - node0) * a.words + tile_idx] : 0u;
-        }
-        allow >>= 4 * grp4;
+      if (dc + 1 < DC) {
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (!((allow >> (16 * tb + r)) & 1u)) sacc[tb][mb][r] = -INFINITY;
+          kf[(dc + 1) & 1][tb] =
+              *(__attribute__((address_space(3))) const bf16x8*)lds_at(base + koff[tb][dc + 1]);
       }
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int mb = 0; mb < RB; ++mb)
+          sacc[tb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              kf[dc & 1][tb], qf[mb][dc], dc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[tb][mb], 0, 0, 0);
+    }
+  };
+
+  // -inf for tokens outside the tile's valid set (and, in the tree block,
+  // outside the row's ancestor set)
+  auto mask_tile = [&](uint32_t vbits, int tile_idx, f32x4 (&sacc)[2][RB]) {
+    if (!tree && vbits == 0xFFFFFFFFu) return;
+#pragma unroll
+    for (int mb = 0; mb < RB; ++mb) {
+      uint32_t allow = vbits;
+      if (tree) {
+        const int m = row0 + 16 * mb + col;
+        allow &= m < a.rows ? smask[(m / a.grp - node0) * a.words + tile_idx] : 0u;
+      }
+      allow >>= 4 * grp4;
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (!((allow >> (16 * tb + r)) & 1u)) sacc[tb][mb][r] = -INFINITY;
     }
   };
 
   f32x4 o[RB][DB];
-  float mref[RB], lrun[RB];
-  bool mset = false;  // wave-uniform: every real row of the wave has a reference
+  f32x4 lsum[RB];     // row sums of p, from an MFMA against a block of ones
+  float mref[RB];     // reference max per row (log2 units), -inf until set
 
   // p = 2^(s*c - mref) of one tile for row block mb, packed as the PV B
-  // operand.  The reference is taken from the first tile with a finite max.
-  auto softmax_block = [&](f32x4 (&sacc)[2][RB], int mb) -> bf16x8 {
-    if (!mset) {
+  // operand.  With TRACK (first tile) the reference is taken from this tile
+  // where unset.
+  auto softmax_block = [&](f32x4 (&sacc)[2][RB], int mb, auto track_tag) -> bf16x8 {
+    if (decltype(track_tag)::value) {
       float mx = fmaxf(fmaxf(fmaxf(sacc[0][mb][0], sacc[0][mb][1]), fmaxf(sacc[0][mb][2], sacc[0][mb][3])),
                        fmaxf(fmaxf(sacc[1][mb][0], sacc[1][mb][1]), fmaxf(sacc[1][mb][2], sacc[1][mb][3])));
       mx = xmax16_32(mx) * a.c;
@@ -316,93 +418,88 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_kernel(AttnArgs a) {
     }
     const float muse = (mref[mb] == -INFINITY) ? 0.f : mref[mb];
     bf16x8 pb;
-    float psum = 0.f;
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[tb][mb][r], a.c, -muse));
-        psum += pv;
-        pb[tb * 4 + r] = (bf16)pv;
-      }
-    lrun[mb] += psum;
+      for (int r = 0; r < 4; ++r)
+        pb[tb * 4 + r] = (bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[tb][mb][r], a.c, -muse));
     return pb;
   };
 
-  auto update_mset = [&]() {
-    bool missing = false;
+  bf16x8 ones;
 #pragma unroll
-    for (int mb = 0; mb < RB; ++mb) missing |= (row0 + 16 * mb + col < a.rows) && mref[mb] == -INFINITY;
-    mset = !__ballot(missing);
-  };
-
-  // O^T += V^T P^T for one tile.  k-slot j of lane group q is token 4q+j
-  // (j<4) or 16+4q+(j-4): the tokens the lane holds in the S^T registers.
-  // ds_read_b64_tr_b16: in each 16-lane group, lane i receives element i%4
-  // of the 8-byte chunks addressed by lanes 4k + i/4 (k = 0..3); lane
-  // 4k + qq therefore addresses token (base + k), columns 4qq..4qq+3.
+  for (int e = 0; e < 8; ++e) ones[e] = (bf16)1.0f;
   auto pv_tile = [&](int slot, const bf16x8 (&pb)[RB]) {
-    LDSP(bf16) vlo = (LDSP(bf16))&Vs[slot][(4 * grp4 + (col >> 2)) * VSTR + 4 * (col & 3)];
-    opaque(vlo);
-    LDSP(bf16) vhi = vlo + 16 * VSTR;
+    const uint32_t base = ring_base + slot * SLOT_B;
+    auto vfrag = [&](int db) -> bf16x8 {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)lds_at(base + voff[db][0]));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)lds_at(base + voff[db][1]));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 vf[2];
+    vf[0] = vfrag(0);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP(i16x4))(vlo + 16 * db));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP(i16x4))(vhi + 16 * db));
-      typedef short i16x8 __attribute__((ext_vector_type(8)));
-      const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, both);
+      if (db + 1 < DB) vf[(db + 1) & 1] = vfrag(db + 1);
 #pragma unroll
       for (int mb = 0; mb < RB; ++mb)
-        o[mb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[mb], o[mb][db], 0, 0, 0);
+        o[mb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db & 1], pb[mb], o[mb][db], 0, 0, 0);
     }
+#pragma unroll
+    for (int mb = 0; mb < RB; ++mb)
+      lsum[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[mb], lsum[mb], 0, 0, 0);
   };
 
   // ---- pipeline -------------------------------------------------------------
-  // tile t lives in LDS slot t % 3; register stage (t & 1) carries tile t from
-  // its global load (two iterations ahead) to its LDS store (one ahead).
+  // Tile t lives in ring slot t % 4.  Three tiles are requested before the
+  // loop; step it waits for tile it+1 (the older of its two outstanding
+  // tiles), passes a barrier (which also frees the slot of tile it-1), asks
+  // for tile it+3, then computes: softmax of tile it, QK of tile it+1, PV of
+  // tile it.  Tiles past the range re-read a valid row and are discarded.
   const int ntiles = (end - begin + kTile - 1) / kTile;
 
   auto run = [&]() {
 #pragma unroll
     for (int mb = 0; mb < RB; ++mb) {
-      lrun[mb] = 0.f;
+      lsum[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[mb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    load_tile(0, begin);
-    if (ntiles > 1) load_tile(1, begin + kTile);
-    store_tile(0, 0);
-    if (ntiles > 1) store_tile(1, 1);
-    if (ntiles > 2) load_tile(0, begin + 2 * kTile);
-    if (ntiles > 3) load_tile(1, begin + 3 * kTile);
-    __syncthreads();
+    dma_tile(0, begin);
+    dma_tile(1, begin + kTile);
+    dma_tile(2, begin + 2 * kTile);
+    vm_wait<2 * DPT>();
+    lds_barrier();
 
     f32x4 sA[2][RB], sB[2][RB];
-    if (active) qk_tile(0, 0, sA);
+    if (active) {
+      qk_tile(0, sA);
+      mask_tile(tile_bits(begin), 0, sA);
+    }
 
-    // one pipeline step; ST = register stage of tile it+2; scores of tile
-    // it are in `cur`, tile it+1's go to `nxt`
-    auto step = [&](auto st_tag, int it, f32x4 (&cur)[2][RB], f32x4 (&nxt)[2][RB]) {
-      constexpr int ST = decltype(st_tag)::value;
-      if (it + 2 < ntiles) {
-        store_tile(ST, (it + 2) % kSlots);
-        if (it + 4 < ntiles) load_tile(ST, begin + (it + 4) * kTile);
-      }
+    auto step = [&](auto track_tag, int it, f32x4 (&cur)[2][RB], f32x4 (&nxt)[2][RB]) {
+      vm_wait<DPT>();
+      lds_barrier();
+      dma_tile((it + 3) % kRing, begin + (it + 3) * kTile);
       if (active) {
-        if (it + 1 < ntiles) qk_tile((it + 1) % kSlots, it + 1, nxt);
         bf16x8 pb[RB];
 #pragma unroll
-        for (int mb = 0; mb < RB; ++mb) pb[mb] = softmax_block(cur, mb);
-        if (!mset) update_mset();
-        pv_tile(it % kSlots, pb);
+        for (int mb = 0; mb < RB; ++mb) pb[mb] = softmax_block(cur, mb, track_tag);
+        qk_tile((it + 1) % kRing, nxt);
+        pv_tile(it % kRing, pb);
+        if (it + 1 < ntiles) mask_tile(tile_bits(begin + (it + 1) * kTile), it + 1, nxt);
       }
-      __syncthreads();
     };
-    for (int it = 0; it < ntiles; it += 2) {
-      step(std::integral_constant<int, 0>{}, it, sA, sB);
-      if (it + 1 < ntiles) step(std::integral_constant<int, 1>{}, it + 1, sB, sA);
+    // the first tile sets each row's reference max
+    step(std::true_type{}, 0, sA, sB);
+    for (int it = 1; it < ntiles; it += 2) {
+      step(std::false_type{}, it, sB, sA);
+      if (it + 1 < ntiles) step(std::false_type{}, it + 1, sA, sB);
     }
+    vm_wait<0>();   // the requests past the last tile
+    lds_barrier();
   };
 
 #pragma unroll
@@ -417,14 +514,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_kernel(AttnArgs a) {
     bool bad = false;
 #pragma unroll
     for (int mb = 0; mb < RB; ++mb) {
-      const float l = xsum16_32(lrun[mb]);
+      const float l = lsum[mb][0];
       bool fin = true;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int e = 0; e < 4; ++e) fin = fin && __builtin_isfinite(o[mb][db][e]);
       const bool real = row0 + 16 * mb + col < a.rows;
-      bad |= real && mref[mb] != -INFINITY && !(l <= kSumMax && fin);
+      // a row whose first tile was fully masked used 0 as its reference:
+      // recompute it with the exact max as well
+      bad |= real && (mref[mb] == -INFINITY ? l > 0.f : !(l <= kSumMax && fin));
     }
     if (__ballot(bad) && lane == 0) s_redo = 1;
   }
@@ -434,12 +533,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_kernel(AttnArgs a) {
 #pragma unroll
     for (int mb = 0; mb < RB; ++mb) mref[mb] = -INFINITY;
     for (int it = 0; it < ntiles; ++it) {
-      load_tile(0, begin + it * kTile);
-      store_tile(0, 0);
-      __syncthreads();
+      dma_tile(0, begin + it * kTile);
+      vm_wait<0>();
+      lds_barrier();
       if (active) {
         f32x4 sc[2][RB];
-        qk_tile(0, it, sc);
+        qk_tile(0, sc);
+        mask_tile(tile_bits(begin + it * kTile), it, sc);
 #pragma unroll
         for (int mb = 0; mb < RB; ++mb) {
           float mx = -INFINITY;
@@ -450,9 +550,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_kernel(AttnArgs a) {
           mref[mb] = fmaxf(mref[mb], xmax16_32(mx) * a.c);
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
-    mset = true;
     run();
   }
   if (err) raise_err(a.dev_err, err);
@@ -460,7 +559,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_kernel(AttnArgs a) {
   if (!active) return;
 #pragma unroll
   for (int mb = 0; mb < RB; ++mb) {
-    const float l = xsum16_32(lrun[mb]);
+    const float l = lsum[mb][0];
     const int m = row0 + 16 * mb + col;
     if (m < a.rows) {
       const int i = m / a.grp;
@@ -552,19 +651,17 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
 template <int D, int RB>
 void launch_split(const AttnArgs& args, dim3 grid, hipStream_t stream) {
   if (args.max_blocks)
-    hipLaunchKernelGGL((attn_split_kernel<D, RB, true>), grid, dim3(kThreads), 0, stream, args);
+    hipLaunchKernelGGL((attn_split_kernel<D, RB, true>), grid, dim3(kSplitThreads), 0, stream, args);
   else
-    hipLaunchKernelGGL((attn_split_kernel<D, RB, false>), grid, dim3(kThreads), 0, stream, args);
+    hipLaunchKernelGGL((attn_split_kernel<D, RB, false>), grid, dim3(kSplitThreads), 0, stream, args);
 }
 
 template <int D>
 void launch_split_rb(int rb, const AttnArgs& args, dim3 grid, hipStream_t stream) {
-  switch (rb) {
-    case 1: launch_split<D, 1>(args, grid, stream); break;
-    case 2: launch_split<D, 2>(args, grid, stream); break;
-    case 3: launch_split<D, 3>(args, grid, stream); break;
-    default: launch_split<D, 4>(args, grid, stream); break;
-  }
+  if (rb == 1)
+    launch_split<D, 1>(args, grid, stream);
+  else
+    launch_split<D, 2>(args, grid, stream);
 }
 
 }  // namespace
@@ -573,10 +670,10 @@ AttnPlan plan_attention(const tv_attn_desc& d, int cu_count) {
   AttnPlan p{};
   const int grp = d.n_q_heads / d.n_kv_heads;
   p.rows = d.n_nodes * grp;
-  p.row_groups = (p.rows + 255) / 256;
+  // a workgroup covers 16 * kWaves * RB rows, RB in {1, 2}
+  p.row_groups = (p.rows + 16 * kWaves * 2 - 1) / (16 * kWaves * 2);
   const int per_group = (p.rows + p.row_groups - 1) / p.row_groups;
-  p.row_blocks = (per_group + 63) / 64;
-  if (p.row_blocks < 1) p.row_blocks = 1;
+  p.row_blocks = per_group <= 16 * kWaves ? 1 : 2;
   p.prefix_slots = d.max_blocks ? d.max_blocks * d.block_size : d.max_prefix_len;
   const int units = d.batch * d.n_kv_heads * p.row_groups;
   int splits;
@@ -590,6 +687,11 @@ AttnPlan plan_attention(const tv_attn_desc& d, int cu_count) {
   }
   int chunk = p.prefix_slots > 0 ? (p.prefix_slots + splits - 1) / splits : kTile;
   chunk = ((chunk + kTile - 1) / kTile) * kTile;
+  if (d.max_blocks) {
+    // the block ids a split touches must fit its LDS table
+    const int64_t lim = std::max<int64_t>(kTile, ((kBlkCache - 2) * (int64_t)d.block_size / kTile) * kTile);
+    if (chunk > lim) chunk = (int)lim;
+  }
   p.chunk = chunk;
   p.splits = p.prefix_slots > 0 ? (p.prefix_slots + chunk - 1) / chunk : 1;
   const size_t parts = (size_t)d.batch * (p.splits + 1) * d.n_nodes * d.n_q_heads;
