@@ -181,6 +181,28 @@ def test_attention_bad_block_is_skipped():
     assert int(err.item()) & binding.DERR_BAD_BLOCK
 
 
+def test_attention_tree_split_with_only_invalid_blocks():
+    # The last prefix split also runs the tree block.  Here every block id of
+    # that split is invalid, so it must still produce the tree's partial.
+    _say("[attention] last split all-invalid blocks, tree still attended")
+    wl = W.make_random_case(33, batch=1, n_nodes=9, hq=8, hkv=2, d=128, prefix_lens=[300],
+                            block_size=32, blocks_per_seq=4)
+    good = wl.block_idx.copy()
+    dw = DevWorkload(wl)
+    bad = np.concatenate([good, np.array([[-1, 1000, -7, 99]], dtype=np.int32)], axis=1)
+    dw.block_idx = dev_i32(bad)
+    dw.n_blocks = dev_i32(np.array([8], dtype=np.int32))
+    wl.block_idx = bad
+    mask, _ = binding.build_tree_mask(dw.parents)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = dw.attention(mask, partial=True, dev_err=err, num_splits=2)
+    torch.cuda.synchronize()
+    wl.block_idx, wl.n_blocks = good, np.array([4], dtype=np.int32)
+    ref, _ = oracle_attention(wl, partial=True)
+    check_attention_close(out, ref, "tree-split-invalid-blocks")
+    assert int(err.item()) & binding.DERR_BAD_BLOCK
+
+
 # ---------------------------------------------------------------------------
 # a5-a6 acceptance
 # ---------------------------------------------------------------------------

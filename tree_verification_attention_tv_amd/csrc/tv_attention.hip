@@ -14,21 +14,26 @@
 //    of 16 rows.  Two waves per SIMD are needed to keep the matrix core
 //    busy: a single wave issues dependent-free MFMAs at well under peak.
 //  * The prefix (full rows, or the listed blocks) is cut into `splits`
-//    contiguous ranges; the tree block is one more split whose tiles are
-//    masked with the packed ancestor bits.  A combine kernel merges the
-//    (max, sum, unnormalised output) partials in a fixed order.
-//  * 32-token K/V tiles flow HBM -> registers -> LDS through a 3-slot LDS
-//    ring with two register stages, so two tiles are in flight per CU.  LDS
-//    rows are padded (K: D+8, V: D+16 elements) so that the 16-byte K reads
-//    and the 8-byte transposing V reads below are free of bank conflicts,
-//    and every operand address is a per-lane base plus an immediate.
+//    contiguous ranges, one workgroup each, with `splits` chosen so that the
+//    grid fits the CUs in one round.  The workgroup of the last non-empty
+//    range also runs the tree block's tiles, masked with the packed ancestor
+//    bits, after its prefix tiles.  A combine kernel merges the (max, sum,
+//    unnormalised output) partials in a fixed order.
+//  * 32-token K/V tiles go from HBM straight to LDS with LDS DMA
+//    (global_load_lds_dwordx4) into a 4-slot ring, two tiles in flight, with
+//    no staging registers.  The tile layout in LDS (column blocks, below)
+//    keeps the K and V operand reads free of bank conflicts and makes every
+//    operand address one per-lane base plus an immediate.
 //  * S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_16x16x32_bf16.  The
 //    S^T accumulator gives every lane one query row and four tokens, so row
-//    statistics need two cross-lane steps; P^T is packed to bf16 straight
-//    from those registers as the B operand of the PV product, and the V^T
-//    A operand comes from ds_read_b64_tr_b16 (two per operand).
-//  * Software pipeline: QK of tile i+1 is issued before the softmax of tile
-//    i, so MFMA work overlaps the VALU softmax.
+//    statistics need two cross-lane steps (the row sum only once, at the
+//    end: each lane accumulates its share in fp32 before p is rounded).
+//    P^T is packed to bf16 straight from those registers as the B operand
+//    of the PV product, and the V^T A operand comes from ds_read_b64_tr_b16
+//    (two per operand).
+//  * Software pipeline: each step first issues all LDS operand reads (K of
+//    tile i+1, V of tile i), then the softmax of tile i, then the QK chains
+//    of tile i+1 interleaved with the independent PV products of tile i.
 //  * Softmax in fp32, log2 domain (scale * log2 e folded into one FMA
 //    before v_exp_f32).  Each row's reference max is fixed at the first tile
 //    in which the row sees a key, so the hot loop never rescales the output
@@ -117,6 +122,13 @@ __device__ __forceinline__ void lds_barrier() {
 // Reductions over the four 16-lane groups (lanes l, l^16, l^32, l^48) with
 // the gfx950 row-swap permutes: after swapping, the two results of each
 // swap hold the value of a lane and of its partner.
+__device__ __forceinline__ float xsum16_32(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ float xmax16_32(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
@@ -137,17 +149,17 @@ __device__ __forceinline__ void dma16(uint32_t lds_addr, const void* gptr) {
                : "memory");
 }
 
+// Same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane offset.
+__device__ __forceinline__ void dma16s(uint32_t lds_addr, const void* sbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(sbase)
+               : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void vm_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-
-// XOR swizzle of the 16-byte chunks of tile row t (CH chunks per row): keeps
-// the 16-byte K fragment reads and the 8-byte transposing V reads free of
-// bank conflicts on unpadded 256-byte rows.
-template <int CH>
-__device__ __forceinline__ int swz(int t) {
-  return (2 * t + (t >> 2)) & (CH - 1);
 }
 
 constexpr int kRing = 4;        // LDS ring slots (tiles)
@@ -155,14 +167,12 @@ constexpr int kBlkCache = 1024; // block ids of one split staged in LDS
 
 template <int D, int RB, bool PARTIAL>
 __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a) {
-  constexpr int CH = D / 8;                 // 16-byte chunks per row
   constexpr int ROWB = D * 2;               // bytes per row
   constexpr int DC = D / 32;                // k-steps of the QK^T product
   constexpr int DB = D / 16;                // 16-wide output blocks of PV
   constexpr int TILE_B = kTile * ROWB;      // bytes of one K (or V) tile
   constexpr int SLOT_B = 2 * TILE_B;        // K tile then V tile
-  constexpr int RPI = 64 / CH;              // tile rows per DMA instruction
-  constexpr int IPT = kTile / RPI;          // DMA instructions per tensor per tile
+  constexpr int IPT = D / 16;               // DMA instructions (1 KB column blocks) per tensor per tile
   constexpr int DPT = 2 * IPT / kWaves;     // DMA instructions per wave per tile
   static_assert(DPT == 1 || DPT == 2, "DMA split across waves");
 
@@ -177,56 +187,55 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int col = lane & 15;   // MFMA column (query row within a block)
   const int grp4 = lane >> 4;  // lane group 0..3
-  const bool tree = (s == a.splits);
-  const bool part = PARTIAL && !tree;
 
   int err = 0;
   const int p_len = clamped_prefix(a, b, &err);
   const int slots = prefix_slots(a, b, p_len, &err);
-  int begin, end;
-  if (tree) {
-    begin = 0;
-    end = a.n;
-  } else {
-    begin = s * a.chunk;
-    end = min(begin + a.chunk, slots);
-  }
   if (err && s == 0 && g == 0 && rg == 0 && tid == 0) raise_err(a.dev_err, err);
   err = 0;
-  if (begin >= end) return;  // uniform over the workgroup
+  // Prefix range of this split.  The last non-empty split of the sequence
+  // (split 0 when the prefix is empty) also takes the tree block, after its
+  // prefix tiles: no workgroup is spent on the tree alone.
+  const int ns = (slots + a.chunk - 1) / a.chunk;
+  const bool has_tree = s == max(ns - 1, 0);
+  const int begin = s * a.chunk;
+  const int end = min(begin + a.chunk, slots);
+  int np = begin < end ? (end - begin + kTile - 1) / kTile : 0;  // prefix tiles
+  const int nt = has_tree ? (a.n + kTile - 1) / kTile : 0;       // tree tiles
+  if (np == 0 && nt == 0) return;  // uniform over the workgroup
 
   const int wg_row0 = rg * (16 * kWaves * RB);
   const int row0 = wg_row0 + wave * (16 * RB);
   const bool active = row0 < a.rows;
   const int node0 = wg_row0 / a.grp;
 
-  // ---- source rows --------------------------------------------------------
-  const char* kbytes;
-  const char* vbytes;
-  int src_rowb;  // bytes between consecutive tokens in the source
-  if (tree) {
-    kbytes = reinterpret_cast<const char*>(a.k_tree + ((int64_t)b * a.n * a.hkv + g) * D);
-    vbytes = reinterpret_cast<const char*>(a.v_tree + ((int64_t)b * a.n * a.hkv + g) * D);
-    src_rowb = a.hkv * ROWB;
-  } else {
-    kbytes = reinterpret_cast<const char*>(a.k_cache + b * a.seq_stride + (int64_t)g * a.cap * D);
-    vbytes = reinterpret_cast<const char*>(a.v_cache + b * a.seq_stride + (int64_t)g * a.cap * D);
-    src_rowb = ROWB;
-  }
+  // ---- sources --------------------------------------------------------------
+  const char* kc = reinterpret_cast<const char*>(a.k_cache + b * a.seq_stride + (int64_t)g * a.cap * D);
+  const char* vc = reinterpret_cast<const char*>(a.v_cache + b * a.seq_stride + (int64_t)g * a.cap * D);
+  const char* kt = reinterpret_cast<const char*>(a.k_tree + ((int64_t)b * a.n * a.hkv + g) * D);
+  const char* vt = reinterpret_cast<const char*>(a.v_tree + ((int64_t)b * a.n * a.hkv + g) * D);
+  const int64_t tree_rowb = (int64_t)a.hkv * ROWB;  // bytes between tree nodes
+
+  // partial rows of this split: ((b * splits + s) * n + i) * hq + h
+  auto part_index = [&](int m) -> int64_t {
+    const int i = m / a.grp;
+    const int h = g * a.grp + m % a.grp;
+    return (((int64_t)b * a.splits + s) * a.n + i) * a.hq + h;
+  };
 
   // ---- per-split tables staged in LDS --------------------------------------
-  int bi0 = 0;      // partial: first block index of the split
-  int fb_row = begin;  // a row of this split that is valid (stands in for empty slots)
-  if (tree) {
+  int bi0 = 0;         // partial: first block index of the split
+  int fb_row = begin;  // a valid prefix row of this split (stands in for empty slots)
+  if (has_tree) {
     const int node1 = min(a.n, (wg_row0 + 16 * kWaves * RB + a.grp - 1) / a.grp);
     const int cnt = (node1 - node0) * a.words;
     const uint32_t* src = a.mask + ((int64_t)b * a.n + node0) * a.words;
     for (int k = tid; k < cnt; k += kSplitThreads) smask[k] = src[k];
   }
-  if (part) {
+  if (PARTIAL && np > 0) {
     const int32_t* blist = a.block_idx + (int64_t)b * a.max_blocks;
     bi0 = begin / a.block_size;
     const int bi1 = (end - 1) / a.block_size;
@@ -242,28 +251,29 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
     __syncthreads();
     const int first = s_first;
     if (first == INT32_MAX) {
-      // no valid slot in this split: an empty partial
-      if (err) raise_err(a.dev_err, err);
-      for (int mb = 0; mb < RB; ++mb) {
-        const int m = row0 + 16 * mb + col;
-        if (active && m < a.rows && grp4 == 0) {
-          const int i = m / a.grp;
-          const int h = g * a.grp + m % a.grp;
-          const int64_t pi = (((int64_t)b * (a.splits + 1) + s) * a.n + i) * a.hq + h;
-          a.part_ml[pi] = make_float2(-INFINITY, 0.f);
+      // no valid slot in the split's prefix range
+      if (!has_tree) {
+        // an empty partial
+        if (err) raise_err(a.dev_err, err);
+        for (int mb = 0; mb < RB; ++mb) {
+          const int m = row0 + 16 * mb + col;
+          if (active && m < a.rows && grp4 == 0) a.part_ml[part_index(m)] = make_float2(-INFINITY, 0.f);
         }
+        return;
       }
-      return;
+      np = 0;
+    } else {
+      fb_row = blist[bi0 + first] * a.block_size;
     }
-    fb_row = blist[bi0 + first] * a.block_size;
   }
-  // cache row of slot u of this split, fb_row when the slot is empty
+  const int ntiles = np + nt;
+  // cache row of prefix slot u, fb_row when the slot is empty
   auto slot_row = [&](int u, bool& valid) -> int {
     if (u >= end) {
       valid = false;
       return fb_row;
     }
-    if (!part) {
+    if (!PARTIAL) {
       valid = true;
       return u;
     }
@@ -274,41 +284,81 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
     return valid ? row : fb_row;
   };
 
-  // ---- DMA of one tile into a ring slot ------------------------------------
-  // DMA instruction q of a tensor covers tile rows RPI*q .. RPI*q+RPI-1; lane
-  // i fills physical chunk (i % CH) of row RPI*q + i/CH, i.e. the logical
-  // chunk (i % CH) ^ swz(row).
+  // ---- tile layout in LDS and its DMA ------------------------------------
+  // A K (or V) tile is stored as D/16 column blocks of 1 KB; block cb holds
+  // columns 16cb..16cb+15 of the 32 tokens, 32 bytes per token.  The
+  // 16-byte K reads of a wave then cover two contiguous 512-byte runs and
+  // the transposing V reads 128 contiguous bytes per 16 lanes, both at the
+  // full LDS rate on gfx950 (measured: 16-byte reads at ~250 B/clk per CU,
+  // transposing 8-byte reads at ~125), and every operand read is one
+  // per-lane base plus an immediate.  DMA instruction cb of a tensor fills
+  // block cb: lane i writes 16-byte slot i, i.e. token i/2, half i&1.
   const uint32_t ring_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)ring;
-  int dq[DPT], dt[DPT];       // instruction index and tensor (0 = K, 1 = V)
-  int dr[DPT];                // tile row of this lane
-  uint32_t dcol[DPT];         // byte offset of this lane's logical chunk
+  const int dtok = lane >> 1;                               // token of this lane's DMA slot
+  const int dhalf = lane & 1;                               // 16-byte half it carries
+  int dt[DPT];        // tensor of the instruction (0 = K, 1 = V)
+  uint32_t ddst[DPT]; // slot-relative LDS byte offset of the instruction
+  uint32_t dcol[DPT]; // byte offset of the lane's 16 bytes within the source row
 #pragma unroll
   for (int k = 0; k < DPT; ++k) {
     const int inst = wave * DPT + k;  // 0 .. 2*IPT-1
+    const int cb = inst % IPT;
     dt[k] = inst / IPT;
-    dq[k] = inst % IPT;
-    dr[k] = RPI * dq[k] + lane / CH;
-    dcol[k] = 16u * (uint32_t)((lane % CH) ^ swz<CH>(dr[k]));
+    ddst[k] = dt[k] * TILE_B + cb * 1024;
+    dcol[k] = 16u * (2 * cb + dhalf);
   }
-  auto dma_tile = [&](int slot, int t0) {
+  // Whole prefix tiles of full mode read 32 consecutive rows: a scalar base
+  // per tile plus a fixed per-lane offset.
+  const int nfull = PARTIAL ? 0 : (end - begin) / kTile;
+  uint32_t fvoff[DPT];      // per-lane offset within the tile's rows
+  const char* fbase[DPT];   // source of tile 0 (wave-uniform)
+  uint32_t fdst[DPT];       // LDS address in slot 0 (wave-uniform)
 #pragma unroll
-    for (int k = 0; k < DPT; ++k) {
+  for (int k = 0; k < DPT; ++k) {
+    fvoff[k] = dtok * ROWB + dcol[k];
+    fbase[k] = (dt[k] ? vc : kc) + (int64_t)begin * ROWB;
+    fdst[k] = __builtin_amdgcn_readfirstlane(ring_base + ddst[k]);
+  }
+  // Tile it of the split: prefix tiles 0..np-1, then tree tiles.  Tiles past
+  // the end (prefetched, then discarded) re-read the last tree node.
+  auto dma_tile = [&](int slot, int it) {
+    if (it < nfull) {
+#pragma unroll
+      for (int k = 0; k < DPT; ++k)
+        dma16s(fdst[k] + slot * SLOT_B, fbase[k] + (int64_t)it * (kTile * ROWB), fvoff[k]);
+      return;
+    }
+    const char* kb;
+    const char* vb;
+    int64_t off;
+    if (it < np) {
       bool valid;
-      const int row = slot_row(t0 + dr[k], valid);
-      const char* src = (dt[k] ? vbytes : kbytes) + (uint32_t)row * (uint32_t)src_rowb + dcol[k];
-      const uint32_t dst = ring_base + slot * SLOT_B + dt[k] * TILE_B + dq[k] * 1024;
-      dma16(__builtin_amdgcn_readfirstlane(dst), src);
+      off = (int64_t)slot_row(begin + it * kTile + dtok, valid) * ROWB;
+      kb = kc;
+      vb = vc;
+    } else {
+      off = (int64_t)min((it - np) * kTile + dtok, a.n - 1) * tree_rowb;
+      kb = kt;
+      vb = vt;
     }
+#pragma unroll
+    for (int k = 0; k < DPT; ++k)
+      dma16(__builtin_amdgcn_readfirstlane(ring_base + slot * SLOT_B + ddst[k]),
+            (dt[k] ? vb : kb) + off + dcol[k]);
   };
-  // validity bits of the 32 slots of the tile starting at t0 (wave-uniform)
-  auto tile_bits = [&](int t0) -> uint32_t {
-    if (!part) {
-      const int cnt = end - t0;
-      return cnt >= kTile ? 0xFFFFFFFFu : (cnt <= 0 ? 0u : ((1u << cnt) - 1u));
+  // validity bits of the 32 slots of tile it (wave-uniform)
+  auto tile_bits = [&](int it) -> uint32_t {
+    int cnt;
+    if (it >= np) {
+      cnt = a.n - (it - np) * kTile;
+    } else if (!PARTIAL) {
+      cnt = end - (begin + it * kTile);
+    } else {
+      bool valid = false;
+      if (lane < kTile) slot_row(begin + it * kTile + lane, valid);
+      return (uint32_t)__ballot(valid);
     }
-    bool valid = false;
-    if (lane < kTile) slot_row(t0 + lane, valid);
-    return (uint32_t)__ballot(valid);
+    return cnt >= kTile ? 0xFFFFFFFFu : (cnt <= 0 ? 0u : ((1u << cnt) - 1u));
   };
 
   // ---- Q^T fragments (B operand of S^T = K Q^T) ----------------------------
@@ -328,70 +378,66 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
   // be placed inside the loop (vmcnt(0), draining the tile DMA each step).
   __builtin_amdgcn_s_waitcnt(0x0F70);  // gfx9 encoding: vmcnt(0)
 
-  // ---- LDS operand offsets (per lane, slot relative) -----------------------
-  // K fragment (tb, dc): row tb*16 + col, logical chunk 4*dc + grp4.
-  uint32_t koff[2][DC];
-#pragma unroll
-  for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
-      const int t = tb * 16 + col;
-      koff[tb][dc] = t * ROWB + 16 * ((4 * dc + grp4) ^ swz<CH>(t));
-    }
-  // V^T fragment (db, half): ds_read_b64_tr_b16 gives, in each 16-lane group,
-  // lane i element i%4 of the 8-byte chunks addressed by lanes 4k + i/4
-  // (k = 0..3); lane 4k + qq addresses token base + k, columns 4qq..4qq+3.
-  // k-slot j of lane group q is token 4q+j (j<4) or 16+4q+(j-4): the tokens
-  // the lane holds in the S^T accumulators.
-  uint32_t voff[DB][2];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int t = 16 * hf + 4 * grp4 + (col >> 2);
-      const int c = 2 * db + ((col & 3) >> 1);
-      voff[db][hf] = TILE_B + t * ROWB + 16 * (c ^ swz<CH>(t)) + 8 * (col & 1);
-    }
+  // ---- LDS operand addressing ----------------------------------------------
+  // K fragment (tb, dc): token 16tb + col, columns 32dc + 8grp4 .. +7, i.e.
+  // block 2dc + grp4/2, half grp4&1 -> kbase + 2048 dc + 512 tb.
+  const uint32_t kbase = 1024u * (grp4 >> 1) + 32u * col + 16u * (grp4 & 1);
+  // V^T fragment (db, hf): ds_read_b64_tr_b16 gives, in each 16-lane group,
+  // lane i element i%4 of the 8-byte pieces addressed by lanes 4k + i/4
+  // (k = 0..3).  Lane 4kk + qq addresses token 16hf + 4grp4 + kk, columns
+  // 16db + 4qq .. +3, so lane i receives column 16db + i of tokens
+  // 16hf + 4grp4 + 0..3: k-slot j of lane group q is token 4q+j (j<4) or
+  // 16+4q+(j-4), the tokens the lane holds in the S^T accumulators.
+  // Address: vbase + 1024 db + 512 hf.
+  const uint32_t vbase = TILE_B + 32u * (4 * grp4 + (col >> 2)) + 16u * ((col & 3) >> 1) + 8u * (col & 1);
 
   typedef __attribute__((address_space(3))) char lds_char;
   auto lds_at = [&](uint32_t addr) { return (lds_char*)(uintptr_t)addr; };
+  auto kfrag = [&](uint32_t slot_addr, int tb, int dc) -> bf16x8 {
+    return *(__attribute__((address_space(3))) const bf16x8*)lds_at(slot_addr + kbase + 2048 * dc + 512 * tb);
+  };
+  auto vfrag = [&](uint32_t slot_addr, int db) -> bf16x8 {
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)lds_at(slot_addr + vbase + 1024 * db));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)lds_at(slot_addr + vbase + 1024 * db + 512));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
 
   // ---- per-tile math --------------------------------------------------------
   // S^T for one tile: sacc[tb][mb][r] = score of token tb*16 + 4*grp4 + r,
   // row row0 + 16*mb + col.  The first k-step starts from a zero accumulator.
-  auto qk_tile = [&](int slot, f32x4 (&sacc)[2][RB]) {
-    const uint32_t base = ring_base + slot * SLOT_B;
-    bf16x8 kf[2][2];
+  auto qk_mfma = [&](const bf16x8 (&kf)[DC][2], f32x4 (&sacc)[2][RB], int dc) {
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
-      kf[0][tb] = *(__attribute__((address_space(3))) const bf16x8*)lds_at(base + koff[tb][0]);
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
-      if (dc + 1 < DC) {
+      for (int mb = 0; mb < RB; ++mb)
+        sacc[tb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            kf[dc][tb], qf[mb][dc], dc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[tb][mb], 0, 0, 0);
+  };
+  auto qk_tile = [&](int slot, f32x4 (&sacc)[2][RB]) {
+    const uint32_t sa = ring_base + slot * SLOT_B;
+    bf16x8 kf[DC][2];
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-          kf[(dc + 1) & 1][tb] =
-              *(__attribute__((address_space(3))) const bf16x8*)lds_at(base + koff[tb][dc + 1]);
-      }
+    for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
+      for (int tb = 0; tb < 2; ++tb) kf[dc][tb] = kfrag(sa, tb, dc);
 #pragma unroll
-        for (int mb = 0; mb < RB; ++mb)
-          sacc[tb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              kf[dc & 1][tb], qf[mb][dc], dc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[tb][mb], 0, 0, 0);
-    }
+    for (int dc = 0; dc < DC; ++dc) qk_mfma(kf, sacc, dc);
   };
 
   // -inf for tokens outside the tile's valid set (and, in the tree block,
   // outside the row's ancestor set)
-  auto mask_tile = [&](uint32_t vbits, int tile_idx, f32x4 (&sacc)[2][RB]) {
-    if (!tree && vbits == 0xFFFFFFFFu) return;
+  auto mask_tile = [&](int it, f32x4 (&sacc)[2][RB]) {
+    const uint32_t vbits = tile_bits(it);
+    const bool tt = it >= np;  // a tree tile
+    if (!tt && vbits == 0xFFFFFFFFu) return;
 #pragma unroll
     for (int mb = 0; mb < RB; ++mb) {
       uint32_t allow = vbits;
-      if (tree) {
+      if (tt) {
         const int m = row0 + 16 * mb + col;
-        allow &= m < a.rows ? smask[(m / a.grp - node0) * a.words + tile_idx] : 0u;
+        allow &= m < a.rows ? smask[(m / a.grp - node0) * a.words + (it - np)] : 0u;
       }
       allow >>= 4 * grp4;
 #pragma unroll
@@ -403,7 +449,7 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
   };
 
   f32x4 o[RB][DB];
-  f32x4 lsum[RB];     // row sums of p, from an MFMA against a block of ones
+  float lpart[RB];    // this lane's share of the row sum of p (fp32, before rounding)
   float mref[RB];     // reference max per row (log2 units), -inf until set
 
   // p = 2^(s*c - mref) of one tile for row block mb, packed as the PV B
@@ -417,87 +463,145 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
       mref[mb] = mref[mb] == -INFINITY ? mx : mref[mb];
     }
     const float muse = (mref[mb] == -INFINITY) ? 0.f : mref[mb];
-    bf16x8 pb;
+    float pv[8];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        pb[tb * 4 + r] = (bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[tb][mb][r], a.c, -muse));
+        pv[tb * 4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[tb][mb][r], a.c, -muse));
+    lpart[mb] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+    bf16x8 pb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pb[e] = (bf16)pv[e];
     return pb;
   };
 
-  bf16x8 ones;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = (bf16)1.0f;
-  auto pv_tile = [&](int slot, const bf16x8 (&pb)[RB]) {
-    const uint32_t base = ring_base + slot * SLOT_B;
-    auto vfrag = [&](int db) -> bf16x8 {
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)lds_at(base + voff[db][0]));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)lds_at(base + voff[db][1]));
-      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    bf16x8 vf[2];
-    vf[0] = vfrag(0);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      if (db + 1 < DB) vf[(db + 1) & 1] = vfrag(db + 1);
-#pragma unroll
-      for (int mb = 0; mb < RB; ++mb)
-        o[mb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db & 1], pb[mb], o[mb][db], 0, 0, 0);
-    }
+  auto pv_mfma = [&](const bf16x8 (&vf)[DB], const bf16x8 (&pb)[RB], int db) {
 #pragma unroll
     for (int mb = 0; mb < RB; ++mb)
-      lsum[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[mb], lsum[mb], 0, 0, 0);
+      o[mb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pb[mb], o[mb][db], 0, 0, 0);
   };
 
   // ---- pipeline -------------------------------------------------------------
   // Tile t lives in ring slot t % 4.  Three tiles are requested before the
-  // loop; step it waits for tile it+1 (the older of its two outstanding
-  // tiles), passes a barrier (which also frees the slot of tile it-1), asks
-  // for tile it+3, then computes: softmax of tile it, QK of tile it+1, PV of
-  // tile it.  Tiles past the range re-read a valid row and are discarded.
-  const int ntiles = (end - begin + kTile - 1) / kTile;
+  // loop; step s waits for tile s+1 (the older of its two outstanding
+  // tiles), passes the workgroup barrier (after which the slot of tile s-1 is
+  // free) and asks for tile s+3.  The math of a tile is split in two halves:
+  //   R(s): read the operands of M(s) from LDS (K of tile s+1, V of tile s),
+  //         mask and softmax the scores S(s);
+  //   M(s): QK of tile s+1 -> S(s+1), then PV of tile s.
+  // Waves 0-3 (one per SIMD) run R(s) then M(s) in step s; waves 4-7 run
+  // M(s-1) then R(s).  On every SIMD one wave is then on the matrix core
+  // while the other uses LDS and the VALU.  All LDS reads of tile s finish
+  // before the barrier of step s+1, so the slot reuse above is safe.  Tiles
+  // past the end are prefetched (from valid rows) and never used.
+  const bool lead = wave < kWaves / 2;
 
   auto run = [&]() {
 #pragma unroll
     for (int mb = 0; mb < RB; ++mb) {
-      lsum[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      lpart[mb] = 0.f;
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[mb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    dma_tile(0, begin);
-    dma_tile(1, begin + kTile);
-    dma_tile(2, begin + 2 * kTile);
+    dma_tile(0, 0);
+    dma_tile(1, 1);
+    dma_tile(2, 2);
     vm_wait<2 * DPT>();
     lds_barrier();
 
     f32x4 sA[2][RB], sB[2][RB];
-    if (active) {
-      qk_tile(0, sA);
-      mask_tile(tile_bits(begin), 0, sA);
-    }
+    bf16x8 kf[DC][2], vf[DB], pb[RB];
+    if (active) qk_tile(0, sA);
 
-    auto step = [&](auto track_tag, int it, f32x4 (&cur)[2][RB], f32x4 (&nxt)[2][RB]) {
+    // operand reads of M(s): K of tile s+1, V of tile s
+    auto read_k = [&](int s) {
+      const uint32_t ka = ring_base + ((s + 1) % kRing) * SLOT_B;
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) kf[dc][tb] = kfrag(ka, tb, dc);
+    };
+    auto read_v = [&](int s) {
+      const uint32_t va = ring_base + (s % kRing) * SLOT_B;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) vf[db] = vfrag(va, db);
+    };
+    auto soft = [&](auto track_tag, int s, f32x4 (&cur)[2][RB]) {
+      mask_tile(s, cur);
+#pragma unroll
+      for (int mb = 0; mb < RB; ++mb) pb[mb] = softmax_block(cur, mb, track_tag);
+    };
+    auto qk = [&](f32x4 (&nxt)[2][RB]) {
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) qk_mfma(kf, nxt, dc);
+    };
+    auto pv = [&]() {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) pv_mfma(vf, pb, db);
+    };
+#define TV_SCHED_FENCE __builtin_amdgcn_sched_barrier(0)
+    // b1: tile s+1 has landed for every wave; the slot of tile s-1 is free
+    auto sync = [&](int s) {
       vm_wait<DPT>();
       lds_barrier();
-      dma_tile((it + 3) % kRing, begin + (it + 3) * kTile);
-      if (active) {
-        bf16x8 pb[RB];
-#pragma unroll
-        for (int mb = 0; mb < RB; ++mb) pb[mb] = softmax_block(cur, mb, track_tag);
-        qk_tile((it + 1) % kRing, nxt);
-        pv_tile(it % kRing, pb);
-        if (it + 1 < ntiles) mask_tile(tile_bits(begin + (it + 1) * kTile), it + 1, nxt);
-      }
+      dma_tile((s + 3) % kRing, s + 3);
     };
-    // the first tile sets each row's reference max
-    step(std::true_type{}, 0, sA, sB);
-    for (int it = 1; it < ntiles; it += 2) {
-      step(std::false_type{}, it, sB, sA);
-      if (it + 1 < ntiles) step(std::false_type{}, it + 1, sA, sB);
+    // b2: mid-step barrier that only keeps the two groups half a step apart
+    // (no data hand-off: outstanding LDS reads may cross it)
+    auto half_sync = [&]() {
+      TV_SCHED_FENCE;
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      TV_SCHED_FENCE;
+    };
+    // R(s): operand reads first (their latency hides behind the softmax)
+    auto R = [&](auto track_tag, int s, f32x4 (&cur)[2][RB]) {
+      read_k(s);
+      read_v(s);
+      TV_SCHED_FENCE;
+      soft(track_tag, s, cur);
+      TV_SCHED_FENCE;
+    };
+    auto M = [&](int s, f32x4 (&nxt)[2][RB]) {
+      if (s + 1 < ntiles) qk(nxt);
+      pv();
+      TV_SCHED_FENCE;
+    };
+    // Each group runs its own loop (separate register allocation); both pass
+    // the same 2 (ntiles + 1) barriers.  S(s) of even s lives in sA, odd in sB.
+    if (lead) {
+      // b1 R(s) b2 M(s)
+      auto step = [&](auto track_tag, int s, f32x4 (&cur)[2][RB], f32x4 (&nxt)[2][RB]) {
+        sync(s);
+        const bool work = active && s < ntiles;
+        if (work) R(track_tag, s, cur);
+        half_sync();
+        if (work) M(s, nxt);
+      };
+      step(std::true_type{}, 0, sA, sB);
+      for (int s = 1; s <= ntiles; s += 2) {
+        step(std::false_type{}, s, sB, sA);
+        if (s + 1 <= ntiles) step(std::false_type{}, s + 1, sA, sB);
+      }
+    } else {
+      // b1 M(s-1) b2 R(s); M(s-1) writes S(s) into cur, R(s) consumes it
+      auto step = [&](int s, f32x4 (&cur)[2][RB]) {
+        sync(s);
+        if (active) M(s - 1, cur);
+        half_sync();
+        if (active && s < ntiles) R(std::false_type{}, s, cur);
+      };
+      sync(0);
+      half_sync();
+      if (active) R(std::true_type{}, 0, sA);
+      for (int s = 1; s <= ntiles; s += 2) {
+        step(s, sB);
+        if (s + 1 <= ntiles) step(s + 1, sA);
+      }
     }
+#undef TV_SCHED_FENCE
     vm_wait<0>();   // the requests past the last tile
     lds_barrier();
   };
@@ -514,7 +618,7 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
     bool bad = false;
 #pragma unroll
     for (int mb = 0; mb < RB; ++mb) {
-      const float l = lsum[mb][0];
+      const float l = xsum16_32(lpart[mb]);
       bool fin = true;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -533,13 +637,13 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
 #pragma unroll
     for (int mb = 0; mb < RB; ++mb) mref[mb] = -INFINITY;
     for (int it = 0; it < ntiles; ++it) {
-      dma_tile(0, begin + it * kTile);
+      dma_tile(0, it);
       vm_wait<0>();
       lds_barrier();
       if (active) {
         f32x4 sc[2][RB];
         qk_tile(0, sc);
-        mask_tile(tile_bits(begin + it * kTile), it, sc);
+        mask_tile(it, sc);
 #pragma unroll
         for (int mb = 0; mb < RB; ++mb) {
           float mx = -INFINITY;
@@ -559,12 +663,10 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
   if (!active) return;
 #pragma unroll
   for (int mb = 0; mb < RB; ++mb) {
-    const float l = lsum[mb][0];
+    const float l = xsum16_32(lpart[mb]);
     const int m = row0 + 16 * mb + col;
     if (m < a.rows) {
-      const int i = m / a.grp;
-      const int h = g * a.grp + m % a.grp;
-      const int64_t pi = (((int64_t)b * (a.splits + 1) + s) * a.n + i) * a.hq + h;
+      const int64_t pi = part_index(m);
       float* dst = a.part_o + pi * D + 4 * grp4;
 #pragma unroll
       for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db) = o[mb][db];
@@ -592,20 +694,16 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
   int err = 0;
   const int p_len = clamped_prefix(a, b, &err);
   const int slots = prefix_slots(a, b, p_len, &err);
-  const int ns = (slots + a.chunk - 1) / a.chunk;
-  const int64_t base = (int64_t)b * (a.splits + 1);
+  // splits 0..max(ns, 1)-1 hold partials (the last of them includes the tree)
+  const int cnt = max((slots + a.chunk - 1) / a.chunk, 1);
   const int64_t stride = (int64_t)a.n * a.hq;  // partial rows between splits
-  const int64_t p0 = (base * a.n + i) * a.hq + h;
-
-  // splits 0..ns-1 then the tree split
-  auto split_of = [&](int k) { return k < ns ? k : a.splits; };
-  const int cnt = ns + 1;
+  const int64_t p0 = (((int64_t)b * a.splits) * a.n + i) * a.hq + h;
   float m = -INFINITY;
   for (int k0 = 0; k0 < cnt; k0 += U) {
     float mv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      mv[u] = (k0 + u < cnt) ? a.part_ml[p0 + split_of(k0 + u) * stride].x : -INFINITY;
+      mv[u] = (k0 + u < cnt) ? a.part_ml[p0 + (k0 + u) * stride].x : -INFINITY;
 #pragma unroll
     for (int u = 0; u < U; ++u) m = fmaxf(m, mv[u]);
   }
@@ -624,7 +722,7 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (k0 + u < cnt) {
-          const int64_t pi = p0 + split_of(k0 + u) * stride;
+          const int64_t pi = p0 + (k0 + u) * stride;
           ml[u] = a.part_ml[pi];
           ov[u] = *reinterpret_cast<const f32x4*>(a.part_o + pi * D + 4 * dq);
         } else {
@@ -680,7 +778,9 @@ AttnPlan plan_attention(const tv_attn_desc& d, int cu_count) {
   if (d.num_splits > 0) {
     splits = d.num_splits;
   } else {
-    splits = (cu_count + units - 1) / units;
+    // one workgroup per CU (two waves per SIMD): a grid of at most cu_count
+    // workgroups runs in a single round
+    splits = cu_count / units;
     const int cap = (p.prefix_slots + kMinChunk - 1) / kMinChunk;
     if (splits > cap) splits = cap;
     if (splits < 1) splits = 1;
@@ -694,7 +794,7 @@ AttnPlan plan_attention(const tv_attn_desc& d, int cu_count) {
   }
   p.chunk = chunk;
   p.splits = p.prefix_slots > 0 ? (p.prefix_slots + chunk - 1) / chunk : 1;
-  const size_t parts = (size_t)d.batch * (p.splits + 1) * d.n_nodes * d.n_q_heads;
+  const size_t parts = (size_t)d.batch * p.splits * d.n_nodes * d.n_q_heads;
   p.ws_o_bytes = ((parts * d.head_dim * sizeof(float) + 255) / 256) * 256;
   p.ws_ml_bytes = ((parts * sizeof(float2) + 255) / 256) * 256;
   return p;
@@ -739,7 +839,7 @@ hipError_t launch_attention(const tv_attn_desc& d, const AttnPlan& plan, const t
   const float scale = d.softmax_scale > 0.f ? d.softmax_scale : 1.f / sqrtf((float)d.head_dim);
   a.c = scale * 1.44269504088896340736f;
 
-  const dim3 grid(plan.splits + 1, d.n_kv_heads * plan.row_groups, d.batch);
+  const dim3 grid(plan.splits, d.n_kv_heads * plan.row_groups, d.batch);
   if (d.head_dim == 128)
     launch_split_rb<128>(plan.row_blocks, a, grid, stream);
   else
