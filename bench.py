@@ -11,14 +11,26 @@ than cache bandwidth, the step rotates over enough independent copies of its
 inputs that their total exceeds the 256 MB Infinity Cache.
 
 Prints one JSON line (rank 0):
-  value = microseconds per verify step (lower is better); also KV GB/s,
-  a roofline entry for the dominant kernel (HIP-event timing of its own
-  launches) and the fp64 CPU oracle timed on a bounded sample.
+  value = microseconds per verify step (lower is better); KV GB/s; a roofline
+  entry for the dominant call (HIP-event timing of its own launches on the
+  stream they run on, algorithmic bytes, and the HBM traffic measured with
+  rocprofv3 counters when those were taken on the current kernel source);
+  the long-context (60K prefix) full and partial lines; the fp64 CPU oracle
+  timed on a bounded sample of the same workload.
+
+Helper modes (used to produce the committed profile summaries):
+  --copy-calibration      plain 256 MiB device copies, for scaling counters
+  --pmc-summary F W CF CW rocprofv3 FETCH_SIZE / WRITE_SIZE directories (bench
+                          run, copy run) -> traffic summary text on stdout
+  --trace-summary CSV CMD rocprofv3 kernel-stats CSV -> text summary on stdout
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +42,10 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
 MALL_BYTES = 256 * 1024 * 1024  # Infinity Cache
+COPY_BYTES = 256 * 1024 * 1024  # calibration copy size
+ATTN_SOURCE = os.path.join(ROOT, "tree_verification_attention_tv_amd", "csrc", "tv_attention.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_8b_layer_hbm_traffic.txt")
+ATTN_KERNELS = ("attn_split_kernel", "attn_combine_kernel")
 
 
 def parse():
@@ -44,8 +60,26 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the long-context (60K prefix) full/partial lines")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain 256 MiB device copies (for scaling HBM counters)")
+    ap.add_argument("--pmc-summary", nargs=4,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="summarise rocprofv3 FETCH_SIZE/WRITE_SIZE runs into a traffic text")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("STATS_CSV", "COMMAND"),
+                    help="condense a rocprofv3 kernel-stats CSV into a text summary")
     return ap.parse_args()
 
+
+def source_hash() -> str:
+    with open(ATTN_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# measurement
+# ---------------------------------------------------------------------------
 
 class InputSet:
     """One device copy of every input and output of a step."""
@@ -75,15 +109,188 @@ class InputSet:
                    if isinstance(t, torch.Tensor))
 
 
+class StepRunner:
+    """The four library calls of one verify step, on torch's current stream."""
+
+    def __init__(self, wl, partial, warm, num_splits, dev):
+        import numpy as np
+        import torch
+
+        from tree_verification_attention_tv_amd import binding
+
+        self.wl, self.partial, self.dev = wl, partial, dev
+        self.binding = binding
+        first = InputSet(wl, dev, torch, np)
+        rot = 1 if warm else max(2, int(np.ceil(1.25 * MALL_BYTES / first.nbytes())))
+        self.rot = min(rot, 64)
+        self.sets = [first] + [InputSet(wl, dev, torch, np) for _ in range(self.rot - 1)]
+        self.b, self.n = wl.parents.shape
+        self.num_splits = num_splits
+        self.desc = binding.attn_desc(first.q, first.k_cache, max_prefix_len=wl.max_prefix_len,
+                                      block_size=wl.block_size if partial else 0,
+                                      max_blocks=wl.max_blocks if partial else 0,
+                                      num_splits=num_splits)
+        self.ws_attn = torch.empty(binding.attention_workspace_size(self.desc), dtype=torch.uint8,
+                                   device=dev)
+        self.ws_acc = torch.empty(binding.accept_workspace_size(self.b, self.n, wl.vocab),
+                                  dtype=torch.uint8, device=dev)
+        self.acc_out = (torch.empty((self.b, self.n), dtype=torch.int32, device=dev),
+                        torch.empty((self.b,), dtype=torch.int32, device=dev),
+                        torch.empty((self.b, self.n), dtype=torch.int32, device=dev),
+                        torch.empty((self.b,), dtype=torch.int32, device=dev))
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.stream = torch.cuda.current_stream(dev)
+
+    # -- the four calls ------------------------------------------------------
+    def k_mask(self, s):
+        bd = self.binding
+        st = bd.lib().tv_build_tree_mask(bd._ptr(s.parents), self.b, self.n, bd._ptr(s.mask), None,
+                                         bd._ptr(self.err), bd._stream(self.dev))
+        if st:
+            raise bd.TVError("tv_build_tree_mask", st)
+
+    def k_attn(self, s):
+        wl, p = self.wl, self.partial
+        self.binding.tree_attention(
+            s.q, s.k_cache, s.v_cache, s.k_tree, s.v_tree, s.prefix_len, s.mask,
+            max_prefix_len=wl.max_prefix_len, block_idx=s.block_idx if p else None,
+            n_blocks=s.n_blocks if p else None, block_size=wl.block_size if p else 0,
+            num_splits=self.num_splits, out=s.out, workspace=self.ws_attn, dev_err=self.err)
+
+    def k_accept(self, s):
+        self.binding.greedy_accept(s.logits, s.parents, s.draft, workspace=self.ws_acc,
+                                   dev_err=self.err, outputs=self.acc_out)
+
+    def k_commit(self, s):
+        self.binding.commit_kv(s.k_tree, s.v_tree, self.acc_out[2], self.acc_out[1], s.prefix_len,
+                               s.k_cache, s.v_cache, new_prefix_len=s.new_prefix,
+                               dev_err=self.err)
+
+    def step(self, s):
+        self.k_mask(s)
+        self.k_attn(s)
+        self.k_accept(s)
+        self.k_commit(s)
+
+    # -- timing ----------------------------------------------------------------
+    def timed(self, fn, iters):
+        """Average microseconds of `fn` over `iters` back-to-back calls, from
+        HIP events recorded on the stream the library launches on."""
+        import torch
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(self.stream)
+        for k in range(iters):
+            fn(self.sets[k % self.rot])
+        z.record(self.stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(z) * 1e3 / iters
+
+    def check_errors(self):
+        if int(self.err.item()) != 0:
+            print(f"device error bits {int(self.err.item())}", file=sys.stderr)
+            sys.exit(1)
+
+    def bytes(self):
+        """Algorithmic bytes: visible prefix tokens, KV bytes, bytes of the
+        attention call (KV, Q, O, mask) and of the acceptance (logits)."""
+        wl = self.wl
+        b, n = self.b, self.n
+        hq, hkv, d = wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+        if self.partial:
+            prefix_tokens = []
+            for s in range(b):
+                vis = 0
+                for x in wl.block_idx[s, :int(wl.n_blocks[s])]:
+                    lo = int(x) * wl.block_size
+                    vis += max(0, min(wl.block_size, int(wl.prefix_len[s]) - lo))
+                prefix_tokens.append(vis)
+        else:
+            prefix_tokens = [int(p) for p in wl.prefix_len]
+        kv = (sum(prefix_tokens) + b * n) * hkv * d * 2 * 2   # K and V, bf16
+        qo = 2 * b * n * hq * d * 2                            # Q read, O written
+        mask = b * n * ((n + 31) // 32) * 4
+        return prefix_tokens, kv, kv + qo + mask, wl.logits.nbytes
+
+
+def measure(wl, partial, steps, warmup, warm, num_splits, dev):
+    import torch
+    r = StepRunner(wl, partial, warm, num_splits, dev)
+    for k in range(warmup):
+        r.step(r.sets[k % r.rot])
+    torch.cuda.synchronize()
+    r.check_errors()
+    t0 = time.perf_counter()
+    step_us = r.timed(r.step, steps)
+    wall_us = (time.perf_counter() - t0) * 1e6 / steps
+    iters = max(steps, 50)
+    calls = {"mask": r.timed(r.k_mask, iters), "attention": r.timed(r.k_attn, iters),
+             "accept": r.timed(r.k_accept, iters), "commit": r.timed(r.k_commit, iters)}
+    r.check_errors()
+    return r, step_us, wall_us, calls
+
+
+def secondary_line(name, partial, steps, dev):
+    import torch
+
+    from tree_verification_attention_tv_amd import workloads as W
+    wl = W.make_workload(name)
+    r, step_us, _, calls = measure(wl, partial, steps, 5, False, 0, dev)
+    prefix_tokens, kv, attn_bytes, _ = r.bytes()
+    gbps = attn_bytes / (calls["attention"] * 1e-6) / 1e9
+    out = {
+        "mode": "partial" if partial else "full",
+        "step_us": round(step_us, 3),
+        "attention_us": round(calls["attention"], 3),
+        "kv_bytes": kv,
+        "kv_gbps": round(kv / (calls["attention"] * 1e-6) / 1e9, 1),
+        "attention_gbps": round(gbps, 1),
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "prefix_tokens": prefix_tokens,
+        "num_splits": r.binding.attention_num_splits(r.desc),
+        "cache_rotation": r.rot,
+        "call_us": {k: round(v, 3) for k, v in calls.items()},
+    }
+    del r
+    torch.cuda.empty_cache()
+    return out
+
+
+def read_traffic():
+    """HBM bytes per attention call from the committed counter summary, or
+    None when it is missing or was taken on another kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if ":" in line and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("source_sha256_16") != source_hash():
+        return None
+    try:
+        return int(fields["hbm_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
+
+
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
+    if args.trace_summary:
+        trace_summary(*args.trace_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU (asked for {args.gpus}); "
               "multi-GPU sharding is described in the design notes but not built.",
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     from tree_verification_attention_tv_amd import binding
@@ -95,115 +302,22 @@ def main():
     dev = torch.device("cuda:0")
     binding.lib()   # fail loudly if the HIP library is missing
 
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
+        return
+
     wl = W.make_workload(args.workload)
     partial = args.partial and wl.block_idx is not None
-    b, n = wl.parents.shape
-    hq, hkv, d = wl.n_q_heads, wl.n_kv_heads, wl.head_dim
-
-    # ---- rotation so that the working set exceeds the Infinity Cache ------
-    first = InputSet(wl, dev, torch, np)
-    per_set = first.nbytes()
-    rot = 1 if args.warm else max(2, int(np.ceil(1.25 * MALL_BYTES / per_set)))
-    rot = min(rot, 64)
-    sets = [first] + [InputSet(wl, dev, torch, np) for _ in range(rot - 1)]
-
-    desc = binding.attn_desc(first.q, first.k_cache, max_prefix_len=wl.max_prefix_len,
-                             block_size=wl.block_size if partial else 0,
-                             max_blocks=wl.max_blocks if partial else 0,
-                             num_splits=args.num_splits)
-    ws_attn = torch.empty(binding.attention_workspace_size(desc), dtype=torch.uint8, device=dev)
-    ws_acc = torch.empty(binding.accept_workspace_size(b, n, wl.vocab), dtype=torch.uint8,
-                         device=dev)
-    acc_out = (torch.empty((b, n), dtype=torch.int32, device=dev),
-               torch.empty((b,), dtype=torch.int32, device=dev),
-               torch.empty((b, n), dtype=torch.int32, device=dev),
-               torch.empty((b,), dtype=torch.int32, device=dev))
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
-
-    def k_mask(s):
-        st = binding.lib().tv_build_tree_mask(binding._ptr(s.parents), b, n, binding._ptr(s.mask),
-                                              None, binding._ptr(err), binding._stream(dev))
-        if st:
-            raise binding.TVError("tv_build_tree_mask", st)
-
-    def k_attn(s):
-        binding.tree_attention(s.q, s.k_cache, s.v_cache, s.k_tree, s.v_tree, s.prefix_len,
-                               s.mask, max_prefix_len=wl.max_prefix_len,
-                               block_idx=s.block_idx if partial else None,
-                               n_blocks=s.n_blocks if partial else None,
-                               block_size=wl.block_size if partial else 0,
-                               num_splits=args.num_splits, out=s.out, workspace=ws_attn,
-                               dev_err=err)
-
-    def k_accept(s):
-        binding.greedy_accept(s.logits, s.parents, s.draft, workspace=ws_acc, dev_err=err,
-                              outputs=acc_out)
-
-    def k_commit(s):
-        binding.commit_kv(s.k_tree, s.v_tree, acc_out[2], acc_out[1], s.prefix_len,
-                          s.k_cache, s.v_cache, new_prefix_len=s.new_prefix, dev_err=err)
-
-    def step(s):
-        k_mask(s)
-        k_attn(s)
-        k_accept(s)
-        k_commit(s)
-
-    for k in range(args.warmup):
-        step(sets[k % rot])
-    torch.cuda.synchronize()
-    if int(err.item()) != 0:
-        print(f"device error bits {int(err.item())}", file=sys.stderr)
-        sys.exit(1)
-
-    # ---- timed region: K whole steps -----------------------------------
-    stream = torch.cuda.current_stream(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for k in range(args.steps):
-        step(sets[k % rot])
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    step_us = e0.elapsed_time(e1) * 1e3 / args.steps
-    wall_ms_per_step = (t1 - t0) * 1e3 / args.steps
-
-    # ---- per-call timing (same rotation), for the roofline ------------------
-    def time_call(fn, iters):
-        for k in range(3):
-            fn(sets[k % rot])
-        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for k in range(iters):
-            fn(sets[k % rot])
-        z.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(z) * 1e3 / iters
-
-    iters = max(args.steps, 50)
-    t_mask = time_call(k_mask, iters)
-    t_attn = time_call(k_attn, iters)
-    t_accept = time_call(k_accept, iters)
-    t_commit = time_call(k_commit, iters)
-
-    # algorithmic bytes
-    if partial:
-        vis = sum(min(wl.block_size, int(wl.prefix_len[0]) - int(x) * wl.block_size)
-                  for x in wl.block_idx[0, :int(wl.n_blocks[0])])
-        prefix_tokens = [vis]
-    else:
-        prefix_tokens = [int(p) for p in wl.prefix_len]
-    kv_bytes = (sum(prefix_tokens) + b * n) * hkv * d * 2 * 2
-    qo_bytes = 2 * b * n * hq * d * 2
-    mask_bytes = b * n * ((n + 31) // 32) * 4
-    attn_bytes = kv_bytes + qo_bytes + mask_bytes
-    logit_bytes = wl.logits.nbytes
-    calls = {"mask": t_mask, "attention": t_attn, "accept": t_accept, "commit": t_commit}
+    r, step_us, wall_us, calls = measure(wl, partial, args.steps, args.warmup, args.warm,
+                                         args.num_splits, dev)
+    prefix_tokens, kv_bytes, attn_bytes, logit_bytes = r.bytes()
+    b, n = r.b, r.n
     dominant = max(("attention", "accept"), key=lambda c: calls[c])
     dom_bytes = attn_bytes if dominant == "attention" else logit_bytes
     achieved = dom_bytes / (calls[dominant] * 1e-6) / 1e9
+    traffic = read_traffic() if (dominant == "attention" and args.workload == "8b_layer"
+                                 and not partial and not args.warm
+                                 and args.num_splits == 0) else None
 
     result = {
         "metric": "tree-verify step µs and KV GB/s (% of MI355X HBM peak), 8B shape, 1 GPU",
@@ -213,7 +327,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(step_us / 1e3, 6),
-        "wall_ms_per_step": round(wall_ms_per_step, 6),
+        "wall_ms_per_step": round(wall_us / 1e3, 6),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
@@ -221,27 +335,38 @@ def main():
         "data": "synthetic (seeded; no dataset or weights)",
         "config": {
             "workload": args.workload + ("_partial" if partial else ""),
-            "batch": b, "n_nodes": n, "n_q_heads": hq, "n_kv_heads": hkv, "head_dim": d,
+            "batch": b, "n_nodes": n, "n_q_heads": wl.n_q_heads, "n_kv_heads": wl.n_kv_heads,
+            "head_dim": wl.head_dim,
             "prefix_len": prefix_tokens if b <= 4 else [min(prefix_tokens), max(prefix_tokens)],
-            "vocab": wl.vocab, "cache_rotation": rot,
-            "num_splits": binding.attention_num_splits(desc),
+            "vocab": wl.vocab, "cache_rotation": r.rot,
+            "num_splits": binding.attention_num_splits(r.desc),
         },
-        "kv_gbps": round(kv_bytes / (t_attn * 1e-6) / 1e9, 1),
-        "kv_hbm_frac": round(kv_bytes / (t_attn * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "kv_gbps": round(kv_bytes / (calls["attention"] * 1e-6) / 1e9, 1),
+        "kv_hbm_frac": round(kv_bytes / (calls["attention"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "call_us": {k: round(v, 3) for k, v in calls.items()},
         "roofline": {
-            "kernel": dominant,
+            "kernel": ("tv_tree_attention (attn_split_kernel + attn_combine_kernel)"
+                       if dominant == "attention" else
+                       "tv_greedy_accept (vocab_argmax_kernel + path_walk_kernel)"),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "algorithmic_bytes": dom_bytes,
         },
+        "secondary": None,
         "cpu_baseline": None,
     }
-
+    first, acc_out = r.sets[0], r.acc_out
+    if not args.no_secondary and args.workload != "long_context":
+        del r
+        torch.cuda.empty_cache()
+        result["secondary"] = {
+            "long_context_full": secondary_line("long_context", False, 40, dev),
+            "long_context_partial": secondary_line("long_context", True, 100, dev),
+        }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, partial, first, acc_out, args.cpu_seconds)
     print(json.dumps(result), flush=True)
@@ -276,7 +401,7 @@ def cpu_baseline(wl, partial, dev_set, acc_out, seconds):
     while True:
         res = one_step()
         reps += 1
-        if time.perf_counter() - t0 >= seconds or reps >= 100:
+        if time.perf_counter() - t0 >= seconds:
             break
     el = time.perf_counter() - t0
     mask, o, amax, alen, path, bonus = res
@@ -295,6 +420,90 @@ def cpu_baseline(wl, partial, dev_set, acc_out, seconds):
                   f"{el:.1f} s",
         "sample_parity": parity,
     }
+
+
+# ---------------------------------------------------------------------------
+# helper modes for the committed profile summaries
+# ---------------------------------------------------------------------------
+
+def copy_calibration(torch, dev):
+    """Plain device copies of a known size: the counters' reading for them
+    scales FETCH_SIZE / WRITE_SIZE to bytes."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 5}), flush=True)
+
+
+def short_name(full, keep_template=False):
+    """Kernel name without return type, anonymous namespace and arguments."""
+    s = full.replace("(anonymous namespace)::", "")
+    if s.startswith("void "):
+        s = s[5:]
+    s = s.split("(")[0]
+    return s if keep_template else s.split("<")[0].split("::")[-1]
+
+
+def _counter_per_dispatch(directory, counter, match):
+    """Per kernel (short name): the counter summed over its instances within
+    a dispatch, averaged over dispatches."""
+    per = {}
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if row["Counter_Name"] != counter or match not in row["Kernel_Name"]:
+                    continue
+                key = short_name(row["Kernel_Name"])
+                d = per.setdefault(key, {})
+                d[row["Dispatch_Id"]] = d.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+    return {k: sum(v.values()) / len(v) for k, v in per.items() if v}
+
+
+def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", "attn_")
+    write = _counter_per_dispatch(write_dir, "WRITE_SIZE", "attn_")
+    cf = _counter_per_dispatch(copy_fetch_dir, "FETCH_SIZE", "")
+    cw = _counter_per_dispatch(copy_write_dir, "WRITE_SIZE", "")
+    # the copy kernel is the largest reading of the calibration run
+    cf_k = max(cf.values()) if cf else 0.0
+    cw_k = max(cw.values()) if cw else 0.0
+    f_scale = COPY_BYTES / cf_k if cf_k else float("nan")
+    w_scale = COPY_BYTES / cw_k if cw_k else float("nan")
+    tot_f = sum(fetch.get(k, 0.0) for k in ATTN_KERNELS)
+    tot_w = sum(write.get(k, 0.0) for k in ATTN_KERNELS)
+    hbm = int(round(tot_f * f_scale + tot_w * w_scale))
+    lines = [
+        "HBM traffic of one tv_tree_attention call, 8B-layer workload (bench.py default,",
+        "inputs rotated over 16 copies so that they miss the Infinity Cache).",
+        "Counter readings are scaled by what the same counter reads for a plain",
+        f"device copy of {COPY_BYTES} bytes (bench.py --copy-calibration).",
+        f"source_sha256_16: {source_hash()}",
+        f"hbm_bytes_per_call: {hbm}",
+        f"fetch_bytes_per_call: {int(round(tot_f * f_scale))}",
+        f"write_bytes_per_call: {int(round(tot_w * w_scale))}",
+        f"fetch_scale_bytes_per_unit: {f_scale:.2f}",
+        f"write_scale_bytes_per_unit: {w_scale:.2f}",
+        "  per dispatch (counter units, average over dispatches):",
+    ]
+    for k in ATTN_KERNELS:
+        lines.append(f"    {k:22s} FETCH_SIZE {fetch.get(k, 0.0):12.1f}  "
+                     f"WRITE_SIZE {write.get(k, 0.0):12.1f}")
+    lines.append(f"    copy of {COPY_BYTES} B  FETCH_SIZE {cf_k:12.1f}  WRITE_SIZE {cw_k:12.1f}")
+    print("\n".join(lines))
+
+
+def trace_summary(stats_csv, command):
+    with open(stats_csv) as fh:
+        rows = list(csv.DictReader(fh))
+    print(f"rocprofv3 kernel-trace stats\ncommand: {command}\n")
+    print(f"{'kernel':60s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}")
+    for r in rows:
+        name = short_name(r["Name"], keep_template=True)
+        print(f"{name[:60]:60s} {r['Calls']:>6s} {float(r['AverageNs']) / 1e3:9.2f} "
+              f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} "
+              f"{float(r['Percentage']):6.2f}")
 
 
 if __name__ == "__main__":
