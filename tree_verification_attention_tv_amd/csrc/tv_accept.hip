@@ -25,7 +25,7 @@ namespace tv {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 8;  // 16-byte vectors per thread per chunk
+constexpr int kUnroll = 8;  // 16-byte bf16 vectors per thread per chunk (fp32: twice as many)
 
 struct ValIdx {
   float v;
@@ -77,39 +77,39 @@ __global__ __launch_bounds__(kThreads) void vocab_argmax_kernel(const T* __restr
 
   float bv = -INFINITY;
   int bi = INT32_MAX;
+  auto take = [&](float f, int64_t k) {
+    // scanning in increasing index: a strict '>' keeps the first occurrence
+    if (f > bv || bi == INT32_MAX) {
+      bv = f;
+      bi = (int)k;
+    }
+  };
   if (kVector) {
     typedef T vec_t __attribute__((ext_vector_type(VEC)));
-    // chunk_len is a multiple of kThreads * VEC; only the last chunk is ragged
-    for (int64_t base = begin + (int64_t)threadIdx.x * VEC; base < end;
-         base += (int64_t)kThreads * VEC) {
-      if (base + VEC <= end) {
-        const vec_t x = *reinterpret_cast<const vec_t*>(src + base);
+    // All of the thread's loads are issued before any is used, so the chunk
+    // costs one memory round trip.  Vector u of thread t covers elements
+    // begin + (u * kThreads + t) * VEC .. +VEC-1 (coalesced for each u).
+    // chunk_len <= kThreads * 8 * kUnroll = kThreads * VEC * U elements, so
+    // U vectors per thread cover the chunk; only the last chunk is ragged.
+    constexpr int U = kUnroll * 8 / VEC;
+    vec_t x[U];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const float f = to_f32<T>(x[e]);
-          if (f > bv || bi == INT32_MAX) {
-            bv = f;
-            bi = (int)(base + e);
-          }
-        }
+    for (int u = 0; u < U; ++u) {
+      const int64_t base = begin + ((int64_t)u * kThreads + threadIdx.x) * VEC;
+      if (base + VEC <= end) x[u] = *reinterpret_cast<const vec_t*>(src + base);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t base = begin + ((int64_t)u * kThreads + threadIdx.x) * VEC;
+      if (base + VEC <= end) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) take(to_f32<T>(x[u][e]), base + e);
       } else {
-        for (int64_t k = base; k < end; ++k) {
-          const float f = to_f32<T>(src[k]);
-          if (f > bv || bi == INT32_MAX) {
-            bv = f;
-            bi = (int)k;
-          }
-        }
+        for (int64_t k = base; k < end; ++k) take(to_f32<T>(src[k]), k);
       }
     }
   } else {
-    for (int64_t k = begin + threadIdx.x; k < end; k += kThreads) {
-      const float f = to_f32<T>(src[k]);
-      if (f > bv || bi == INT32_MAX) {
-        bv = f;
-        bi = (int)k;
-      }
-    }
+    for (int64_t k = begin + threadIdx.x; k < end; k += kThreads) take(to_f32<T>(src[k]), k);
   }
 
   ValIdx a = wave_argmax(ValIdx{bv, bi});
@@ -149,21 +149,31 @@ __global__ __launch_bounds__(kThreads) void path_walk_kernel(
   __syncthreads();
   if (i < n) {
     const int64_t row = (int64_t)b * n + i;
-    float bv = part_v[row * chunks];
-    int bi = part_i[row * chunks];
-    for (int c = 1; c < chunks; ++c) {
-      const float v = part_v[row * chunks + c];
-      const int k = part_i[row * chunks + c];
-      if (better(v, k, bv, bi)) {
-        bv = v;
-        bi = k;
+    const int p = parents[row];
+    const int dt = draft[row];
+    // chunk partials in groups of 8, all loads of a group in flight at once
+    float bv = -INFINITY;
+    int bi = INT32_MAX;
+    for (int c0 = 0; c0 < chunks; c0 += 8) {
+      float v[8];
+      int k[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool in = c0 + u < chunks;
+        v[u] = in ? part_v[row * chunks + c0 + u] : -INFINITY;
+        k[u] = in ? part_i[row * chunks + c0 + u] : INT32_MAX;
       }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (better(v[u], k[u], bv, bi)) {
+          bv = v[u];
+          bi = k[u];
+        }
     }
     amax[i] = bi;
     target_argmax[row] = bi;
-    const int p = parents[row];
     par[i] = p;
-    dtok[i] = draft[row];
+    dtok[i] = dt;
     const bool ok = (i == 0) ? (p == -1) : (p >= 0 && p < i);
     if (!ok) bad = 1;
   }

@@ -11,6 +11,7 @@ namespace tv {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kBatch = 8;  // copy items per thread in flight
 
 __global__ __launch_bounds__(kThreads) void commit_kernel(
     const uint4* __restrict__ k_tree, const uint4* __restrict__ v_tree,
@@ -22,6 +23,9 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(
   __shared__ int s_node[TV_MAX_NODES];
   const int b = blockIdx.x;
   const int t = threadIdx.x;
+  // One round trip for every small input: the path entries are read before
+  // accept_len is known (t < n is always in bounds).
+  const int node_t = t < n ? path[(int64_t)b * n + t] : 0;
   if (t == 0) {
     const int p = prefix_len[b];
     const int a = accept_len[b];
@@ -43,9 +47,8 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(
   __syncthreads();
   const int a = s_len;
   if (s_ok && t <= a) {
-    const int node = path[(int64_t)b * n + t];
-    s_node[t] = node;
-    if (node < 0 || node >= n) {
+    s_node[t] = node_t;
+    if (node_t < 0 || node_t >= n) {
       raise_err(dev_err, TV_DERR_BAD_PATH);
       s_ok = 0;  // benign race: every writer stores 0
     }
@@ -59,15 +62,35 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(
     const uint4* vt = v_tree + (int64_t)b * n * hkv * per_row;
     uint4* kc = k_cache + b * seq_stride_vec;
     uint4* vc = v_cache + b * seq_stride_vec;
-    for (int it = t; it < items; it += kThreads) {
+    // batches of kBatch items per thread: all loads, then all stores
+    auto locate = [&](int it, int64_t& src, int64_t& dst) {
       const int c = it % per_row;
       const int rh = it / per_row;
       const int h = rh % hkv;
       const int r = rh / hkv;
-      const int64_t src = ((int64_t)s_node[r] * hkv + h) * per_row + c;
-      const int64_t dst = ((int64_t)h * cap + p + r) * per_row + c;
-      kc[dst] = kt[src];
-      vc[dst] = vt[src];
+      src = ((int64_t)s_node[r] * hkv + h) * per_row + c;
+      dst = ((int64_t)h * cap + p + r) * per_row + c;
+    };
+    for (int it0 = t; it0 < items; it0 += kBatch * kThreads) {
+      uint4 kx[kBatch], vx[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int it = min(it0 + u * kThreads, items - 1);  // clamped: always a valid item
+        int64_t src, dst;
+        locate(it, src, dst);
+        kx[u] = kt[src];
+        vx[u] = vt[src];
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int it = it0 + u * kThreads;
+        if (it < items) {
+          int64_t src, dst;
+          locate(it, src, dst);
+          kc[dst] = kx[u];
+          vc[dst] = vx[u];
+        }
+      }
     }
   }
   if (t == 0) new_prefix_len[b] = s_ok ? s_prefix + a + 1 : s_prefix;
