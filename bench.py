@@ -11,7 +11,9 @@ than cache bandwidth, the step rotates over enough independent copies of its
 inputs that their total exceeds the 256 MB Infinity Cache.
 
 Prints one JSON line (rank 0):
-  value = microseconds per verify step (lower is better); KV GB/s; a roofline
+  value = microseconds per verify step (lower is better), the step replayed
+  from a captured HIP graph (the same four calls; the eager time is reported
+  beside it); KV GB/s; a roofline
   entry for the dominant call (HIP-event timing of its own launches on the
   stream they run on, algorithmic bytes, and the HBM traffic measured with
   rocprofv3 counters when those were taken on the current kernel source);
@@ -60,6 +62,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the step with eager launches only (no HIP graph replay)")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the long-context (60K prefix) full/partial lines")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -124,6 +128,9 @@ class StepRunner:
         rot = 1 if warm else max(2, int(np.ceil(1.25 * MALL_BYTES / first.nbytes())))
         self.rot = min(rot, 64)
         self.sets = [first] + [InputSet(wl, dev, torch, np) for _ in range(self.rot - 1)]
+        for i, st in enumerate(self.sets):
+            st.gidx = i
+        self.graphs = []
         self.b, self.n = wl.parents.shape
         self.num_splits = num_splits
         self.desc = binding.attn_desc(first.q, first.k_cache, max_prefix_len=wl.max_prefix_len,
@@ -172,6 +179,22 @@ class StepRunner:
         self.k_accept(s)
         self.k_commit(s)
 
+    def capture(self):
+        """One HIP graph per input set holding that set's whole step (the
+        same four calls, same buffers; no allocation or memset inside)."""
+        import torch
+        torch.cuda.synchronize()
+        self.graphs = []
+        for s in self.sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.step(s)
+            self.graphs.append(g)
+        torch.cuda.synchronize()
+
+    def replay(self, s):
+        self.graphs[s.gidx].replay()
+
     # -- timing ----------------------------------------------------------------
     def timed(self, fn, iters):
         """Average microseconds of `fn` over `iters` back-to-back calls, from
@@ -213,7 +236,9 @@ class StepRunner:
         return prefix_tokens, kv, kv + qo + mask, wl.logits.nbytes
 
 
-def measure(wl, partial, steps, warmup, warm, num_splits, dev):
+def measure(wl, partial, steps, warmup, warm, num_splits, dev, graph=True):
+    """Returns (runner, step_us, wall_us, eager_step_us, calls).  step_us is
+    the graph-replayed step when `graph`, else the eager one."""
     import torch
     r = StepRunner(wl, partial, warm, num_splits, dev)
     for k in range(warmup):
@@ -221,13 +246,21 @@ def measure(wl, partial, steps, warmup, warm, num_splits, dev):
     torch.cuda.synchronize()
     r.check_errors()
     t0 = time.perf_counter()
-    step_us = r.timed(r.step, steps)
+    eager_us = r.timed(r.step, steps)
     wall_us = (time.perf_counter() - t0) * 1e6 / steps
+    step_us = eager_us
+    if graph:
+        r.capture()
+        for k in range(warmup):
+            r.replay(r.sets[k % r.rot])
+        t0 = time.perf_counter()
+        step_us = r.timed(r.replay, steps)
+        wall_us = (time.perf_counter() - t0) * 1e6 / steps
     iters = max(steps, 50)
     calls = {"mask": r.timed(r.k_mask, iters), "attention": r.timed(r.k_attn, iters),
              "accept": r.timed(r.k_accept, iters), "commit": r.timed(r.k_commit, iters)}
     r.check_errors()
-    return r, step_us, wall_us, calls
+    return r, step_us, wall_us, eager_us, calls
 
 
 def secondary_line(name, partial, steps, dev):
@@ -235,12 +268,13 @@ def secondary_line(name, partial, steps, dev):
 
     from tree_verification_attention_tv_amd import workloads as W
     wl = W.make_workload(name)
-    r, step_us, _, calls = measure(wl, partial, steps, 5, False, 0, dev)
+    r, step_us, _, eager_us, calls = measure(wl, partial, steps, 5, False, 0, dev)
     prefix_tokens, kv, attn_bytes, _ = r.bytes()
     gbps = attn_bytes / (calls["attention"] * 1e-6) / 1e9
     out = {
         "mode": "partial" if partial else "full",
         "step_us": round(step_us, 3),
+        "eager_step_us": round(eager_us, 3),
         "attention_us": round(calls["attention"], 3),
         "kv_bytes": kv,
         "kv_gbps": round(kv / (calls["attention"] * 1e-6) / 1e9, 1),
@@ -308,8 +342,9 @@ def main():
 
     wl = W.make_workload(args.workload)
     partial = args.partial and wl.block_idx is not None
-    r, step_us, wall_us, calls = measure(wl, partial, args.steps, args.warmup, args.warm,
-                                         args.num_splits, dev)
+    r, step_us, wall_us, eager_us, calls = measure(wl, partial, args.steps, args.warmup,
+                                                   args.warm, args.num_splits, dev,
+                                                   graph=not args.no_graph)
     prefix_tokens, kv_bytes, attn_bytes, logit_bytes = r.bytes()
     b, n = r.b, r.n
     dominant = max(("attention", "accept"), key=lambda c: calls[c])
@@ -328,6 +363,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(step_us / 1e3, 6),
         "wall_ms_per_step": round(wall_us / 1e3, 6),
+        "step_launch": "hip_graph_replay" if not args.no_graph else "eager",
+        "eager_step_us": round(eager_us, 3),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,

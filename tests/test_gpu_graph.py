@@ -1,0 +1,89 @@
+"""A whole verify step captured in a HIP graph replays to the eager results.
+
+The library only launches kernels (no memset, no allocation), so the four
+calls can be captured.  The graph is replayed several times, with eager work
+and synchronisation between the replays, and every replay is compared bit for
+bit with an eager step on an identical copy of the inputs.
+"""
+
+import pytest
+import torch
+
+from tree_verification_attention_tv_amd import binding
+from tree_verification_attention_tv_amd import workloads as W
+
+from .gpu_util import DevWorkload
+
+pytestmark = pytest.mark.gpu
+
+
+class _Step:
+    """Inputs (a private device copy) and preallocated outputs of one step."""
+
+    def __init__(self, wl):
+        self.dw = DevWorkload(wl)
+        dw = self.dw
+        b, n = wl.parents.shape
+        dev = dw.q.device
+        self.mask = torch.empty((b, n, (n + 31) // 32), dtype=torch.int32, device=dev)
+        self.out = torch.empty_like(dw.q)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.acc = tuple(torch.empty(s, dtype=torch.int32, device=dev)
+                         for s in ((b, n), (b,), (b, n), (b,)))
+        self.new_prefix = torch.empty_like(dw.prefix_len)
+        desc = binding.attn_desc(dw.q, dw.k_cache, max_prefix_len=wl.max_prefix_len)
+        self.ws_attn = torch.empty(binding.attention_workspace_size(desc), dtype=torch.uint8,
+                                   device=dev)
+        self.ws_acc = torch.empty(binding.accept_workspace_size(b, n, wl.vocab), dtype=torch.uint8,
+                                  device=dev)
+
+    def run(self):
+        dw, wl = self.dw, self.dw.wl
+        b, n = wl.parents.shape
+        st = binding.lib().tv_build_tree_mask(binding._ptr(dw.parents), b, n,
+                                              binding._ptr(self.mask), None,
+                                              binding._ptr(self.err),
+                                              binding._stream(dw.q.device))
+        assert st == 0
+        binding.tree_attention(dw.q, dw.k_cache, dw.v_cache, dw.k_tree, dw.v_tree, dw.prefix_len,
+                               self.mask, max_prefix_len=wl.max_prefix_len, out=self.out,
+                               workspace=self.ws_attn, dev_err=self.err)
+        binding.greedy_accept(dw.logits, dw.parents, dw.draft, workspace=self.ws_acc,
+                              dev_err=self.err, outputs=self.acc)
+        binding.commit_kv(dw.k_tree, dw.v_tree, self.acc[2], self.acc[1], dw.prefix_len,
+                          dw.k_cache, dw.v_cache, new_prefix_len=self.new_prefix,
+                          dev_err=self.err)
+
+    def results(self):
+        return [self.mask, self.out.view(torch.int16), *self.acc, self.new_prefix,
+                self.dw.k_cache.view(torch.int16), self.dw.v_cache.view(torch.int16), self.err]
+
+    def scramble(self):
+        # outputs overwritten with junk by eager kernels, outside the graph
+        for t in (self.mask, self.out.view(torch.int16), *self.acc, self.new_prefix):
+            t.fill_(-7)
+
+
+@pytest.mark.parametrize("name", ["8b_layer", "batched"])
+def test_step_graph_replays_match_eager(name):
+    print(f"[graph] {name} step capture and replay", flush=True)
+    wl = W.make_workload(name)
+    eager, graphed = _Step(wl), _Step(wl)
+    eager.run()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in eager.results()]
+    assert int(eager.err.item()) == 0
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        graphed.run()
+    torch.cuda.synchronize()
+
+    for rep in range(4):
+        graphed.scramble()
+        eager.run()              # eager library work between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, (got, want) in enumerate(zip(graphed.results(), ref)):
+            assert torch.equal(got, want), f"replay {rep}: output {k} differs from the eager step"
