@@ -134,7 +134,14 @@ typedef struct {
                                partial mode raises it so that one split spans at most
                                1022 blocks; tv_tree_attention_num_splits gives the count */
   int64_t cache_seq_stride; /* elements between sequences; 0 = n_kv_heads*capacity*head_dim */
+  int32_t tree_placement;   /* where the tree block runs: TV_TREE_AUTO (chosen by the
+                               planner), TV_TREE_OWN_WORKGROUP, or TV_TREE_IN_LAST_SPLIT
+                               (after the prefix tiles of the last non-empty split).
+                               Results are the same; only the schedule differs. */
+  int32_t reserved;         /* must be 0 */
 } tv_attn_desc;
+
+enum { TV_TREE_AUTO = 0, TV_TREE_OWN_WORKGROUP = 1, TV_TREE_IN_LAST_SPLIT = 2 };
 
 typedef struct {
   const void* q;

@@ -68,3 +68,18 @@ def test_null_and_shape_errors_enqueue_nothing():
     # accept: row stride below vocab
     assert L.tv_greedy_accept(p, 0, 100, 50, p, p, 1, 8, p, p, p, p, p, 1 << 20, None,
                               None) == 2
+
+
+def test_attention_descriptor_tree_placement_is_validated():
+    # descriptor checks come before the pointer checks: a valid descriptor with
+    # null pointers gives TV_ERR_NULL, an invalid placement TV_ERR_SHAPE
+    L = binding.lib()
+    d = binding.AttnDesc(batch=1, n_nodes=60, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                         cache_capacity=1088, max_prefix_len=1000)
+    for placement in (binding.TREE_AUTO, binding.TREE_OWN_WORKGROUP, binding.TREE_IN_LAST_SPLIT):
+        d.tree_placement = placement
+        assert L.tv_tree_attention(ctypes.byref(d), None, None, 0, None, None) == 1
+    d.tree_placement = 3
+    assert L.tv_tree_attention(ctypes.byref(d), None, None, 0, None, None) == 2
+    d.tree_placement, d.reserved = 0, 1
+    assert L.tv_tree_attention(ctypes.byref(d), None, None, 0, None, None) == 2

@@ -139,6 +139,18 @@ def test_attention_random(case):
     _run_attention_case(dw, partial=bool(bs), label=f"case{seed}")
 
 
+@pytest.mark.parametrize("placement", [binding.TREE_IN_LAST_SPLIT, binding.TREE_OWN_WORKGROUP])
+@pytest.mark.parametrize("case", [c for c in ATTN_CASES if c[0] in (2, 3, 4, 8, 10, 12)],
+                         ids=lambda c: f"case{c[0]}")
+def test_attention_tree_placements(case, placement):
+    seed, bsz, n, hq, hkv, d, plens, bs, bps, tree = case
+    _say(f"[attention] tree placement {placement} case {seed}")
+    wl = W.make_random_case(seed, batch=bsz, n_nodes=n, hq=hq, hkv=hkv, d=d, prefix_lens=plens,
+                            block_size=bs, blocks_per_seq=bps, tree=tree)
+    _run_attention_case(DevWorkload(wl), partial=bool(bs), label=f"case{seed}-p{placement}",
+                        tree_placement=placement)
+
+
 @pytest.mark.parametrize("splits", [1, 2, 7, 31])
 def test_attention_split_counts(workloads, splits):
     _say(f"[attention] 8b_layer splits={splits}")
@@ -181,10 +193,12 @@ def test_attention_bad_block_is_skipped():
     assert int(err.item()) & binding.DERR_BAD_BLOCK
 
 
-def test_attention_tree_split_with_only_invalid_blocks():
-    # The last prefix split also runs the tree block.  Here every block id of
-    # that split is invalid, so it must still produce the tree's partial.
-    _say("[attention] last split all-invalid blocks, tree still attended")
+@pytest.mark.parametrize("placement", [binding.TREE_IN_LAST_SPLIT, binding.TREE_OWN_WORKGROUP])
+def test_attention_tree_split_with_only_invalid_blocks(placement):
+    # Every block id of the last prefix split is invalid.  With the tree
+    # folded into that split it must still produce the tree's partial; with
+    # the tree in its own workgroup the split contributes nothing.
+    _say(f"[attention] last split all-invalid blocks, tree placement {placement}")
     wl = W.make_random_case(33, batch=1, n_nodes=9, hq=8, hkv=2, d=128, prefix_lens=[300],
                             block_size=32, blocks_per_seq=4)
     good = wl.block_idx.copy()
@@ -195,7 +209,7 @@ def test_attention_tree_split_with_only_invalid_blocks():
     wl.block_idx = bad
     mask, _ = binding.build_tree_mask(dw.parents)
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
-    out = dw.attention(mask, partial=True, dev_err=err, num_splits=2)
+    out = dw.attention(mask, partial=True, dev_err=err, num_splits=2, tree_placement=placement)
     torch.cuda.synchronize()
     wl.block_idx, wl.n_blocks = good, np.array([4], dtype=np.int32)
     ref, _ = oracle_attention(wl, partial=True)

@@ -37,6 +37,7 @@ class AttnDesc(ctypes.Structure):
         ("block_size", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float), ("num_splits", ctypes.c_int32),
         ("cache_seq_stride", ctypes.c_int64),
+        ("tree_placement", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
 
@@ -153,8 +154,11 @@ def build_tree_mask(parents: torch.Tensor, *, dev_err=None, with_depth=True):
     return mask, depth
 
 
+TREE_AUTO, TREE_OWN_WORKGROUP, TREE_IN_LAST_SPLIT = 0, 1, 2
+
+
 def attn_desc(q, k_cache, *, max_prefix_len, block_size=0, max_blocks=0, scale=0.0,
-              num_splits=0) -> AttnDesc:
+              num_splits=0, tree_placement=TREE_AUTO) -> AttnDesc:
     bsz, n, hq, d = q.shape
     _, hkv, cap, d2 = k_cache.shape
     if d2 != d:
@@ -163,6 +167,7 @@ def attn_desc(q, k_cache, *, max_prefix_len, block_size=0, max_blocks=0, scale=0
                     cache_capacity=cap, max_prefix_len=int(max_prefix_len),
                     block_size=int(block_size), max_blocks=int(max_blocks),
                     softmax_scale=float(scale), num_splits=int(num_splits),
+                    tree_placement=int(tree_placement), reserved=0,
                     cache_seq_stride=int(k_cache.stride(0)))
 
 
@@ -176,6 +181,7 @@ def attention_num_splits(desc: AttnDesc) -> int:
 
 def tree_attention(q, k_cache, v_cache, k_tree, v_tree, prefix_len, mask, *, max_prefix_len,
                    block_idx=None, n_blocks=None, block_size=0, scale=0.0, num_splits=0,
+                   tree_placement=TREE_AUTO,
                    want_lse=False, out=None, lse=None, workspace=None, dev_err=None):
     """bf16 tree-masked GQA attention.  Returns out (and lse if asked)."""
     bf = torch.bfloat16
@@ -195,7 +201,7 @@ def tree_attention(q, k_cache, v_cache, k_tree, v_tree, prefix_len, mask, *, max
     desc = attn_desc(q, k_cache, max_prefix_len=max_prefix_len,
                      block_size=block_size if partial else 0,
                      max_blocks=block_idx.shape[1] if partial else 0,
-                     scale=scale, num_splits=num_splits)
+                     scale=scale, num_splits=num_splits, tree_placement=tree_placement)
     if out is None:
         out = torch.empty_like(q)
     if want_lse and lse is None:

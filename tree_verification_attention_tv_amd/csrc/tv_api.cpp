@@ -41,6 +41,9 @@ tv_status check_attn_desc(const tv_attn_desc* d) {
   if ((int64_t)d->n_nodes * (d->n_q_heads / d->n_kv_heads) > 1024) return TV_ERR_UNSUPPORTED;
   if (d->cache_capacity < 0) return TV_ERR_SHAPE;
   if (d->max_blocks < 0 || d->num_splits < 0 || d->num_splits > 4096) return TV_ERR_SHAPE;
+  if (d->tree_placement < TV_TREE_AUTO || d->tree_placement > TV_TREE_IN_LAST_SPLIT ||
+      d->reserved != 0)
+    return TV_ERR_SHAPE;
   if (d->max_blocks > 0) {
     if (d->block_size < 1) return TV_ERR_SHAPE;
     if ((int64_t)d->max_blocks * d->block_size > INT_MAX / 2) return TV_ERR_SHAPE;

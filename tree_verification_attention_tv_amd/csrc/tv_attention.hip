@@ -80,6 +80,7 @@ struct AttnArgs {
   int batch, n, hq, hkv, grp, cap, words;
   int block_size, block_shift, max_blocks, max_prefix;  // block_shift < 0: not a power of 2
   int chunk, splits, row_groups, rows;
+  int tree_sep, nparts;  // tree in its own workgroup (split index `splits`); partials per sequence
   float c;  // softmax scale * log2(e)
 };
 
@@ -191,26 +192,60 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
   const int col = lane & 15;   // MFMA column (query row within a block)
   const int grp4 = lane >> 4;  // lane group 0..3
 
+  const int wg_row0 = rg * (16 * kWaves * RB);
+  const int row0 = wg_row0 + wave * (16 * RB);
+  const bool active = row0 < a.rows;
+  const int node0 = wg_row0 / a.grp;
+
+  // ---- loads that do not depend on the prefix length ------------------------
+  // Issued first so that they share one memory round trip with prefix_len:
+  // the Q^T fragments (B operand of S^T = K Q^T) and this workgroup's mask
+  // words (kept in registers until it is known whether the tree is ours).
+  bf16x8 qf[RB][DC];
+#pragma unroll
+  for (int mb = 0; mb < RB; ++mb) {
+    const int m = row0 + 16 * mb + col;
+    const bool real = m < a.rows;
+    const int i = real ? m / a.grp : 0;
+    const int h = g * a.grp + (real ? m - i * a.grp : 0);
+    const bf16* qrow = a.q + (((int64_t)b * a.n + i) * a.hq + h) * D + 8 * grp4;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+      qf[mb][dc] = real ? *reinterpret_cast<const bf16x8*>(qrow + 32 * dc) : bf16x8{};
+  }
+  constexpr int kMaskPer = TV_MAX_NODES * (TV_MAX_NODES / 32) / kSplitThreads;  // words per thread
+  const int node1 = min(a.n, (wg_row0 + 16 * kWaves * RB + a.grp - 1) / a.grp);
+  const int mcnt = (node1 - node0) * a.words;
+  uint32_t mw[kMaskPer];
+  {
+    const uint32_t* src = a.mask + ((int64_t)b * a.n + node0) * a.words;
+#pragma unroll
+    for (int u = 0; u < kMaskPer; ++u) {
+      const int k = tid + u * kSplitThreads;
+      mw[u] = k < mcnt ? src[k] : 0u;
+    }
+  }
+
   int err = 0;
   const int p_len = clamped_prefix(a, b, &err);
   const int slots = prefix_slots(a, b, p_len, &err);
+  // Wait for all of the above here, on every path: the compiler's own wait
+  // would otherwise be placed inside the loop (vmcnt(0), draining the tile
+  // DMA each step).
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // gfx9 encoding: vmcnt(0)
   if (err && s == 0 && g == 0 && rg == 0 && tid == 0) raise_err(a.dev_err, err);
   err = 0;
-  // Prefix range of this split.  The last non-empty split of the sequence
-  // (split 0 when the prefix is empty) also takes the tree block, after its
-  // prefix tiles: no workgroup is spent on the tree alone.
+  // Prefix range of this split.  The tree block runs either in a workgroup of
+  // its own (split index `splits`, whose prefix range is empty) or, when the
+  // grid must stay within one workgroup per CU, after the prefix tiles of the
+  // last non-empty split (split 0 when the prefix is empty).
   const int ns = (slots + a.chunk - 1) / a.chunk;
-  const bool has_tree = s == max(ns - 1, 0);
+  const bool has_tree = a.tree_sep ? s == a.splits : s == max(ns - 1, 0);
   const int begin = s * a.chunk;
   const int end = min(begin + a.chunk, slots);
   int np = begin < end ? (end - begin + kTile - 1) / kTile : 0;  // prefix tiles
   const int nt = has_tree ? (a.n + kTile - 1) / kTile : 0;       // tree tiles
   if (np == 0 && nt == 0) return;  // uniform over the workgroup
-
-  const int wg_row0 = rg * (16 * kWaves * RB);
-  const int row0 = wg_row0 + wave * (16 * RB);
-  const bool active = row0 < a.rows;
-  const int node0 = wg_row0 / a.grp;
 
   // ---- sources --------------------------------------------------------------
   const char* kc = reinterpret_cast<const char*>(a.k_cache + b * a.seq_stride + (int64_t)g * a.cap * D);
@@ -219,21 +254,22 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
   const char* vt = reinterpret_cast<const char*>(a.v_tree + ((int64_t)b * a.n * a.hkv + g) * D);
   const int64_t tree_rowb = (int64_t)a.hkv * ROWB;  // bytes between tree nodes
 
-  // partial rows of this split: ((b * splits + s) * n + i) * hq + h
+  // partial rows of this split: ((b * nparts + s) * n + i) * hq + h
   auto part_index = [&](int m) -> int64_t {
     const int i = m / a.grp;
     const int h = g * a.grp + m % a.grp;
-    return (((int64_t)b * a.splits + s) * a.n + i) * a.hq + h;
+    return (((int64_t)b * a.nparts + s) * a.n + i) * a.hq + h;
   };
 
   // ---- per-split tables staged in LDS --------------------------------------
   int bi0 = 0;         // partial: first block index of the split
   int fb_row = begin;  // a valid prefix row of this split (stands in for empty slots)
   if (has_tree) {
-    const int node1 = min(a.n, (wg_row0 + 16 * kWaves * RB + a.grp - 1) / a.grp);
-    const int cnt = (node1 - node0) * a.words;
-    const uint32_t* src = a.mask + ((int64_t)b * a.n + node0) * a.words;
-    for (int k = tid; k < cnt; k += kSplitThreads) smask[k] = src[k];
+#pragma unroll
+    for (int u = 0; u < kMaskPer; ++u) {
+      const int k = tid + u * kSplitThreads;
+      if (k < mcnt) smask[k] = mw[u];
+    }
   }
   if (PARTIAL && np > 0) {
     const int32_t* blist = a.block_idx + (int64_t)b * a.max_blocks;
@@ -360,23 +396,6 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
     }
     return cnt >= kTile ? 0xFFFFFFFFu : (cnt <= 0 ? 0u : ((1u << cnt) - 1u));
   };
-
-  // ---- Q^T fragments (B operand of S^T = K Q^T) ----------------------------
-  bf16x8 qf[RB][DC];
-#pragma unroll
-  for (int mb = 0; mb < RB; ++mb) {
-    const int m = row0 + 16 * mb + col;
-    const bool real = m < a.rows;
-    const int i = real ? m / a.grp : 0;
-    const int h = g * a.grp + (real ? m - i * a.grp : 0);
-    const bf16* qrow = a.q + (((int64_t)b * a.n + i) * a.hq + h) * D + 8 * grp4;
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc)
-      qf[mb][dc] = real ? *reinterpret_cast<const bf16x8*>(qrow + 32 * dc) : bf16x8{};
-  }
-  // Wait for Q here, on every path: the compiler's own wait would otherwise
-  // be placed inside the loop (vmcnt(0), draining the tile DMA each step).
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // gfx9 encoding: vmcnt(0)
 
   // ---- LDS operand addressing ----------------------------------------------
   // K fragment (tb, dc): token 16tb + col, columns 32dc + 8grp4 .. +7, i.e.
@@ -680,7 +699,7 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
   constexpr int Q4 = D / 4;
-  constexpr int U = 8;
+  constexpr int U = 16;
   const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const int64_t total = (int64_t)a.batch * a.n * a.hq * Q4;
   if (gid >= total) return;
@@ -694,18 +713,47 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
   int err = 0;
   const int p_len = clamped_prefix(a, b, &err);
   const int slots = prefix_slots(a, b, p_len, &err);
-  // splits 0..max(ns, 1)-1 hold partials (the last of them includes the tree)
-  const int cnt = max((slots + a.chunk - 1) / a.chunk, 1);
+  // Partials: prefix splits 0..ns-1, then the tree's own split (index
+  // `splits`) when it has one; otherwise splits 0..max(ns, 1)-1, the last of
+  // which includes the tree.
+  const int ns = (slots + a.chunk - 1) / a.chunk;
+  const int cnt = a.tree_sep ? ns + 1 : max(ns, 1);
   const int64_t stride = (int64_t)a.n * a.hq;  // partial rows between splits
-  const int64_t p0 = (((int64_t)b * a.splits) * a.n + i) * a.hq + h;
-  float m = -INFINITY;
+  const int64_t p0 = (((int64_t)b * a.nparts) * a.n + i) * a.hq + h;
+  auto split_of = [&](int k) { return (a.tree_sep && k == ns) ? a.splits : k; };
+  // One pass over the partials in batches of U, each batch's (m, l) and o
+  // loads in flight together; the running (m, l, acc) is rescaled when a
+  // batch raises the maximum.  Empty partials have m = -inf and weigh 0.
+  float m = -INFINITY, l = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < cnt; k0 += U) {
-    float mv[U];
+    float2 ml[U];
+    f32x4 ov[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      mv[u] = (k0 + u < cnt) ? a.part_ml[p0 + (k0 + u) * stride].x : -INFINITY;
+    for (int u = 0; u < U; ++u) {
+      if (k0 + u < cnt) {
+        const int64_t pi = p0 + split_of(k0 + u) * stride;
+        ml[u] = a.part_ml[pi];
+        ov[u] = *reinterpret_cast<const f32x4*>(a.part_o + pi * D + 4 * dq);
+      } else {
+        ml[u] = make_float2(-INFINITY, 0.f);
+        ov[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    float mb = m;
 #pragma unroll
-    for (int u = 0; u < U; ++u) m = fmaxf(m, mv[u]);
+    for (int u = 0; u < U; ++u) mb = fmaxf(mb, ml[u].x);
+    if (mb == -INFINITY) continue;
+    const float r = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mb);
+    l *= r;
+    acc *= r;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = ml[u].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[u].x - mb);
+      l += w * ml[u].y;
+      acc += w * ov[u];
+    }
+    m = mb;
   }
 
   bf16x4 res;
@@ -714,29 +762,6 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
     res = bf16x4{};
     lse_v = -INFINITY;
   } else {
-    float l = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < cnt; k0 += U) {
-      float2 ml[U];
-      f32x4 ov[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (k0 + u < cnt) {
-          const int64_t pi = p0 + (k0 + u) * stride;
-          ml[u] = a.part_ml[pi];
-          ov[u] = *reinterpret_cast<const f32x4*>(a.part_o + pi * D + 4 * dq);
-        } else {
-          ml[u] = make_float2(-INFINITY, 0.f);
-          ov[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float w = __builtin_amdgcn_exp2f(ml[u].x - m);
-        l += w * ml[u].y;
-        acc += w * ov[u];
-      }
-    }
     const float inv = 1.f / l;
 #pragma unroll
     for (int e = 0; e < 4; ++e) res[e] = (bf16)(acc[e] * inv);
@@ -774,27 +799,53 @@ AttnPlan plan_attention(const tv_attn_desc& d, int cu_count) {
   p.row_blocks = per_group <= 16 * kWaves ? 1 : 2;
   p.prefix_slots = d.max_blocks ? d.max_blocks * d.block_size : d.max_prefix_len;
   const int units = d.batch * d.n_kv_heads * p.row_groups;
+  const int tree_tiles = (d.n_nodes + kTile - 1) / kTile;
+  auto chunk_for = [&](int splits) {
+    int c = p.prefix_slots > 0 ? (p.prefix_slots + splits - 1) / splits : kTile;
+    c = ((c + kTile - 1) / kTile) * kTile;
+    if (d.max_blocks) {
+      // the block ids a split touches must fit its LDS table
+      const int64_t lim =
+          std::max<int64_t>(kTile, ((kBlkCache - 2) * (int64_t)d.block_size / kTile) * kTile);
+      if (c > lim) c = (int)lim;
+    }
+    return c;
+  };
+  // tiles on the longest workgroup: with the tree folded into the last
+  // non-empty split, or with the tree in a workgroup of its own
+  auto critical = [&](int splits, bool sep) {
+    const int c = chunk_for(splits);
+    const int full = (c + kTile - 1) / kTile;
+    if (sep) return std::max(full, tree_tiles);
+    const int ns = p.prefix_slots > 0 ? (p.prefix_slots + c - 1) / c : 1;
+    const int last = p.prefix_slots - (ns - 1) * c;
+    return std::max(full, (std::max(last, 0) + kTile - 1) / kTile + tree_tiles);
+  };
   int splits;
+  bool sep;
   if (d.num_splits > 0) {
     splits = d.num_splits;
+    sep = (int64_t)units * (splits + 1) <= cu_count;
+  } else if (d.tree_placement != TV_TREE_AUTO) {
+    splits = std::max(std::min(std::max(cu_count / units, 1),
+                               std::max((p.prefix_slots + kMinChunk - 1) / kMinChunk, 1)), 1);
+    sep = d.tree_placement == TV_TREE_OWN_WORKGROUP;
   } else {
     // one workgroup per CU (two waves per SIMD): a grid of at most cu_count
     // workgroups runs in a single round
-    splits = cu_count / units;
-    const int cap = (p.prefix_slots + kMinChunk - 1) / kMinChunk;
-    if (splits > cap) splits = cap;
-    if (splits < 1) splits = 1;
+    const int smax = std::max(cu_count / units, 1);
+    const int cap = std::max((p.prefix_slots + kMinChunk - 1) / kMinChunk, 1);
+    const int s_fold = std::min(smax, cap);
+    const int s_sep = std::min(smax - 1, cap);
+    sep = s_sep >= 1 && critical(s_sep, true) <= critical(s_fold, false);
+    splits = sep ? s_sep : s_fold;
   }
-  int chunk = p.prefix_slots > 0 ? (p.prefix_slots + splits - 1) / splits : kTile;
-  chunk = ((chunk + kTile - 1) / kTile) * kTile;
-  if (d.max_blocks) {
-    // the block ids a split touches must fit its LDS table
-    const int64_t lim = std::max<int64_t>(kTile, ((kBlkCache - 2) * (int64_t)d.block_size / kTile) * kTile);
-    if (chunk > lim) chunk = (int)lim;
-  }
-  p.chunk = chunk;
-  p.splits = p.prefix_slots > 0 ? (p.prefix_slots + chunk - 1) / chunk : 1;
-  const size_t parts = (size_t)d.batch * p.splits * d.n_nodes * d.n_q_heads;
+  p.chunk = chunk_for(splits);
+  p.splits = p.prefix_slots > 0 ? (p.prefix_slots + p.chunk - 1) / p.chunk : 1;
+  if (d.tree_placement != TV_TREE_AUTO) sep = d.tree_placement == TV_TREE_OWN_WORKGROUP;
+  else if ((int64_t)units * (p.splits + 1) > std::max(cu_count, units * 2)) sep = false;
+  p.tree_sep = sep ? 1 : 0;
+  const size_t parts = (size_t)d.batch * (p.splits + p.tree_sep) * d.n_nodes * d.n_q_heads;
   p.ws_o_bytes = ((parts * d.head_dim * sizeof(float) + 255) / 256) * 256;
   p.ws_ml_bytes = ((parts * sizeof(float2) + 255) / 256) * 256;
   return p;
@@ -834,12 +885,14 @@ hipError_t launch_attention(const tv_attn_desc& d, const AttnPlan& plan, const t
   a.max_prefix = d.max_prefix_len;
   a.chunk = plan.chunk;
   a.splits = plan.splits;
+  a.tree_sep = plan.tree_sep;
+  a.nparts = plan.splits + plan.tree_sep;
   a.row_groups = plan.row_groups;
   a.rows = plan.rows;
   const float scale = d.softmax_scale > 0.f ? d.softmax_scale : 1.f / sqrtf((float)d.head_dim);
   a.c = scale * 1.44269504088896340736f;
 
-  const dim3 grid(plan.splits, d.n_kv_heads * plan.row_groups, d.batch);
+  const dim3 grid(plan.splits + plan.tree_sep, d.n_kv_heads * plan.row_groups, d.batch);
   if (d.head_dim == 128)
     launch_split_rb<128>(plan.row_blocks, a, grid, stream);
   else

@@ -27,7 +27,9 @@ struct AttnPlan {
   int rows;          // query rows per (sequence, kv head) = n_nodes * group
   int row_blocks;    // 16-row MFMA blocks per wave (1..4)
   int row_groups;    // workgroups sharing one (sequence, kv head, split) in rows
-  int splits;        // prefix splits (the tree block is one more split)
+  int splits;        // prefix splits
+  int tree_sep;      // 1: the tree block has a workgroup of its own (split index `splits`);
+                     // 0: it runs in the last non-empty prefix split
   int chunk;         // prefix slots per split (multiple of the 32-token tile)
   int prefix_slots;  // upper bound of prefix slots per sequence
   size_t ws_o_bytes, ws_ml_bytes;
