@@ -546,11 +546,6 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
 #pragma unroll
       for (int db = 0; db < DB; ++db) vf[db] = vfrag(va, db);
     };
-    auto soft = [&](auto track_tag, int s, f32x4 (&cur)[2][RB]) {
-      mask_tile(s, cur);
-#pragma unroll
-      for (int mb = 0; mb < RB; ++mb) pb[mb] = softmax_block(cur, mb, track_tag);
-    };
     auto qk = [&](f32x4 (&nxt)[2][RB]) {
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) qk_mfma(kf, nxt, dc);
@@ -575,16 +570,30 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       TV_SCHED_FENCE;
     };
-    // R(s): operand reads first (their latency hides behind the softmax)
-    auto R = [&](auto track_tag, int s, f32x4 (&cur)[2][RB]) {
+    // R(s): the operand reads of M(s) and the mask of S(s): LDS work and
+    // little VALU.
+    auto R = [&](int s, f32x4 (&cur)[2][RB]) {
       read_k(s);
       read_v(s);
       TV_SCHED_FENCE;
-      soft(track_tag, s, cur);
+      mask_tile(s, cur);
       TV_SCHED_FENCE;
     };
-    auto M = [&](int s, f32x4 (&nxt)[2][RB]) {
-      if (s + 1 < ntiles) qk(nxt);
+    // M(s): the softmax of S(s) interleaved with the QK products of tile s+1
+    // (one MFMA, then a few VALU instructions that issue while it runs), then
+    // the PV products of tile s.  The QK of the tile after the last one reads
+    // a prefetched slot of valid rows; its result is never used.
+    auto M = [&](auto track_tag, f32x4 (&cur)[2][RB], f32x4 (&nxt)[2][RB]) {
+      TV_SCHED_FENCE;
+#pragma unroll
+      for (int mb = 0; mb < RB; ++mb) pb[mb] = softmax_block(cur, mb, track_tag);
+      qk(nxt);
+#pragma unroll
+      for (int i = 0; i < 2 * RB * DC; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);  // VALU incl. transcendental
+      }
+      TV_SCHED_FENCE;
       pv();
       TV_SCHED_FENCE;
     };
@@ -595,9 +604,9 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
       auto step = [&](auto track_tag, int s, f32x4 (&cur)[2][RB], f32x4 (&nxt)[2][RB]) {
         sync(s);
         const bool work = active && s < ntiles;
-        if (work) R(track_tag, s, cur);
+        if (work) R(s, cur);
         half_sync();
-        if (work) M(s, nxt);
+        if (work) M(track_tag, cur, nxt);
       };
       step(std::true_type{}, 0, sA, sB);
       for (int s = 1; s <= ntiles; s += 2) {
@@ -605,19 +614,21 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
         if (s + 1 <= ntiles) step(std::false_type{}, s + 1, sA, sB);
       }
     } else {
-      // b1 M(s-1) b2 R(s); M(s-1) writes S(s) into cur, R(s) consumes it
-      auto step = [&](int s, f32x4 (&cur)[2][RB]) {
+      // b1 M(s-1) b2 R(s): M(s-1) consumes S(s-1) in prev and writes S(s)
+      // into cur, which R(s) masks
+      auto step = [&](auto track_tag, int s, f32x4 (&prev)[2][RB], f32x4 (&cur)[2][RB]) {
         sync(s);
-        if (active) M(s - 1, cur);
+        if (active) M(track_tag, prev, cur);
         half_sync();
-        if (active && s < ntiles) R(std::false_type{}, s, cur);
+        if (active && s < ntiles) R(s, cur);
       };
       sync(0);
       half_sync();
-      if (active) R(std::true_type{}, 0, sA);
-      for (int s = 1; s <= ntiles; s += 2) {
-        step(s, sB);
-        if (s + 1 <= ntiles) step(s + 1, sA);
+      if (active) R(0, sA);
+      step(std::true_type{}, 1, sA, sB);  // ntiles >= 1
+      for (int s = 2; s <= ntiles; s += 2) {
+        step(std::false_type{}, s, sB, sA);
+        if (s + 1 <= ntiles) step(std::false_type{}, s + 1, sA, sB);
       }
     }
 #undef TV_SCHED_FENCE
