@@ -17,8 +17,9 @@
 //    contiguous ranges, one workgroup each, with `splits` chosen so that the
 //    grid fits the CUs in one round.  The workgroup of the last non-empty
 //    range also runs the tree block's tiles, masked with the packed ancestor
-//    bits, after its prefix tiles.  A combine kernel merges the (max, sum,
-//    unnormalised output) partials in a fixed order.
+//    bits, after its prefix tiles.  Each split writes, per row, its output
+//    divided by its own row sum (bf16) and the (reference max, sum) pair
+//    (fp32); a combine kernel merges them in a fixed order.
 //  * 32-token K/V tiles go from HBM straight to LDS with LDS DMA
 //    (global_load_lds_dwordx4) into a 4-slot ring, two tiles in flight, with
 //    no staging registers.  The tile layout in LDS (column blocks, below)
@@ -71,8 +72,8 @@ struct AttnArgs {
   const uint32_t* mask;
   const int32_t* block_idx;
   const int32_t* n_blocks;
-  float* part_o;
-  float2* part_ml;
+  bf16* part_o;     // [batch][nparts][hkv][rows][D], normalised by the row's own sum
+  float2* part_ml;  // [batch][nparts][hkv][rows]: (reference max, row sum)
   int32_t* dev_err;
   bf16* out;
   float* lse;
@@ -254,12 +255,9 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
   const char* vt = reinterpret_cast<const char*>(a.v_tree + ((int64_t)b * a.n * a.hkv + g) * D);
   const int64_t tree_rowb = (int64_t)a.hkv * ROWB;  // bytes between tree nodes
 
-  // partial rows of this split: ((b * nparts + s) * n + i) * hq + h
-  auto part_index = [&](int m) -> int64_t {
-    const int i = m / a.grp;
-    const int h = g * a.grp + m % a.grp;
-    return (((int64_t)b * a.nparts + s) * a.n + i) * a.hq + h;
-  };
+  // partial rows of this (sequence, split, kv head) are consecutive, in row
+  // order m = node * grp + head within the group
+  const int64_t prow0 = (((int64_t)b * a.nparts + s) * a.hkv + g) * a.rows;
 
   // ---- per-split tables staged in LDS --------------------------------------
   int bi0 = 0;         // partial: first block index of the split
@@ -293,7 +291,7 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
         if (err) raise_err(a.dev_err, err);
         for (int mb = 0; mb < RB; ++mb) {
           const int m = row0 + 16 * mb + col;
-          if (active && m < a.rows && grp4 == 0) a.part_ml[part_index(m)] = make_float2(-INFINITY, 0.f);
+          if (active && m < a.rows && grp4 == 0) a.part_ml[prow0 + m] = make_float2(-INFINITY, 0.f);
         }
         return;
       }
@@ -690,36 +688,69 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
   }
   if (err) raise_err(a.dev_err, err);
 
+  // ---- partial write -------------------------------------------------------
+  // Each row's output is divided by its own sum and stored as bf16, its
+  // (reference max, sum) pair in fp32.  A wave stages its 16 RB rows in its
+  // own part of the (now idle) ring and writes them back as contiguous 1 KB
+  // runs.  Staging address of row r, 32-byte chunk ch: r * 2D + 32 (ch ^ z(r))
+  // with z(r) = (r / RPB) mod DB, so that the 16 rows written by one
+  // instruction, and the rows read back by one, cover all 64 banks.
   if (!active) return;
+  {
+    constexpr int RPB = 128 / D;  // rows per 256-byte row of banks
+    constexpr int RPI = 512 / D;  // rows per 1 KB store
+    constexpr int QPR = D / 8;    // 16-byte pieces per row
+    static_assert(kWaves * 32 * RB * D <= kRing * SLOT_B, "staging fits the ring");
+    const uint32_t stage = ring_base + wave * (32 * RB * D);
 #pragma unroll
-  for (int mb = 0; mb < RB; ++mb) {
-    const float l = xsum16_32(lpart[mb]);
-    const int m = row0 + 16 * mb + col;
-    if (m < a.rows) {
-      const int64_t pi = part_index(m);
-      float* dst = a.part_o + pi * D + 4 * grp4;
+    for (int mb = 0; mb < RB; ++mb) {
+      const float l = xsum16_32(lpart[mb]);
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      const int r = 16 * mb + col;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db) = o[mb][db];
-      if (grp4 == 0) a.part_ml[pi] = make_float2(mref[mb], l);
+      for (int db = 0; db < DB; ++db) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (bf16)(o[mb][db][e] * inv);
+        *(__attribute__((address_space(3))) bf16x4*)lds_at(
+            stage + r * (2 * D) + 32 * (db ^ ((r / RPB) & (DB - 1))) + 8 * grp4) = v;
+      }
+      if (grp4 == 0 && row0 + r < a.rows) a.part_ml[prow0 + row0 + r] = make_float2(mref[mb], l);
+    }
+#pragma unroll
+    for (int j = 0; j < 16 * RB / RPI; ++j) {
+      const int r = j * RPI + lane / QPR;
+      const int q = lane % QPR;
+      const bf16x8 v = *(__attribute__((address_space(3))) const bf16x8*)lds_at(
+          stage + r * (2 * D) + 32 * ((q >> 1) ^ ((r / RPB) & (DB - 1))) + 16 * (q & 1));
+      if (row0 + r < a.rows) *reinterpret_cast<bf16x8*>(a.part_o + (prow0 + row0 + r) * D + 8 * q) = v;
     }
   }
 }
 
-// Merge the split partials of one (sequence, node, head): m = max m_s,
-// l = sum 2^(m_s - m) l_s, o = sum 2^(m_s - m) o_s / l.  Fixed split order.
+// Merge the split partials of one (sequence, node, head) row: with weights
+// w_s = 2^(m_s - m) l_s, m = max m_s, the output is sum w_s o_s / sum w_s
+// (o_s already divided by l_s) and the log-sum-exp is m + log2(sum w_s),
+// in natural-log units.  One wave per row: lane t C + c (C = D/8 chunks of
+// 8 elements, T = 64/C) folds the partials k = t, t+T, ... for elements
+// 8c..8c+7 into a running (max, sum, output), and the T running states are
+// merged across lanes in a fixed order.
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
-  constexpr int Q4 = D / 4;
-  constexpr int U = 16;
-  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t total = (int64_t)a.batch * a.n * a.hq * Q4;
-  if (gid >= total) return;
-  const int dq = (int)(gid % Q4);
-  const int64_t rowid = gid / Q4;  // (b * n + i) * hq + h
+  constexpr int C = D / 8;
+  constexpr int T = 64 / C;
+  constexpr int U = 8;  // partials per lane with loads in flight together
+  const int lane = threadIdx.x & 63;
+  const int64_t rowid = (int64_t)blockIdx.x * (kThreads / 64) + threadIdx.x / 64;  // (b * n + i) * hq + h
+  if (rowid >= (int64_t)a.batch * a.n * a.hq) return;
+  const int c = lane % C;
+  const int t = lane / C;
   const int h = (int)(rowid % a.hq);
   const int64_t bi = rowid / a.hq;
   const int i = (int)(bi % a.n);
   const int b = (int)(bi / a.n);
+  const int g = h / a.grp;
+  const int m_row = i * a.grp + h % a.grp;
 
   int err = 0;
   const int p_len = clamped_prefix(a, b, &err);
@@ -729,57 +760,81 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
   // which includes the tree.
   const int ns = (slots + a.chunk - 1) / a.chunk;
   const int cnt = a.tree_sep ? ns + 1 : max(ns, 1);
-  const int64_t stride = (int64_t)a.n * a.hq;  // partial rows between splits
-  const int64_t p0 = (((int64_t)b * a.nparts) * a.n + i) * a.hq + h;
+  const int64_t stride = (int64_t)a.hkv * a.rows;  // partial rows between splits
+  const int64_t p0 = ((int64_t)b * a.nparts * a.hkv + g) * a.rows + m_row;
   auto split_of = [&](int k) { return (a.tree_sep && k == ns) ? a.splits : k; };
-  // One pass over the partials in batches of U, each batch's (m, l) and o
-  // loads in flight together; the running (m, l, acc) is rescaled when a
-  // batch raises the maximum.  Empty partials have m = -inf and weigh 0.
-  float m = -INFINITY, l = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < cnt; k0 += U) {
+
+  float mx = -INFINITY, l = 0.f;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int k0 = t; k0 < cnt; k0 += T * U) {
     float2 ml[U];
-    f32x4 ov[U];
+    bf16x8 ov[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (k0 + u < cnt) {
-        const int64_t pi = p0 + split_of(k0 + u) * stride;
+      const int k = k0 + u * T;
+      if (k < cnt) {
+        const int64_t pi = p0 + split_of(k) * stride;
         ml[u] = a.part_ml[pi];
-        ov[u] = *reinterpret_cast<const f32x4*>(a.part_o + pi * D + 4 * dq);
+        ov[u] = *reinterpret_cast<const bf16x8*>(a.part_o + pi * D + 8 * c);
       } else {
         ml[u] = make_float2(-INFINITY, 0.f);
-        ov[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        ov[u] = bf16x8{};
       }
     }
-    float mb = m;
+    float mb = mx;
 #pragma unroll
     for (int u = 0; u < U; ++u) mb = fmaxf(mb, ml[u].x);
     if (mb == -INFINITY) continue;
-    const float r = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mb);
+    const float r = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx - mb);
     l *= r;
-    acc *= r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= r;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float w = ml[u].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[u].x - mb);
-      l += w * ml[u].y;
-      acc += w * ov[u];
+      // an empty partial (m = -inf) weighs 0 and its output is not read
+      const float w = ml[u].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[u].x - mb) * ml[u].y;
+      l += w;
+      if (w != 0.f) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(w, (float)ov[u][e], acc[e]);
+      }
     }
-    m = mb;
+    mx = mb;
   }
-
-  bf16x4 res;
+  // merge the T states of a chunk (lanes c, c + C, ...)
+#pragma unroll
+  for (int off = C; off < 64; off <<= 1) {
+    const float mo = __shfl_xor(mx, off);
+    const float lo = __shfl_xor(l, off);
+    float ao[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ao[e] = __shfl_xor(acc[e], off);
+    const float mn = fmaxf(mx, mo);
+    if (mn != -INFINITY) {
+      const float r0 = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx - mn);
+      const float r1 = mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mo - mn);
+      l = l * r0 + lo * r1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = acc[e] * r0 + ao[e] * r1;
+    }
+    mx = mn;
+  }
+  if (t != 0) return;
+  bf16x8 res;
   float lse_v;
-  if (m == -INFINITY) {
-    res = bf16x4{};
+  if (mx == -INFINITY) {
+    res = bf16x8{};
     lse_v = -INFINITY;
   } else {
     const float inv = 1.f / l;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) res[e] = (bf16)(acc[e] * inv);
-    lse_v = (m + log2f(l)) * 0.69314718055994530942f;
+    for (int e = 0; e < 8; ++e) res[e] = (bf16)(acc[e] * inv);
+    lse_v = (mx + log2f(l)) * 0.69314718055994530942f;
   }
-  *reinterpret_cast<bf16x4*>(a.out + rowid * D + 4 * dq) = res;
-  if (dq == 0 && a.lse) a.lse[rowid] = lse_v;
+  *reinterpret_cast<bf16x8*>(a.out + rowid * D + 8 * c) = res;
+  if (c == 0 && a.lse) a.lse[rowid] = lse_v;
 }
 
 template <int D, int RB>
@@ -857,7 +912,7 @@ AttnPlan plan_attention(const tv_attn_desc& d, int cu_count) {
   else if ((int64_t)units * (p.splits + 1) > std::max(cu_count, units * 2)) sep = false;
   p.tree_sep = sep ? 1 : 0;
   const size_t parts = (size_t)d.batch * (p.splits + p.tree_sep) * d.n_nodes * d.n_q_heads;
-  p.ws_o_bytes = ((parts * d.head_dim * sizeof(float) + 255) / 256) * 256;
+  p.ws_o_bytes = ((parts * d.head_dim * sizeof(uint16_t) + 255) / 256) * 256;  // bf16
   p.ws_ml_bytes = ((parts * sizeof(float2) + 255) / 256) * 256;
   return p;
 }
@@ -874,7 +929,7 @@ hipError_t launch_attention(const tv_attn_desc& d, const AttnPlan& plan, const t
   a.mask = p.mask;
   a.block_idx = p.block_idx;
   a.n_blocks = p.n_blocks;
-  a.part_o = reinterpret_cast<float*>(workspace);
+  a.part_o = reinterpret_cast<bf16*>(workspace);
   a.part_ml = reinterpret_cast<float2*>(reinterpret_cast<char*>(workspace) + plan.ws_o_bytes);
   a.dev_err = dev_err;
   a.out = (bf16*)p.out;
@@ -911,8 +966,8 @@ hipError_t launch_attention(const tv_attn_desc& d, const AttnPlan& plan, const t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  const int64_t total = (int64_t)d.batch * d.n_nodes * d.n_q_heads * (d.head_dim / 4);
-  const dim3 cgrid((unsigned)((total + kThreads - 1) / kThreads));
+  const int64_t rows_total = (int64_t)d.batch * d.n_nodes * d.n_q_heads;  // one wave each
+  const dim3 cgrid((unsigned)((rows_total + kThreads / 64 - 1) / (kThreads / 64)));
   if (d.head_dim == 128)
     hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, dim3(kThreads), 0, stream, a);
   else
