@@ -24,6 +24,7 @@ Helper modes (used to produce the committed profile summaries):
   --copy-calibration      plain 256 MiB device copies, for scaling counters
   --pmc-summary F W CF CW rocprofv3 FETCH_SIZE / WRITE_SIZE directories (bench
                           run, copy run) -> traffic summary text on stdout
+                          (with --workload: the workload those runs used)
   --trace-summary CSV CMD rocprofv3 kernel-stats CSV -> text summary on stdout
 """
 
@@ -314,7 +315,7 @@ def read_traffic():
 def main():
     args = parse()
     if args.pmc_summary:
-        pmc_summary(*args.pmc_summary)
+        pmc_summary(*args.pmc_summary, workload=args.workload)
         return
     if args.trace_summary:
         trace_summary(*args.trace_summary)
@@ -498,7 +499,7 @@ def _counter_per_dispatch(directory, counter, match):
     return {k: sum(v.values()) / len(v) for k, v in per.items() if v}
 
 
-def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, workload="8b_layer"):
     fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", "attn_")
     write = _counter_per_dispatch(write_dir, "WRITE_SIZE", "attn_")
     cf = _counter_per_dispatch(copy_fetch_dir, "FETCH_SIZE", "")
@@ -511,9 +512,11 @@ def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     tot_f = sum(fetch.get(k, 0.0) for k in ATTN_KERNELS)
     tot_w = sum(write.get(k, 0.0) for k in ATTN_KERNELS)
     hbm = int(round(tot_f * f_scale + tot_w * w_scale))
+    what = {"8b_layer": "8B-layer workload (bench.py default",
+            "long_context": "60K-prefix workload, full KV (bench.py --workload long_context"}
     lines = [
-        "HBM traffic of one tv_tree_attention call, 8B-layer workload (bench.py default,",
-        "inputs rotated over 16 copies so that they miss the Infinity Cache).",
+        f"HBM traffic of one tv_tree_attention call, {what.get(workload, workload + ' (')},",
+        "inputs rotated over copies so that they miss the Infinity Cache).",
         "Counter readings are scaled by what the same counter reads for a plain",
         f"device copy of {COPY_BYTES} bytes (bench.py --copy-calibration).",
         f"source_sha256_16: {source_hash()}",

@@ -298,6 +298,42 @@ def test_accept_malformed_parents():
     assert int(err.item()) == binding.DERR_BAD_PARENT
 
 
+def test_accept_workspace_reused_across_calls():
+    """One workspace and one set of output buffers serve consecutive calls
+    with different inputs: nothing from a previous call leaks into the next
+    (outputs are scrambled in between, so a stale result shows)."""
+    _say("[accept] one workspace, several calls")
+    rng = np.random.default_rng(17)
+    bsz, n, v = 3, 40, 70000
+    ws = torch.empty(binding.accept_workspace_size(bsz, n, v), dtype=torch.uint8, device="cuda")
+    outs = tuple(torch.empty(sh, dtype=torch.int32, device="cuda")
+                 for sh in ((bsz, n), (bsz,), (bsz, n), (bsz,)))
+    for call in range(4):
+        parents = np.full((bsz, n), -1, dtype=np.int32)
+        for b in range(bsz):
+            for i in range(1, n):
+                parents[b, i] = rng.integers(0, i)
+        logits = W.f32_to_bf16_bits(rng.normal(size=(bsz, n, v)).astype(np.float32))
+        amax_ref, _, _, _ = oracle.greedy_accept(logits, parents, np.zeros((bsz, n), np.int32))
+        draft = np.zeros((bsz, n), dtype=np.int32)
+        for b in range(bsz):
+            for i in range(1, n):
+                draft[b, i] = amax_ref[b, parents[b, i]] if rng.random() < 0.8 else rng.integers(v)
+        for t in outs:
+            t.fill_(-7)
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        amax, alen, path, bonus = binding.greedy_accept(dev_bf16(logits), dev_i32(parents),
+                                                        dev_i32(draft), workspace=ws, dev_err=err,
+                                                        outputs=outs)
+        torch.cuda.synchronize()
+        r_amax, r_alen, r_path, r_bonus = oracle.greedy_accept(logits, parents, draft)
+        assert np.array_equal(amax.cpu().numpy(), r_amax), f"call {call}"
+        assert np.array_equal(alen.cpu().numpy(), r_alen), f"call {call}"
+        assert np.array_equal(path.cpu().numpy(), r_path), f"call {call}"
+        assert np.array_equal(bonus.cpu().numpy(), r_bonus), f"call {call}"
+        assert int(err.item()) == 0
+
+
 # ---------------------------------------------------------------------------
 # a7 commit
 # ---------------------------------------------------------------------------
