@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for tree verification -- test infrastructure only.
+"""fp64 CPU oracle for tree verification and SpecPV block selection -- test
+infrastructure only.
 
 Only the tests, the smoke check and the benchmark's CPU-baseline leg may use
 this package.  The product path (the HIP library and its Python binding)
@@ -15,4 +16,13 @@ from .tree_verify import (  # noqa: F401
     greedy_accept,
     pack_accepted_tokens,
     tree_attention,
+)
+from .block_select import (  # noqa: F401
+    REDUCTIONS,
+    block_scores,
+    block_summaries,
+    num_blocks,
+    select_blocks,
+    specpv_select,
+    ub_score,
 )

@@ -83,3 +83,84 @@ def test_wrong_acceptance_rule_is_caught(monkeypatch, mut):
     monkeypatch.setattr(TV, "greedy_accept", broken)
     monkeypatch.setattr(pins.oracle, "greedy_accept", broken)
     assert any(_fails(pins.test_p3_accept_equals_path_enumeration, s) for s in range(40))
+
+
+# ---------------------------------------------------------------------------
+# block selection (SpecPV)
+# ---------------------------------------------------------------------------
+
+import oracle.block_select as BS  # noqa: E402
+from tests import test_oracle_select_pins as spins  # noqa: E402
+
+
+def test_bound_with_max_key_only_is_caught(monkeypatch):
+    # forgetting the min key: negative query coordinates then bound nothing
+    monkeypatch.setattr(BS, "ub_score", lambda q, hi, lo: (q * hi).sum(axis=-1))
+    assert _fails(spins.test_p14_bound_holds_for_every_token, 0)
+    assert _fails(spins.test_p14_scores_equal_corner_brute_force, spins.CASES[0], "mean")
+
+
+def test_swapped_summaries_are_caught(monkeypatch):
+    orig = BS.block_summaries
+    swapped = lambda *a: (lambda r: (r[1], r[0], r[2]))(orig(*a))  # noqa: E731
+    monkeypatch.setattr(BS, "block_summaries", swapped)
+    monkeypatch.setattr(spins.oracle, "block_summaries", swapped)
+    assert _fails(spins.test_p13_summary_contains_and_attains_every_coordinate, spins.CASES[0])
+
+
+def test_summary_including_a_row_past_the_prefix_is_caught(monkeypatch):
+    # one row too many in the last block pulls a cache row past the prefix in
+    monkeypatch.setattr(BS, "num_blocks", lambda p, bs: -(-(int(p) + 1) // bs))
+    assert _fails(spins.test_p13_summary_contains_and_attains_every_coordinate, spins.CASES[1])
+
+
+@pytest.mark.parametrize("mut", ["first_node", "sum", "min"])
+def test_wrong_reduction_is_caught(monkeypatch, mut):
+    orig = BS._reduce
+
+    def broken(per_node, reduction):
+        if mut == "first_node" and reduction == "last":
+            return per_node[0]
+        if mut == "sum" and reduction == "mean":
+            return per_node.sum(axis=0)
+        if mut == "min" and reduction == "max":
+            return per_node.min(axis=0)
+        return orig(per_node, reduction)
+    monkeypatch.setattr(BS, "_reduce", broken)
+    red = {"first_node": "last", "sum": "mean", "min": "max"}[mut]
+    assert _fails(spins.test_p14_scores_equal_corner_brute_force, spins.CASES[0], red)
+
+
+def test_wrong_head_to_kv_group_is_caught(monkeypatch):
+    orig = BS.block_scores
+
+    def broken(q, kmax, kmin, n_valid, reduction="mean", **kw):
+        # heads interleaved over KV groups instead of contiguous groups
+        qq = np.asarray(q)
+        hq, hkv = qq.shape[2], kmax.shape[1]
+        grp = hq // hkv
+        perm = [(h % hkv) * grp + h // hkv for h in range(hq)]
+        return orig(qq[:, :, perm, :], kmax, kmin, n_valid, reduction, **kw)
+    monkeypatch.setattr(BS, "block_scores", broken)
+    monkeypatch.setattr(spins.oracle, "block_scores", broken)
+    assert _fails(spins.test_p14_scores_equal_corner_brute_force, spins.CASES[3], "mean")
+
+
+@pytest.mark.parametrize("mut", ["high_id_ties", "window_short", "no_sinks"])
+def test_wrong_selection_rule_is_caught(monkeypatch, mut):
+    orig = BS.select_blocks
+
+    def broken(scores_row, n_valid, n_sink, n_window, top_k):
+        if mut == "window_short":
+            return orig(scores_row, n_valid, n_sink, max(n_window - 1, 0), top_k)
+        if mut == "no_sinks":
+            return orig(scores_row, n_valid, 0, n_window, top_k + n_sink)
+        rest = [j for j in range(n_valid) if j >= n_sink and j < n_valid - n_window]
+        ranked = sorted(rest, key=lambda j: (-float(scores_row[j]), -j))
+        keep = set(range(min(n_sink, n_valid))) | set(range(max(n_valid - n_window, 0), n_valid))
+        return np.asarray(sorted(keep | set(ranked[:top_k])), dtype=np.int64)
+    monkeypatch.setattr(BS, "select_blocks", broken)
+    monkeypatch.setattr(spins.oracle, "select_blocks", broken)
+    caught = _fails(spins.test_p17_hand_worked_selection) or any(
+        _fails(spins.test_p17_selection_equals_brute_force_counting, s) for s in range(30))
+    assert caught

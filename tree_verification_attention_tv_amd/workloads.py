@@ -26,6 +26,13 @@ Workloads (one seeded generator each):
                      KV list of 64-token blocks (2 sink blocks, the last 16
                      blocks and 46 distinct random others).
 
+SpecPV retrieval settings (App. D "Generation Settings": 16-token blocks,
+32 sink tokens, a 128-token local window; Sec. 4.3: a 4096-token partial KV
+budget) are the ``SPECPV_*`` constants.  ``make_select_case`` draws small
+seeded cases for block selection, optionally with planted relevant blocks:
+every query of a sequence leans toward one random direction, and one token of
+each planted block carries a large multiple of that direction.
+
 Sources for the shapes: "Dynamic Speculative Decoding" (Problem Context:
 ~1000-token prompts; Benchmark Table: (steps, topk, draft tokens) triples);
 SpecBlock (Sec. 4 setup: 8B-class GQA targets at batch 1; papernotes key
@@ -323,6 +330,16 @@ def specpv_block_list(rng: np.random.Generator, prefix_len: int, block_size: int
     return np.asarray(sorted(sink + window + [int(x) for x in pick]), dtype=np.int32)
 
 
+# SpecPV App. D: blocks of 16 tokens, 32 sink tokens (2 blocks), a 128-token
+# window (8 blocks); Sec. 4.3: a 4096-token budget, so 256 blocks of which
+# 246 are retrieved.
+SPECPV_BLOCK_SIZE = 16
+SPECPV_SINK_BLOCKS = 2
+SPECPV_WINDOW_BLOCKS = 8
+SPECPV_BUDGET_TOKENS = 4096
+SPECPV_TOP_K = SPECPV_BUDGET_TOKENS // SPECPV_BLOCK_SIZE - SPECPV_SINK_BLOCKS - SPECPV_WINDOW_BLOCKS
+
+
 # ---------------------------------------------------------------------------
 # the five workloads
 # ---------------------------------------------------------------------------
@@ -430,4 +447,48 @@ def make_random_case(seed: int, *, batch: int, n_nodes: int, hq: int, hkv: int,
         wl.block_size = block_size
         wl.block_idx = bidx
         wl.n_blocks = np.array([len(x) for x in lists], dtype=np.int32)
+    return wl
+
+
+def make_select_case(seed: int, *, batch: int, n_nodes: int, hq: int, hkv: int, d: int,
+                     prefix_lens, block_size: int, n_planted: int = 0,
+                     query_lean: float = 2.0, key_lean: float | None = None) -> Workload:
+    """Seeded case for block selection: N(0,1) bf16 queries and keys, plus,
+    when ``n_planted`` > 0, planted relevant blocks.
+
+    For each sequence a random unit direction u is drawn; every query gets
+    ``query_lean * u`` added, and one random token in each of ``n_planted``
+    distinct random blocks below the prefix gets ``key_lean * u`` added to its
+    key in every KV head (default key_lean = 8 * sqrt(d)).  The planted block
+    ids are returned in ``wl.block_idx`` / ``wl.n_blocks`` (bookkeeping only,
+    not an input of the method).
+    """
+    wl = make_random_case(seed, batch=batch, n_nodes=n_nodes, hq=hq, hkv=hkv, d=d,
+                          prefix_lens=prefix_lens, name="select")
+    wl.block_size = block_size
+    if not n_planted:
+        return wl
+    if key_lean is None:
+        key_lean = 8.0 * math.sqrt(d)
+    rng = np.random.Generator(np.random.PCG64(seed * 7 + 3))
+    q = bf16_bits_to_f32(wl.q)
+    planted = np.full((batch, n_planted), -1, dtype=np.int32)
+    counts = np.zeros(batch, dtype=np.int32)
+    for b in range(batch):
+        u = rng.standard_normal(d).astype(np.float32)
+        u /= np.float32(np.linalg.norm(u))
+        q[b] += np.float32(query_lean) * u
+        p = int(wl.prefix_len[b])
+        n_avail = (p + block_size - 1) // block_size
+        take = min(n_planted, n_avail)
+        blocks = np.sort(rng.choice(n_avail, size=take, replace=False)) if take else []
+        for t, blk in enumerate(blocks):
+            lo, hi = int(blk) * block_size, min((int(blk) + 1) * block_size, p)
+            row = int(rng.integers(lo, hi))
+            k = bf16_bits_to_f32(wl.k_cache[b, :, row, :])
+            wl.k_cache[b, :, row, :] = f32_to_bf16_bits(k + np.float32(key_lean) * u)
+            planted[b, t] = blk
+        counts[b] = take
+    wl.q = f32_to_bf16_bits(q)
+    wl.block_idx, wl.n_blocks = planted, counts
     return wl
