@@ -13,6 +13,9 @@
  *   tv_greedy_accept     per-node vocabulary argmax, longest accepted path,
  *                        accepted length and bonus token
  *   tv_commit_kv         copy the accepted nodes' K/V rows into the cache
+ *   tv_block_summaries   per-block element-wise max/min keys (SpecPV retrieval)
+ *   tv_select_blocks     score blocks against the tree's queries and pick the
+ *                        sink + top-k + window list for partial attention
  *
  * Conventions shared by every call
  * --------------------------------
@@ -220,6 +223,98 @@ tv_status tv_commit_kv(const void* k_tree, const void* v_tree, const int32_t* ac
                        int64_t cache_seq_stride, int32_t cache_capacity, int32_t batch,
                        int32_t n_nodes, int32_t n_kv_heads, int32_t head_dim, int32_t* dev_err,
                        hipStream_t stream);
+
+/*
+ * tv_block_summaries -- element-wise max and min key of every KV block.
+ *
+ * Source: SpecPV Sec. 3.2 "Partial Verification": the key states of each
+ * block are summarised by their element-wise maximum and minimum, and the
+ * summaries are cached so that retrieval does not re-read the keys.
+ *
+ * Block j of sequence b covers cache rows j*block_size ..
+ * min((j+1)*block_size, prefix_len[b]) - 1.  For every kv head h and every
+ * block j with first_token[b] <= (j+1)*block_size - 1 and j*block_size <
+ * prefix_len[b] (that is, every block that holds a row in
+ * [first_token[b], prefix_len[b])):
+ *   summaries[b][h][j][0][d] = max over the block's rows of k_cache[..][d]
+ *   summaries[b][h][j][1][d] = min over the block's rows of k_cache[..][d]
+ * as bf16 values (a maximum or minimum of zero may carry either sign).  No
+ * other record is touched, so after tv_commit_kv a call with first_token =
+ * the old prefix length and prefix_len = the new one updates the cache.
+ *
+ * k_cache     bf16, sequence b at k_cache + b * cache_seq_stride elements
+ *             (0 = n_kv_heads*capacity*head_dim), then [n_kv_heads][capacity][head_dim]
+ * prefix_len  int32 [batch]; first_token int32 [batch] or NULL (= 0)
+ * summaries   bf16 [batch][n_kv_heads][ceil(capacity / block_size)][2][head_dim]
+ * max_tokens  host-side estimate of max_b (prefix_len[b] - first_token[b]);
+ *             it only sizes the grid (every block is processed whatever it is).
+ * Supported: head_dim 64 or 128, block_size >= 1.
+ * Fallback: a sequence with prefix_len outside [0, capacity] or first_token
+ *   outside [0, prefix_len] is skipped (TV_DERR_BAD_PREFIX).
+ */
+tv_status tv_block_summaries(const void* k_cache, int64_t cache_seq_stride,
+                             int32_t cache_capacity, int32_t batch, int32_t n_kv_heads,
+                             int32_t head_dim, int32_t block_size, const int32_t* prefix_len,
+                             const int32_t* first_token, int32_t max_tokens, void* summaries,
+                             int32_t* dev_err, hipStream_t stream);
+
+/*
+ * tv_select_blocks -- the KV blocks a partial verification attends to.
+ *
+ * Sources: SpecPV Sec. 3.2 (blocks are scored against the query states of
+ * all candidate tokens, the per-query scores folded by a reduction such as
+ * max, mean or last; the partial cache keeps sink blocks, retrieved blocks
+ * and a local window), App. C (mean works best), App. D (16-token blocks,
+ * 32 sink tokens, a 128-token window).
+ *
+ * For sequence b let nv = ceil(P / block_size), P = prefix_len[b].  For block
+ * j < nv, query head h (kv head g = h / (Hq/Hkv)) and node i:
+ *   ub(i, h, j) = sum_d max(q[b][i][h][d] * hi[d], q[b][i][h][d] * lo[d])
+ * with hi, lo = summaries[b][g][j][0], [1] (the largest q.k over the box
+ * between them, so an upper bound of q.k for each key of the block).  Then
+ *   TV_REDUCE_MEAN: score[j] = mean over h of (mean over i of ub)
+ *   TV_REDUCE_MAX:  score[j] = mean over h of (max over i of ub)
+ *   TV_REDUCE_LAST: score[j] = mean over h of ub(n_nodes - 1, h, j)
+ * accumulated in fp32.  The selected list is the union, ascending and
+ * without duplicates, of
+ *   sinks   0 .. n_sink_blocks - 1,
+ *   window  the last n_window_blocks blocks below nv,
+ *   the top_k blocks of the rest by score (equal scores: lower id first),
+ * each clipped to [0, nv).  It is written to block_idx[b][0 .. n_blocks[b]-1]
+ * and the rest of the row is set to -1: the format tv_tree_attention's
+ * partial mode reads (same block_size).
+ *
+ * Layouts: q bf16 [batch][n_nodes][n_q_heads][head_dim]; summaries as
+ *   written by tv_block_summaries for this cache_capacity and block_size;
+ *   prefix_len int32 [batch]; block_idx int32 [batch][max_blocks];
+ *   n_blocks int32 [batch]; scores fp32 [batch][ceil(capacity / block_size)]
+ *   or NULL (entries j >= nv are not written).
+ * Supported: head_dim 64 or 128; TV_REDUCE_MAX needs n_q_heads / n_kv_heads
+ *   <= TV_MAX_SELECT_GROUP; max_blocks >= n_sink_blocks + n_window_blocks + top_k.
+ * Fallback: prefix_len outside [0, min(capacity, max_prefix_len)] is clamped
+ *   to that range (TV_DERR_BAD_PREFIX).  NaN or infinite inputs give an
+ *   unspecified (but valid, ascending) list.
+ * Workspace: tv_select_blocks_workspace_size(desc) bytes, 256-byte aligned.
+ */
+enum { TV_REDUCE_MEAN = 0, TV_REDUCE_MAX = 1, TV_REDUCE_LAST = 2 };
+#define TV_MAX_SELECT_GROUP 64
+
+typedef struct {
+  int32_t batch, n_nodes, n_q_heads, n_kv_heads, head_dim;
+  int32_t cache_capacity;   /* rows per (sequence, kv head) of the summarised cache */
+  int32_t max_prefix_len;   /* host-side upper bound of prefix_len[] (grid sizing) */
+  int32_t block_size;       /* tokens per block (>= 1) */
+  int32_t n_sink_blocks, n_window_blocks, top_k;  /* each >= 0 */
+  int32_t reduction;        /* TV_REDUCE_MEAN, TV_REDUCE_MAX or TV_REDUCE_LAST */
+  int32_t max_blocks;       /* columns of block_idx */
+  int32_t reserved;         /* must be 0 */
+} tv_select_desc;
+
+size_t tv_select_blocks_workspace_size(const tv_select_desc* desc);
+tv_status tv_select_blocks(const tv_select_desc* desc, const void* q, const void* summaries,
+                           const int32_t* prefix_len, int32_t* block_idx, int32_t* n_blocks,
+                           float* scores, void* workspace, size_t workspace_bytes,
+                           int32_t* dev_err, hipStream_t stream);
 
 /* human-readable name of a status code (static storage) */
 const char* tv_status_string(tv_status status);

@@ -83,3 +83,44 @@ def test_attention_descriptor_tree_placement_is_validated():
     assert L.tv_tree_attention(ctypes.byref(d), None, None, 0, None, None) == 2
     d.tree_placement, d.reserved = 0, 1
     assert L.tv_tree_attention(ctypes.byref(d), None, None, 0, None, None) == 2
+
+
+def test_header_declares_the_selection_calls():
+    names = declared_functions()
+    for fn in ("tv_block_summaries", "tv_select_blocks", "tv_select_blocks_workspace_size"):
+        assert fn in names
+
+
+def test_selection_host_checks_enqueue_nothing():
+    L = binding.lib()
+    p = ctypes.c_void_p(256)
+    # summaries: null cache, unsupported head_dim, zero block size, bad stride
+    assert L.tv_block_summaries(None, 0, 64, 1, 1, 128, 16, p, None, 64, p, None, None) == 1
+    assert L.tv_block_summaries(p, 0, 64, 1, 1, 96, 16, p, None, 64, p, None, None) == 3
+    assert L.tv_block_summaries(p, 0, 64, 1, 1, 128, 0, p, None, 64, p, None, None) == 2
+    assert L.tv_block_summaries(p, 8, 64, 1, 1, 128, 16, p, None, 64, p, None, None) == 2
+    assert L.tv_block_summaries(p, 0, 64, 0, 1, 128, 16, p, None, 64, p, None, None) == 0
+
+    def desc(**kw):
+        base = dict(batch=1, n_nodes=60, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                    cache_capacity=60096, max_prefix_len=60000, block_size=16, n_sink_blocks=2,
+                    n_window_blocks=8, top_k=246, reduction=binding.REDUCE_MEAN,
+                    max_blocks=256, reserved=0)
+        base.update(kw)
+        return binding.SelectDesc(**base)
+
+    def call(d, ptr=None):
+        return L.tv_select_blocks(ctypes.byref(d), ptr, ptr, ptr, ptr, ptr, None, ptr, 1 << 20,
+                                  None, None)
+
+    assert call(desc()) == 1                                   # valid, null pointers
+    assert call(desc(max_blocks=255)) == 2                     # list cannot hold the selection
+    assert call(desc(reduction=3)) == 2
+    assert call(desc(head_dim=96)) == 3
+    assert call(desc(block_size=0)) == 2
+    assert call(desc(top_k=-1)) == 2
+    assert call(desc(max_prefix_len=60097)) == 2
+    assert call(desc(reserved=1)) == 2
+    assert call(desc(n_q_heads=130, n_kv_heads=2, reduction=binding.REDUCE_MAX)) == 3
+    assert call(desc(n_q_heads=130, n_kv_heads=2, reduction=binding.REDUCE_MEAN)) == 1
+    assert L.tv_select_blocks(None, p, p, p, p, p, None, p, 1 << 20, None, None) == 1

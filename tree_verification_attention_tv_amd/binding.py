@@ -51,6 +51,23 @@ class AttnPtrs(ctypes.Structure):
     ]
 
 
+class SelectDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_nodes", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("cache_capacity", ctypes.c_int32), ("max_prefix_len", ctypes.c_int32),
+        ("block_size", ctypes.c_int32), ("n_sink_blocks", ctypes.c_int32),
+        ("n_window_blocks", ctypes.c_int32), ("top_k", ctypes.c_int32),
+        ("reduction", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+REDUCE_MEAN, REDUCE_MAX, REDUCE_LAST = 0, 1, 2
+REDUCTIONS = {"mean": REDUCE_MEAN, "max": REDUCE_MAX, "last": REDUCE_LAST}
+MAX_SELECT_GROUP = 64
+
+
 def library_path() -> str:
     return _LIB_PATH
 
@@ -85,6 +102,14 @@ def lib() -> ctypes.CDLL:
             L.tv_commit_kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32,
                                        i32, vp, vp]
             L.tv_commit_kv.restype = i32
+            L.tv_block_summaries.argtypes = [vp, i64, i32, i32, i32, i32, i32, vp, vp, i32, vp,
+                                             vp, vp]
+            L.tv_block_summaries.restype = i32
+            L.tv_select_blocks_workspace_size.argtypes = [ctypes.POINTER(SelectDesc)]
+            L.tv_select_blocks_workspace_size.restype = sz
+            L.tv_select_blocks.argtypes = [ctypes.POINTER(SelectDesc), vp, vp, vp, vp, vp, vp, vp,
+                                           sz, vp, vp]
+            L.tv_select_blocks.restype = i32
             L.tv_status_string.argtypes = [i32]
             L.tv_status_string.restype = ctypes.c_char_p
             L.tv_version.argtypes = []
@@ -282,3 +307,95 @@ def commit_kv(k_tree, v_tree, accept_path, accept_len, prefix_len, k_cache, v_ca
         _ptr(new_prefix_len), _ptr(k_cache), _ptr(v_cache), int(k_cache.stride(0)), cap, bsz,
         n, hkv, d, _err_ptr(dev_err), _stream(k_cache.device)))
     return new_prefix_len
+
+
+def summaries_shape(k_cache, block_size):
+    """[B][Hkv][ceil(cap / block_size)][2][D] for a [B][Hkv][cap][D] cache."""
+    bsz, hkv, cap, d = k_cache.shape
+    return (bsz, hkv, (cap + block_size - 1) // block_size, 2, d)
+
+
+def block_summaries(k_cache, prefix_len, *, block_size, first_token=None, max_tokens=None,
+                    summaries=None, dev_err=None):
+    """Element-wise max/min key records of the blocks holding rows in
+    [first_token, prefix_len) (all blocks of the prefix when first_token is
+    None).  Writes into ``summaries`` (allocated if None) and returns it."""
+    _on_gpu("k_cache", k_cache, torch.bfloat16, contiguous=False)
+    _on_gpu("prefix_len", prefix_len, torch.int32)
+    if first_token is not None:
+        _on_gpu("first_token", first_token, torch.int32)
+    bsz, hkv, cap, d = k_cache.shape
+    if k_cache.stride()[1:] != (cap * d, d, 1):
+        raise ValueError("k_cache must be [B][Hkv][cap][D] with contiguous rows per sequence")
+    shape = summaries_shape(k_cache, block_size)
+    if summaries is None:
+        summaries = torch.empty(shape, dtype=torch.bfloat16, device=k_cache.device)
+    _on_gpu("summaries", summaries, torch.bfloat16)
+    if tuple(summaries.shape) != shape:
+        raise ValueError(f"summaries must have shape {shape}")
+    if max_tokens is None:
+        max_tokens = cap
+    _check("tv_block_summaries", lib().tv_block_summaries(
+        _ptr(k_cache), int(k_cache.stride(0)), cap, bsz, hkv, d, int(block_size),
+        _ptr(prefix_len), _ptr(first_token), int(max_tokens), _ptr(summaries),
+        _err_ptr(dev_err), _stream(k_cache.device)))
+    return summaries
+
+
+def select_desc(q, summaries, *, cache_capacity, max_prefix_len, block_size, n_sink, n_window,
+                top_k, reduction="mean", max_blocks=None) -> SelectDesc:
+    bsz, n, hq, d = q.shape
+    hkv = summaries.shape[1]
+    if max_blocks is None:
+        max_blocks = n_sink + n_window + top_k
+    return SelectDesc(batch=bsz, n_nodes=n, n_q_heads=hq, n_kv_heads=hkv, head_dim=d,
+                      cache_capacity=int(cache_capacity), max_prefix_len=int(max_prefix_len),
+                      block_size=int(block_size), n_sink_blocks=int(n_sink),
+                      n_window_blocks=int(n_window), top_k=int(top_k),
+                      reduction=REDUCTIONS[reduction], max_blocks=int(max_blocks), reserved=0)
+
+
+def select_workspace_size(desc: SelectDesc) -> int:
+    return int(lib().tv_select_blocks_workspace_size(ctypes.byref(desc)))
+
+
+def select_blocks(q, summaries, prefix_len, *, cache_capacity, max_prefix_len, block_size,
+                  n_sink, n_window, top_k, reduction="mean", max_blocks=None, want_scores=False,
+                  outputs=None, scores=None, workspace=None, dev_err=None):
+    """Score every block against the tree's queries and select sink + top-k +
+    window.  Returns (block_idx int32 [B][max_blocks], n_blocks int32 [B]) and
+    the fp32 scores [B][nb] when asked."""
+    _on_gpu("q", q, torch.bfloat16)
+    _on_gpu("summaries", summaries, torch.bfloat16)
+    _on_gpu("prefix_len", prefix_len, torch.int32)
+    bsz, n, hq, d = q.shape
+    nb_cap = (int(cache_capacity) + int(block_size) - 1) // int(block_size)
+    if tuple(summaries.shape) != (bsz, summaries.shape[1], nb_cap, 2, d):
+        raise ValueError("summaries do not match q, cache_capacity and block_size")
+    desc = select_desc(q, summaries, cache_capacity=cache_capacity,
+                       max_prefix_len=max_prefix_len, block_size=block_size, n_sink=n_sink,
+                       n_window=n_window, top_k=top_k, reduction=reduction,
+                       max_blocks=max_blocks)
+    dev = q.device
+    if outputs is None:
+        outputs = (torch.empty((bsz, desc.max_blocks), dtype=torch.int32, device=dev),
+                   torch.empty((bsz,), dtype=torch.int32, device=dev))
+    block_idx, n_blocks = outputs
+    _on_gpu("block_idx", block_idx, torch.int32)
+    _on_gpu("n_blocks", n_blocks, torch.int32)
+    if tuple(block_idx.shape) != (bsz, desc.max_blocks):
+        raise ValueError("block_idx must be [B][max_blocks]")
+    if want_scores and scores is None:
+        scores = torch.empty((bsz, nb_cap), dtype=torch.float32, device=dev)
+    if scores is not None:
+        _on_gpu("scores", scores, torch.float32)
+    ws_bytes = select_workspace_size(desc)
+    if ws_bytes == 0:
+        raise TVError("tv_select_blocks_workspace_size", 2)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    _check("tv_select_blocks", lib().tv_select_blocks(
+        ctypes.byref(desc), _ptr(q), _ptr(summaries), _ptr(prefix_len), _ptr(block_idx),
+        _ptr(n_blocks), _ptr(scores), _ptr(workspace), workspace.numel(), _err_ptr(dev_err),
+        _stream(dev)))
+    return (block_idx, n_blocks, scores) if want_scores else (block_idx, n_blocks)

@@ -21,7 +21,8 @@ BUILD = os.path.join(CSRC, "_build")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtreeverify.so")
 
-SOURCES = ["tv_api.cpp", "tv_mask.hip", "tv_attention.hip", "tv_accept.hip", "tv_commit.hip"]
+SOURCES = ["tv_api.cpp", "tv_mask.hip", "tv_attention.hip", "tv_accept.hip", "tv_commit.hip",
+           "tv_select.hip"]
 ARCH = "gfx950"
 
 

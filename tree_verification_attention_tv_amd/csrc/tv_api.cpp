@@ -57,6 +57,30 @@ tv_status check_attn_desc(const tv_attn_desc* d) {
   return TV_OK;
 }
 
+tv_status check_select_desc(const tv_select_desc* d) {
+  if (!d) return TV_ERR_NULL;
+  if (d->batch < 0 || d->batch > 65535 || d->n_nodes < 1 || d->n_nodes > TV_MAX_NODES)
+    return TV_ERR_SHAPE;
+  if (d->n_q_heads < 1 || d->n_kv_heads < 1 || d->n_kv_heads > 65535 ||
+      d->n_q_heads % d->n_kv_heads != 0)
+    return TV_ERR_SHAPE;
+  if (d->head_dim != 64 && d->head_dim != 128) return TV_ERR_UNSUPPORTED;
+  if (d->cache_capacity < 0 || d->max_prefix_len < 0 || d->max_prefix_len > d->cache_capacity)
+    return TV_ERR_SHAPE;
+  if (d->block_size < 1 || d->n_sink_blocks < 0 || d->n_window_blocks < 0 || d->top_k < 0)
+    return TV_ERR_SHAPE;
+  if (d->reduction != TV_REDUCE_MEAN && d->reduction != TV_REDUCE_MAX &&
+      d->reduction != TV_REDUCE_LAST)
+    return TV_ERR_SHAPE;
+  if (d->reduction == TV_REDUCE_MAX && d->n_q_heads / d->n_kv_heads > TV_MAX_SELECT_GROUP)
+    return TV_ERR_UNSUPPORTED;
+  if (d->max_blocks < 0 ||
+      (int64_t)d->max_blocks < (int64_t)d->n_sink_blocks + d->n_window_blocks + d->top_k)
+    return TV_ERR_SHAPE;
+  if (d->reserved != 0) return TV_ERR_SHAPE;
+  return TV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -155,6 +179,55 @@ tv_status tv_commit_kv(const void* k_tree, const void* v_tree, const int32_t* ac
                                          new_prefix_len, k_cache, v_cache, cache_seq_stride,
                                          cache_capacity, batch, n_nodes, n_kv_heads, head_dim,
                                          dev_err, stream));
+}
+
+tv_status tv_block_summaries(const void* k_cache, int64_t cache_seq_stride,
+                             int32_t cache_capacity, int32_t batch, int32_t n_kv_heads,
+                             int32_t head_dim, int32_t block_size, const int32_t* prefix_len,
+                             const int32_t* first_token, int32_t max_tokens, void* summaries,
+                             int32_t* dev_err, hipStream_t stream) {
+  if (!k_cache || !prefix_len || !summaries) return TV_ERR_NULL;
+  if (head_dim != 64 && head_dim != 128) return TV_ERR_UNSUPPORTED;
+  if (batch < 0 || batch > 65535 || n_kv_heads < 1 || n_kv_heads > 65535 || cache_capacity < 0 ||
+      block_size < 1 || max_tokens < 0)
+    return TV_ERR_SHAPE;
+  const int64_t min_stride = (int64_t)n_kv_heads * cache_capacity * head_dim;
+  if (cache_seq_stride == 0) cache_seq_stride = min_stride;
+  if (cache_seq_stride < min_stride || cache_seq_stride % 8) return TV_ERR_SHAPE;
+  if (!aligned(k_cache, 16) || !aligned(summaries, 16)) return TV_ERR_UNSUPPORTED;
+  if (batch == 0 || cache_capacity == 0) return TV_OK;
+  return launch_status(tv::launch_summaries(k_cache, cache_seq_stride, cache_capacity, batch,
+                                            n_kv_heads, head_dim, block_size, prefix_len,
+                                            first_token, max_tokens, summaries, dev_err, stream));
+}
+
+size_t tv_select_blocks_workspace_size(const tv_select_desc* desc) {
+  if (check_select_desc(desc) != TV_OK) return 0;
+  const int cus = cu_count_for_current_device();
+  if (cus <= 0) return 0;
+  const tv::SelectPlan p = tv::plan_select(*desc, cus);
+  return p.ws_part_bytes + p.ws_keys_bytes;
+}
+
+tv_status tv_select_blocks(const tv_select_desc* desc, const void* q, const void* summaries,
+                           const int32_t* prefix_len, int32_t* block_idx, int32_t* n_blocks,
+                           float* scores, void* workspace, size_t workspace_bytes,
+                           int32_t* dev_err, hipStream_t stream) {
+  const tv_status st = check_select_desc(desc);
+  if (st != TV_OK) return st;
+  if (!q || !summaries || !prefix_len || !block_idx || !n_blocks || !workspace)
+    return TV_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(summaries, 16) || !aligned(scores, 4) || !aligned(block_idx, 4) ||
+      !aligned(n_blocks, 4))
+    return TV_ERR_UNSUPPORTED;
+  if (desc->batch == 0) return TV_OK;
+  const int cus = cu_count_for_current_device();
+  if (cus <= 0) return TV_ERR_DEVICE;
+  const tv::SelectPlan plan = tv::plan_select(*desc, cus);
+  if (!aligned(workspace, 256) || workspace_bytes < plan.ws_part_bytes + plan.ws_keys_bytes)
+    return TV_ERR_WORKSPACE;
+  return launch_status(tv::launch_select(*desc, plan, q, summaries, prefix_len, block_idx,
+                                         n_blocks, scores, workspace, dev_err, stream));
 }
 
 const char* tv_status_string(tv_status status) {

@@ -60,6 +60,25 @@ hipError_t launch_commit(const void* k_tree, const void* v_tree, const int32_t* 
                          int64_t seq_stride, int cap, int batch, int n, int hkv, int d,
                          int32_t* dev_err, hipStream_t stream);
 
+struct SelectPlan {
+  int nb_cap;        // summary records per (sequence, kv head): ceil(capacity / block_size)
+  int nb_max;        // blocks that can hold prefix tokens: ceil(min(max_prefix, cap) / bs)
+  int chunk;         // blocks per scoring workgroup (multiple of 16)
+  int chunks;        // scoring workgroups per (sequence, kv head)
+  size_t ws_part_bytes, ws_keys_bytes;
+};
+
+SelectPlan plan_select(const tv_select_desc& d, int cu_count);
+
+hipError_t launch_summaries(const void* k_cache, int64_t seq_stride, int cap, int batch, int hkv,
+                            int d, int bs, const int32_t* prefix_len, const int32_t* first_token,
+                            int max_tokens, void* summaries, int32_t* dev_err, hipStream_t stream);
+
+hipError_t launch_select(const tv_select_desc& d, const SelectPlan& plan, const void* q,
+                         const void* summaries, const int32_t* prefix_len, int32_t* block_idx,
+                         int32_t* n_blocks, float* scores, void* workspace, int32_t* dev_err,
+                         hipStream_t stream);
+
 // ---------------------------------------------------------------------------
 // small device helpers
 // ---------------------------------------------------------------------------
