@@ -59,6 +59,10 @@ def parse():
     ap.add_argument("--workload", default="8b_layer",
                     choices=["tiny", "8b_layer", "specblock_tree", "batched", "long_context"])
     ap.add_argument("--partial", action="store_true", help="partial-KV mode (long_context only)")
+    ap.add_argument("--specpv", action="store_true",
+                    help="long_context only: partial KV chosen each step by SpecPV block "
+                         "selection (16-token blocks, 2 sink + 246 retrieved + 8 window blocks), "
+                         "with the block summaries updated after the commit")
     ap.add_argument("--warm", action="store_true", help="no input rotation (cache-warm)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -107,6 +111,15 @@ class InputSet:
         self.mask = torch.empty((b, n, (n + 31) // 32), dtype=torch.int32, device=dev)
         self.out = torch.empty_like(self.q)
         self.new_prefix = torch.empty_like(self.prefix_len)
+        self.summ = self.sel_idx = self.sel_n = None
+
+    def add_selection(self, binding, torch, bs, max_blocks):
+        """Block summaries of the whole prefix (built here, untimed: they are
+        kept from one step to the next) and the selected-list buffers."""
+        b = self.prefix_len.shape[0]
+        self.summ = binding.block_summaries(self.k_cache, self.prefix_len, block_size=bs)
+        self.sel_idx = torch.empty((b, max_blocks), dtype=torch.int32, device=self.q.device)
+        self.sel_n = torch.empty((b,), dtype=torch.int32, device=self.q.device)
 
     def nbytes(self):
         import torch
@@ -117,12 +130,21 @@ class InputSet:
 class StepRunner:
     """The four library calls of one verify step, on torch's current stream."""
 
-    def __init__(self, wl, partial, warm, num_splits, dev):
+    def __init__(self, wl, partial, warm, num_splits, dev, specpv=False):
         import numpy as np
         import torch
 
         from tree_verification_attention_tv_amd import binding
+        from tree_verification_attention_tv_amd import workloads as W
 
+        self.specpv = specpv
+        if specpv:
+            partial = True
+            wl = wl.without_blocks()
+            wl.block_size = W.SPECPV_BLOCK_SIZE
+            self.sel = dict(n_sink=W.SPECPV_SINK_BLOCKS, n_window=W.SPECPV_WINDOW_BLOCKS,
+                            top_k=W.SPECPV_TOP_K)
+            self.max_blocks = sum(self.sel.values())
         self.wl, self.partial, self.dev = wl, partial, dev
         self.binding = binding
         first = InputSet(wl, dev, torch, np)
@@ -131,13 +153,22 @@ class StepRunner:
         self.sets = [first] + [InputSet(wl, dev, torch, np) for _ in range(self.rot - 1)]
         for i, st in enumerate(self.sets):
             st.gidx = i
+            if specpv:
+                st.add_selection(binding, torch, wl.block_size, self.max_blocks)
         self.graphs = []
         self.b, self.n = wl.parents.shape
         self.num_splits = num_splits
-        self.desc = binding.attn_desc(first.q, first.k_cache, max_prefix_len=wl.max_prefix_len,
-                                      block_size=wl.block_size if partial else 0,
-                                      max_blocks=wl.max_blocks if partial else 0,
-                                      num_splits=num_splits)
+        self.desc = binding.attn_desc(
+            first.q, first.k_cache, max_prefix_len=wl.max_prefix_len,
+            block_size=wl.block_size if partial else 0,
+            max_blocks=(self.max_blocks if specpv else wl.max_blocks) if partial else 0,
+            num_splits=num_splits)
+        if specpv:
+            self.sel_desc = binding.select_desc(
+                first.q, first.summ, cache_capacity=wl.capacity,
+                max_prefix_len=wl.max_prefix_len, block_size=wl.block_size, **self.sel)
+            self.ws_sel = torch.empty(binding.select_workspace_size(self.sel_desc),
+                                      dtype=torch.uint8, device=dev)
         self.ws_attn = torch.empty(binding.attention_workspace_size(self.desc), dtype=torch.uint8,
                                    device=dev)
         self.ws_acc = torch.empty(binding.accept_workspace_size(self.b, self.n, wl.vocab),
@@ -157,12 +188,30 @@ class StepRunner:
         if st:
             raise bd.TVError("tv_build_tree_mask", st)
 
+    def k_select(self, s):
+        self.binding.select_blocks(
+            s.q, s.summ, s.prefix_len, cache_capacity=self.wl.capacity,
+            max_prefix_len=self.wl.max_prefix_len, block_size=self.wl.block_size,
+            outputs=(s.sel_idx, s.sel_n), workspace=self.ws_sel, dev_err=self.err, **self.sel)
+
+    def k_summ_update(self, s):
+        # the committed rows [prefix_len, new_prefix) enter the summaries
+        self.binding.block_summaries(s.k_cache, s.new_prefix, block_size=self.wl.block_size,
+                                     first_token=s.prefix_len, max_tokens=self.n,
+                                     summaries=s.summ, dev_err=self.err)
+
+    def k_summ_full(self, s):
+        self.binding.block_summaries(s.k_cache, s.prefix_len, block_size=self.wl.block_size,
+                                     max_tokens=self.wl.max_prefix_len, summaries=s.summ,
+                                     dev_err=self.err)
+
     def k_attn(self, s):
         wl, p = self.wl, self.partial
+        bidx, nblk = (s.sel_idx, s.sel_n) if self.specpv else (s.block_idx, s.n_blocks)
         self.binding.tree_attention(
             s.q, s.k_cache, s.v_cache, s.k_tree, s.v_tree, s.prefix_len, s.mask,
-            max_prefix_len=wl.max_prefix_len, block_idx=s.block_idx if p else None,
-            n_blocks=s.n_blocks if p else None, block_size=wl.block_size if p else 0,
+            max_prefix_len=wl.max_prefix_len, block_idx=bidx if p else None,
+            n_blocks=nblk if p else None, block_size=wl.block_size if p else 0,
             num_splits=self.num_splits, out=s.out, workspace=self.ws_attn, dev_err=self.err)
 
     def k_accept(self, s):
@@ -175,10 +224,14 @@ class StepRunner:
                                dev_err=self.err)
 
     def step(self, s):
+        if self.specpv:
+            self.k_select(s)
         self.k_mask(s)
         self.k_attn(s)
         self.k_accept(s)
         self.k_commit(s)
+        if self.specpv:
+            self.k_summ_update(s)
 
     def capture(self):
         """One HIP graph per input set holding that set's whole step (the
@@ -215,6 +268,20 @@ class StepRunner:
             print(f"device error bits {int(self.err.item())}", file=sys.stderr)
             sys.exit(1)
 
+    def selection_bytes(self):
+        """Algorithmic bytes of one selection call (summary records of every
+        block of the prefix, the queries, per-KV-head partial scores written
+        and read back, the list) and of one full summary build (the prefix
+        keys read once, the records written)."""
+        wl = self.wl
+        b, n = self.b, self.n
+        hq, hkv, d, bs = wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.block_size
+        nv = [(int(p) + bs - 1) // bs for p in wl.prefix_len]
+        rec = hkv * 2 * d * 2
+        sel = sum(nv) * rec + b * n * hq * d * 2 + 2 * sum(nv) * hkv * 4 + b * self.max_blocks * 4
+        full = sum(int(p) for p in wl.prefix_len) * hkv * d * 2 + sum(nv) * rec
+        return sel, full, nv if b > 1 else nv[0]
+
     def bytes(self):
         """Algorithmic bytes: visible prefix tokens, KV bytes, bytes of the
         attention call (KV, Q, O, mask) and of the acceptance (logits)."""
@@ -223,9 +290,14 @@ class StepRunner:
         hq, hkv, d = wl.n_q_heads, wl.n_kv_heads, wl.head_dim
         if self.partial:
             prefix_tokens = []
+            if self.specpv:
+                st = self.sets[0]
+                lists = [st.sel_idx[s, :int(st.sel_n[s])].cpu().numpy() for s in range(b)]
+            else:
+                lists = [wl.block_idx[s, :int(wl.n_blocks[s])] for s in range(b)]
             for s in range(b):
                 vis = 0
-                for x in wl.block_idx[s, :int(wl.n_blocks[s])]:
+                for x in lists[s]:
                     lo = int(x) * wl.block_size
                     vis += max(0, min(wl.block_size, int(wl.prefix_len[s]) - lo))
                 prefix_tokens.append(vis)
@@ -237,11 +309,11 @@ class StepRunner:
         return prefix_tokens, kv, kv + qo + mask, wl.logits.nbytes
 
 
-def measure(wl, partial, steps, warmup, warm, num_splits, dev, graph=True):
+def measure(wl, partial, steps, warmup, warm, num_splits, dev, graph=True, specpv=False):
     """Returns (runner, step_us, wall_us, eager_step_us, calls).  step_us is
     the graph-replayed step when `graph`, else the eager one."""
     import torch
-    r = StepRunner(wl, partial, warm, num_splits, dev)
+    r = StepRunner(wl, partial, warm, num_splits, dev, specpv=specpv)
     for k in range(warmup):
         r.step(r.sets[k % r.rot])
     torch.cuda.synchronize()
@@ -260,6 +332,10 @@ def measure(wl, partial, steps, warmup, warm, num_splits, dev, graph=True):
     iters = max(steps, 50)
     calls = {"mask": r.timed(r.k_mask, iters), "attention": r.timed(r.k_attn, iters),
              "accept": r.timed(r.k_accept, iters), "commit": r.timed(r.k_commit, iters)}
+    if specpv:
+        calls["select"] = r.timed(r.k_select, iters)
+        calls["summaries_update"] = r.timed(r.k_summ_update, iters)
+        calls["summaries_full"] = r.timed(r.k_summ_full, max(iters // 5, 10))
     r.check_errors()
     return r, step_us, wall_us, eager_us, calls
 
@@ -283,6 +359,39 @@ def secondary_line(name, partial, steps, dev):
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "prefix_tokens": prefix_tokens,
         "num_splits": r.binding.attention_num_splits(r.desc),
+        "cache_rotation": r.rot,
+        "call_us": {k: round(v, 3) for k, v in calls.items()},
+    }
+    del r
+    torch.cuda.empty_cache()
+    return out
+
+
+def specpv_line(steps, dev):
+    """The long-context step with SpecPV selection: select -> mask -> partial
+    attention over the selected blocks -> accept -> commit -> summary update."""
+    import torch
+
+    from tree_verification_attention_tv_amd import workloads as W
+    wl = W.make_workload("long_context")
+    r, step_us, _, eager_us, calls = measure(wl, True, steps, 5, False, 0, dev, specpv=True)
+    prefix_tokens, kv, attn_bytes, _ = r.bytes()
+    sel_bytes, sum_bytes, nv = r.selection_bytes()
+    out = {
+        "mode": "specpv_select",
+        "step_us": round(step_us, 3),
+        "eager_step_us": round(eager_us, 3),
+        "attention_us": round(calls["attention"], 3),
+        "prefix_tokens": prefix_tokens,
+        "blocks": nv,
+        "select_bytes": sel_bytes,
+        "select_gbps": round(sel_bytes / (calls["select"] * 1e-6) / 1e9, 1),
+        "select_hbm_frac": round(sel_bytes / (calls["select"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "summaries_full_bytes": sum_bytes,
+        "summaries_full_gbps": round(sum_bytes / (calls["summaries_full"] * 1e-6) / 1e9, 1),
+        "summaries_full_hbm_frac": round(
+            sum_bytes / (calls["summaries_full"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "attention_gbps": round(attn_bytes / (calls["attention"] * 1e-6) / 1e9, 1),
         "cache_rotation": r.rot,
         "call_us": {k: round(v, 3) for k, v in calls.items()},
     }
@@ -342,10 +451,11 @@ def main():
         return
 
     wl = W.make_workload(args.workload)
-    partial = args.partial and wl.block_idx is not None
+    specpv = args.specpv and args.workload == "long_context"
+    partial = specpv or (args.partial and wl.block_idx is not None)
     r, step_us, wall_us, eager_us, calls = measure(wl, partial, args.steps, args.warmup,
                                                    args.warm, args.num_splits, dev,
-                                                   graph=not args.no_graph)
+                                                   graph=not args.no_graph, specpv=specpv)
     prefix_tokens, kv_bytes, attn_bytes, logit_bytes = r.bytes()
     b, n = r.b, r.n
     dominant = max(("attention", "accept"), key=lambda c: calls[c])
@@ -372,7 +482,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded; no dataset or weights)",
         "config": {
-            "workload": args.workload + ("_partial" if partial else ""),
+            "workload": args.workload + ("_specpv" if specpv else "_partial" if partial else ""),
             "batch": b, "n_nodes": n, "n_q_heads": wl.n_q_heads, "n_kv_heads": wl.n_kv_heads,
             "head_dim": wl.head_dim,
             "prefix_len": prefix_tokens if b <= 4 else [min(prefix_tokens), max(prefix_tokens)],
@@ -404,8 +514,9 @@ def main():
         result["secondary"] = {
             "long_context_full": secondary_line("long_context", False, 40, dev),
             "long_context_partial": secondary_line("long_context", True, 100, dev),
+            "long_context_specpv": specpv_line(100, dev),
         }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not specpv:
         result["cpu_baseline"] = cpu_baseline(wl, partial, first, acc_out, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 

@@ -290,7 +290,9 @@ tv_status tv_block_summaries(const void* k_cache, int64_t cache_seq_stride,
  *   n_blocks int32 [batch]; scores fp32 [batch][ceil(capacity / block_size)]
  *   or NULL (entries j >= nv are not written).
  * Supported: head_dim 64 or 128; TV_REDUCE_MAX needs n_q_heads / n_kv_heads
- *   <= TV_MAX_SELECT_GROUP; max_blocks >= n_sink_blocks + n_window_blocks + top_k.
+ *   <= TV_MAX_SELECT_GROUP; max_blocks >= n_sink_blocks + n_window_blocks + top_k;
+ *   at most TV_MAX_SELECT_BLOCKS blocks in min(capacity, max_prefix_len)
+ *   (TV_ERR_UNSUPPORTED, and a workspace size of 0, beyond).
  * Fallback: prefix_len outside [0, min(capacity, max_prefix_len)] is clamped
  *   to that range (TV_DERR_BAD_PREFIX).  NaN or infinite inputs give an
  *   unspecified (but valid, ascending) list.
@@ -298,6 +300,7 @@ tv_status tv_block_summaries(const void* k_cache, int64_t cache_seq_stride,
  */
 enum { TV_REDUCE_MEAN = 0, TV_REDUCE_MAX = 1, TV_REDUCE_LAST = 2 };
 #define TV_MAX_SELECT_GROUP 64
+#define TV_MAX_SELECT_BLOCKS 32768
 
 typedef struct {
   int32_t batch, n_nodes, n_q_heads, n_kv_heads, head_dim;

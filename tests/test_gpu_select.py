@@ -291,6 +291,43 @@ def test_selected_list_drives_partial_attention():
     check_attention_close(out, ref, "attention over the selected blocks")
 
 
+@pytest.mark.parametrize("reduction", ["mean", "max"])
+@pytest.mark.parametrize("plen,bs", [(100_000, 16), (131_072, 4)])
+def test_many_blocks_per_sequence(plen, bs, reduction):
+    # 6250 and 32768 blocks: 16 and 32 blocks per selection thread
+    _say(f"[select] {plen} tokens, block {bs}, {reduction}")
+    wl = W.make_select_case(71, batch=1, n_nodes=9, hq=8, hkv=2, d=64, prefix_lens=[plen],
+                            block_size=bs, n_planted=5)
+    dw = DevWorkload(wl)
+    summ, _ = summaries_gpu(dw, bs)
+    bidx, nblk, sc, err = run_select(dw, summ, bs, 3, 9, 333, reduction)
+    assert err == 0
+    nv = (plen + bs - 1) // bs
+    want = oracle.select_blocks(sc[0], nv, 3, 9, 333)
+    assert np.array_equal(bidx[0, :nblk[0]], want)
+    assert set(wl.block_idx[0, :wl.n_blocks[0]].tolist()) <= set(want.tolist())
+    rng = np.random.default_rng(3)
+    sample = sorted(set(rng.choice(nv, 48, replace=False).tolist()) | {0, nv - 1})
+    kmax, kmin, nv_o = check_summaries(summ, wl, bs, blocks=sample)
+    s64 = oracle.block_scores(wl.q, kmax, kmin, nv_o, reduction, blocks=sample)
+    mag = oracle.block_scores(wl.q, kmax, kmin, nv_o, reduction, blocks=sample, magnitude=True)
+    assert np.all(np.abs(sc[0, sample] - s64[0, sample]) <= score_tol(wl, mag)[0, sample])
+
+
+def test_too_many_blocks_is_refused():
+    wl = W.make_select_case(72, batch=1, n_nodes=2, hq=2, hkv=1, d=64, prefix_lens=[40],
+                            block_size=1)
+    dw = DevWorkload(wl)
+    summ = torch.empty(binding.summaries_shape(dw.k_cache, 1), dtype=torch.bfloat16,
+                       device="cuda")
+    d = binding.select_desc(dw.q, summ, cache_capacity=binding.MAX_SELECT_BLOCKS + 1,
+                            max_prefix_len=binding.MAX_SELECT_BLOCKS + 1, block_size=1,
+                            n_sink=1, n_window=1, top_k=1)
+    assert binding.select_workspace_size(d) == 0
+    d.max_prefix_len = binding.MAX_SELECT_BLOCKS
+    assert binding.select_workspace_size(d) > 0
+
+
 # ---------------------------------------------------------------------------
 # the 60K-token long-context shape at the pages' settings, sampled
 # ---------------------------------------------------------------------------

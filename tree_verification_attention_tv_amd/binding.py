@@ -66,6 +66,7 @@ class SelectDesc(ctypes.Structure):
 REDUCE_MEAN, REDUCE_MAX, REDUCE_LAST = 0, 1, 2
 REDUCTIONS = {"mean": REDUCE_MEAN, "max": REDUCE_MAX, "last": REDUCE_LAST}
 MAX_SELECT_GROUP = 64
+MAX_SELECT_BLOCKS = 32768
 
 
 def library_path() -> str:

@@ -206,7 +206,7 @@ size_t tv_select_blocks_workspace_size(const tv_select_desc* desc) {
   const int cus = cu_count_for_current_device();
   if (cus <= 0) return 0;
   const tv::SelectPlan p = tv::plan_select(*desc, cus);
-  return p.ws_part_bytes + p.ws_keys_bytes;
+  return p.kpt ? p.ws_part_bytes : 0;
 }
 
 tv_status tv_select_blocks(const tv_select_desc* desc, const void* q, const void* summaries,
@@ -224,8 +224,8 @@ tv_status tv_select_blocks(const tv_select_desc* desc, const void* q, const void
   const int cus = cu_count_for_current_device();
   if (cus <= 0) return TV_ERR_DEVICE;
   const tv::SelectPlan plan = tv::plan_select(*desc, cus);
-  if (!aligned(workspace, 256) || workspace_bytes < plan.ws_part_bytes + plan.ws_keys_bytes)
-    return TV_ERR_WORKSPACE;
+  if (!plan.kpt) return TV_ERR_UNSUPPORTED;
+  if (!aligned(workspace, 256) || workspace_bytes < plan.ws_part_bytes) return TV_ERR_WORKSPACE;
   return launch_status(tv::launch_select(*desc, plan, q, summaries, prefix_len, block_idx,
                                          n_blocks, scores, workspace, dev_err, stream));
 }

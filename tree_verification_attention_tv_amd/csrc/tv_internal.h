@@ -65,7 +65,9 @@ struct SelectPlan {
   int nb_max;        // blocks that can hold prefix tokens: ceil(min(max_prefix, cap) / bs)
   int chunk;         // blocks per scoring workgroup (multiple of 16)
   int chunks;        // scoring workgroups per (sequence, kv head)
-  size_t ws_part_bytes, ws_keys_bytes;
+  int part_stride;   // floats per (sequence, kv head) row of partial scores (multiple of 4)
+  int kpt;           // blocks per selection thread (4, 16 or 32); 0: too many blocks
+  size_t ws_part_bytes;
 };
 
 SelectPlan plan_select(const tv_select_desc& d, int cu_count);

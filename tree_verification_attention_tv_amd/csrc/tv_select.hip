@@ -18,10 +18,12 @@
 //        products with fp32 accumulation (score_max_kernel); the max over a
 //        head's nodes is taken in registers and across lanes.
 //    Both write per-KV-head partial scores; the selection sums them.
-//  * select_kernel: one workgroup per sequence sums the partial scores in KV
-//    head order, keeps the sinks and the window and picks the top-k of the
-//    rest by a 3-pass radix select on order-mapped fp32 keys (11/11/10 bits,
-//    LDS histograms), equal keys taken in ascending block order; the list is
+//  * select_kernel: one workgroup per sequence; thread t owns KPT consecutive
+//    blocks and keeps their keys (order-mapped fp32 scores, the KV heads'
+//    partial scores summed in head order) in registers.  The sinks and the
+//    window are kept; the top-k of the rest come from a radix select over
+//    the bits in which the candidates' keys differ (11-bit digits, LDS
+//    histograms), equal keys taken in ascending block order; the list is
 //    written ascending with workgroup prefix sums.
 #include "tv_internal.h"
 
@@ -34,7 +36,6 @@ constexpr int kScoreWaves = kScoreThreads / kWave;
 constexpr int kSelThreads = 1024;   // selection: one workgroup per sequence
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kMaxRowTilesPerWave = 2;
-constexpr int kSelItems = 4;        // consecutive blocks per thread in the output pass
 
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 
@@ -146,8 +147,8 @@ struct ScoreArgs {
   const uint16_t* q;       // [B][N][Hq][D]
   const uint4* summ;       // [B][Hkv][nb_cap][2][D] bf16
   const int32_t* prefix_len;
-  float* part;             // [B][Hkv][nb_cap]
-  int n, hq, hkv, group, bs, nb_cap, prefix_limit, chunk;
+  float* part;             // [B][Hkv][part_stride]
+  int n, hq, hkv, group, bs, nb_cap, part_stride, prefix_limit, chunk;
   int last_only;           // linear kernel: fold node n-1 only
 };
 
@@ -157,7 +158,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_linear_kernel(ScoreArgs a
   constexpr int SLOTS = kScoreThreads / C;  // query rows folded in parallel
   constexpr int L = 2 * D / 8;              // lanes per block record
   constexpr int BPL = kWave / L;            // blocks per wave-wide load
-  constexpr int U = 8;                      // loads in flight per lane
+  constexpr int U = 8;                      // record loads in flight per lane
+  constexpr int QU = 8;                     // query-row loads in flight per thread
   __shared__ float s_part[SLOTS][2 * D];
   __shared__ float s_qs[2 * D];
   const int b = blockIdx.z, g = blockIdx.y, t = threadIdx.x;
@@ -166,6 +168,23 @@ __global__ __launch_bounds__(kScoreThreads) void score_linear_kernel(ScoreArgs a
   const int j_begin = blockIdx.x * a.chunk;
   if (j_begin >= nv) return;  // uniform over the workgroup
   const int j_end = min(j_begin + a.chunk, nv);
+  const int lane = t % kWave, wave = t / kWave;
+  const int sub = lane / L, li = lane % L;
+  const uint4* sg = a.summ + ((int64_t)b * a.hkv + g) * a.nb_cap * L;
+  float* part = a.part + ((int64_t)b * a.hkv + g) * a.part_stride;
+
+  // The first batch of block records does not depend on the queries: its
+  // loads are in flight while the queries are folded.
+  uint4 v[U];
+  int jb = j_begin + wave * BPL * U;
+  auto load_batch = [&]() {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = jb + u * BPL + sub;
+      if (j < j_end) v[u] = sg[(int64_t)j * L + li];
+    }
+  };
+  load_batch();
 
   // 1. [sum q+ | sum q-] over the folded rows of this KV group, fp32
   {
@@ -176,17 +195,29 @@ __global__ __launch_bounds__(kScoreThreads) void score_linear_kernel(ScoreArgs a
 #pragma unroll
     for (int e = 0; e < 8; ++e) pos[e] = neg[e] = 0.f;
     const uint4* q4 = reinterpret_cast<const uint4*>(a.q);
-    for (int r = slot; r < nrows; r += SLOTS) {
-      const int i = i0 + r / a.group, h = g * a.group + r % a.group;
-      const uint4 v = q4[(((int64_t)b * a.n + i) * a.hq + h) * C + c];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (int r0 = slot; r0 < nrows; r0 += QU * SLOTS) {
+      uint4 qv[QU];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x0 = bf16_lo(w[e]), x1 = bf16_hi(w[e]);
-        pos[2 * e] += fmaxf(x0, 0.f);
-        neg[2 * e] += fminf(x0, 0.f);
-        pos[2 * e + 1] += fmaxf(x1, 0.f);
-        neg[2 * e + 1] += fminf(x1, 0.f);
+      for (int u = 0; u < QU; ++u) {
+        const int r = r0 + u * SLOTS;
+        if (r < nrows) {
+          const int i = i0 + r / a.group, h = g * a.group + r % a.group;
+          qv[u] = q4[(((int64_t)b * a.n + i) * a.hq + h) * C + c];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < QU; ++u) {
+        if (r0 + u * SLOTS < nrows) {
+          const uint32_t w[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x0 = bf16_lo(w[e]), x1 = bf16_hi(w[e]);
+            pos[2 * e] += fmaxf(x0, 0.f);
+            neg[2 * e] += fminf(x0, 0.f);
+            pos[2 * e + 1] += fmaxf(x1, 0.f);
+            neg[2 * e + 1] += fminf(x1, 0.f);
+          }
+        }
       }
     }
 #pragma unroll
@@ -205,20 +236,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_linear_kernel(ScoreArgs a
   }
 
   // 2. one dot product of length 2D per block
-  const int lane = t % kWave, wave = t / kWave;
-  const int sub = lane / L, li = lane % L;
   float qv[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) qv[e] = s_qs[li * 8 + e];
-  const uint4* sg = a.summ + ((int64_t)b * a.hkv + g) * a.nb_cap * L;
-  float* part = a.part + ((int64_t)b * a.hkv + g) * a.nb_cap;
-  for (int jb = j_begin + wave * BPL * U; jb < j_end; jb += kScoreWaves * BPL * U) {
-    uint4 v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = min(jb + u * BPL + sub, j_end - 1);  // clamped: always a valid record
-      v[u] = sg[(int64_t)j * L + li];
-    }
+  while (true) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
@@ -233,6 +254,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_linear_kernel(ScoreArgs a
       const int j = jb + u * BPL + sub;
       if (li == 0 && j < j_end) part[j] = acc;
     }
+    jb += kScoreWaves * BPL * U;
+    if (jb >= j_end) break;  // uniform over the wave
+    load_batch();
   }
 }
 
@@ -294,7 +318,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_max_kernel(ScoreArgs a) {
   if (one_pass) load_a(0);
 
   const uint4* sg = a.summ + ((int64_t)b * a.hkv + g) * a.nb_cap * (2 * C);
-  float* part = a.part + ((int64_t)b * a.hkv + g) * a.nb_cap;
+  float* part = a.part + ((int64_t)b * a.hkv + g) * a.part_stride;
   int buf = 0;
   for (int j0 = j_begin; j0 < j_end; j0 += 16, buf ^= 1) {
     // B operand: lane holds block j0 + col, k = ks*32 + 8*quad .. +7 of its record
@@ -341,14 +365,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_max_kernel(ScoreArgs a) {
 // ---- selection ---------------------------------------------------------------------
 
 struct SelectArgs {
-  const float* part;       // [B][Hkv][nb_cap]
-  uint32_t* keys;          // [B][nb_cap] workspace
+  const float* part;       // [B][Hkv][part_stride]
   float* scores;           // [B][nb_cap] or nullptr
   const int32_t* prefix_len;
   int32_t* block_idx;      // [B][max_blocks]
   int32_t* n_blocks;       // [B]
   int32_t* dev_err;
-  int hkv, nb_cap, bs, prefix_limit, cap, max_prefix;
+  int hkv, nb_cap, part_stride, bs, prefix_limit, cap, max_prefix;
   int n_sink, n_window, top_k, max_blocks;
   float count;             // divisor: query rows averaged
 };
@@ -381,48 +404,102 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* s_wsum
   return x + off;
 }
 
+// KPT consecutive blocks per thread (thread t owns blocks t*KPT ..), keys in
+// registers.  KPT is a multiple of 4.
+template <int KPT>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   __shared__ uint32_t s_hist[2048];
-  __shared__ uint32_t s_wsum[kSelWaves];
+  __shared__ uint32_t s_wsum[kSelWaves], s_wmin[kSelWaves], s_wmax[kSelWaves];
   __shared__ uint32_t s_bin, s_above;
   const int b = blockIdx.x, t = threadIdx.x;
+  const int lane = t % kWave, wave = t / kWave;
   const int p_raw = a.prefix_len[b];
   if (t == 0 && (p_raw < 0 || p_raw > a.cap || p_raw > a.max_prefix))
     raise_err(a.dev_err, TV_DERR_BAD_PREFIX);
   const int p = p_raw < 0 ? 0 : (p_raw > a.prefix_limit ? a.prefix_limit : p_raw);
   const int nv = (p + a.bs - 1) / a.bs;
-  uint32_t* keys = a.keys + (int64_t)b * a.nb_cap;
-
-  // 1. scores: partial scores summed in KV-head order, then averaged
-  for (int j = t; j < nv; j += kSelThreads) {
-    float s = 0.f;
-    for (int g = 0; g < a.hkv; ++g) s += a.part[((int64_t)b * a.hkv + g) * a.nb_cap + j];
-    s = s / a.count;
-    if (a.scores) a.scores[(int64_t)b * a.nb_cap + j] = s;
-    keys[j] = f32_key(s);
-  }
-  __syncthreads();
-
-  // 2. candidates [lo, hi): neither sink nor window
+  const int j0 = t * KPT;
   const int lo = min(a.n_sink, nv);
   const int hi = max(nv - a.n_window, lo);
+
+  // 1. scores: the KV heads' partial scores summed in head order, averaged
+  uint32_t key[KPT];
+#pragma unroll
+  for (int u0 = 0; u0 < KPT; u0 += 4) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    const bool any = j0 + u0 < nv;  // then j0+u0+3 < part_stride (a multiple of 4)
+    constexpr int GB = KPT <= 16 ? 16 : 4;  // heads loaded together (registers)
+    for (int g0 = 0; g0 < a.hkv; g0 += GB) {
+      float4 v[GB];
+#pragma unroll
+      for (int gg = 0; gg < GB; ++gg)
+        if (any && g0 + gg < a.hkv)
+          v[gg] = *reinterpret_cast<const float4*>(
+              a.part + ((int64_t)b * a.hkv + g0 + gg) * a.part_stride + j0 + u0);
+#pragma unroll
+      for (int gg = 0; gg < GB; ++gg)
+        if (any && g0 + gg < a.hkv) {
+          acc[0] += v[gg].x;
+          acc[1] += v[gg].y;
+          acc[2] += v[gg].z;
+          acc[3] += v[gg].w;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float s = acc[e] / a.count;
+      key[u0 + e] = f32_key(s);
+      if (a.scores && j0 + u0 + e < nv) a.scores[(int64_t)b * a.nb_cap + j0 + u0 + e] = s;
+    }
+  }
+
+  // 2. candidates [lo, hi): neither sink nor window
   const int ncand = hi - lo;
   const int k = min(a.top_k, ncand);
   const bool all_cand = k == ncand;
   const bool radix = k > 0 && !all_cand;
-  uint32_t want_val = 0, want_mask = 0, need = 0;
+  uint32_t want_val = 0, need = 0;
   if (radix) {
+    // leading bits shared by every candidate key need no pass
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int j = j0 + u;
+      if (j >= lo && j < hi) {
+        kmin = min(kmin, key[u]);
+        kmax = max(kmax, key[u]);
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      kmin = min(kmin, (uint32_t)__shfl_xor(kmin, off));
+      kmax = max(kmax, (uint32_t)__shfl_xor(kmax, off));
+    }
+    if (lane == 0) {
+      s_wmin[wave] = kmin;
+      s_wmax[wave] = kmax;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kSelWaves; ++i) {
+      kmin = min(kmin, s_wmin[i]);
+      kmax = max(kmax, s_wmax[i]);
+    }
+    const int cp = kmin == kmax ? 32 : __clz(kmin ^ kmax);
+    uint32_t want_mask = cp == 0 ? 0u : (cp == 32 ? 0xFFFFFFFFu : (0xFFFFFFFFu << (32 - cp)));
+    want_val = kmin & want_mask;
     uint32_t remaining = (uint32_t)k;
-    int shift = 32;
-    for (int pass = 0; pass < 3; ++pass) {
-      const int bits = pass < 2 ? 11 : 10;
+    for (int left = 32 - cp; left > 0;) {  // uniform over the workgroup
+      const int bits = left < 11 ? left : 11;
+      const int shift = left - bits;
       const int nbins = 1 << bits;
-      shift -= bits;
-      for (int i = t; i < 2048; i += kSelThreads) s_hist[i] = 0u;
+      for (int i = t; i < nbins; i += kSelThreads) s_hist[i] = 0u;
       __syncthreads();
-      for (int j = lo + t; j < hi; j += kSelThreads) {
-        const uint32_t key = keys[j];
-        if ((key & want_mask) == want_val) atomicAdd(&s_hist[(key >> shift) & (nbins - 1)], 1u);
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) {
+        const int j = j0 + u;
+        if (j >= lo && j < hi && (key[u] & want_mask) == want_val)
+          atomicAdd(&s_hist[(key[u] >> shift) & (nbins - 1)], 1u);
       }
       __syncthreads();
       // bins from the top: thread t covers bins hb and hb - 1
@@ -442,56 +519,49 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
       want_val |= s_bin << shift;
       want_mask |= (uint32_t)(nbins - 1) << shift;
       remaining -= s_above;
+      left = shift;
       __syncthreads();
     }
-    need = remaining;  // blocks with key == want_val still to take, lowest ids first
+    need = remaining;  // candidates with key == want_val still to take, lowest ids first
   }
 
   // 3. ascending output: sinks, window, keys above the threshold, and the
   //    first `need` candidates whose key equals it
-  int32_t* out = a.block_idx + (int64_t)b * a.max_blocks;
-  uint32_t out_base = 0, eq_base = 0;
-  for (int c0 = 0; c0 < nv; c0 += kSelThreads * kSelItems) {
-    bool in[kSelItems], cand[kSelItems], eq[kSelItems];
-    uint32_t key[kSelItems], neq = 0;
+  uint32_t neq = 0;
 #pragma unroll
-    for (int u = 0; u < kSelItems; ++u) {
-      const int j = c0 + t * kSelItems + u;
-      in[u] = j < nv;
-      cand[u] = in[u] && j >= lo && j < hi;
-      key[u] = (cand[u] && radix) ? keys[j] : 0u;
-      eq[u] = cand[u] && radix && key[u] == want_val;
-      neq += eq[u];
-    }
-    uint32_t tot_eq;
-    uint32_t eq_rank = eq_base + block_incl_scan(neq, s_wsum, tot_eq) - neq;
-    bool sel[kSelItems];
-    uint32_t nsel = 0;
-#pragma unroll
-    for (int u = 0; u < kSelItems; ++u) {
-      bool s = in[u] && (!cand[u] || all_cand);
-      if (cand[u] && radix) {
-        if (key[u] > want_val) s = true;
-        if (eq[u]) s = eq_rank++ < need;
-      }
-      sel[u] = s;
-      nsel += s;
-    }
-    uint32_t tot_sel;
-    uint32_t pos = out_base + block_incl_scan(nsel, s_wsum, tot_sel) - nsel;
-#pragma unroll
-    for (int u = 0; u < kSelItems; ++u)
-      if (sel[u]) {
-        if (pos < (uint32_t)a.max_blocks) out[pos] = c0 + t * kSelItems + u;
-        ++pos;
-      }
-    out_base += tot_sel;
-    eq_base += tot_eq;
+  for (int u = 0; u < KPT; ++u) {
+    const int j = j0 + u;
+    neq += (radix && j >= lo && j < hi && key[u] == want_val) ? 1u : 0u;
   }
-  for (int i = (int)out_base + t; i < a.max_blocks; i += kSelThreads) out[i] = -1;
-  if (t == 0) a.n_blocks[b] = (int32_t)min(out_base, (uint32_t)a.max_blocks);
+  uint32_t tot_eq;
+  uint32_t eq_rank = block_incl_scan(neq, s_wsum, tot_eq) - neq;
+  static_assert(KPT <= 64, "selection flags are kept in one 64-bit mask");
+  uint64_t sel = 0;
+  uint32_t nsel = 0;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const int j = j0 + u;
+    const bool cand = j >= lo && j < hi;
+    bool s = j < nv && (!cand || all_cand);
+    if (cand && radix) {
+      if (key[u] > want_val) s = true;
+      else if (key[u] == want_val) s = eq_rank++ < need;
+    }
+    sel |= (uint64_t)s << u;
+    nsel += s;
+  }
+  uint32_t tot_sel;
+  uint32_t pos = block_incl_scan(nsel, s_wsum, tot_sel) - nsel;
+  int32_t* out = a.block_idx + (int64_t)b * a.max_blocks;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u)
+    if ((sel >> u) & 1u) {
+      if (pos < (uint32_t)a.max_blocks) out[pos] = j0 + u;
+      ++pos;
+    }
+  for (int i = (int)tot_sel + t; i < a.max_blocks; i += kSelThreads) out[i] = -1;
+  if (t == 0) a.n_blocks[b] = (int32_t)min(tot_sel, (uint32_t)a.max_blocks);
 }
-
 }  // namespace
 
 SelectPlan plan_select(const tv_select_desc& d, int cu_count) {
@@ -499,18 +569,21 @@ SelectPlan plan_select(const tv_select_desc& d, int cu_count) {
   p.nb_cap = (d.cache_capacity + d.block_size - 1) / d.block_size;
   const int limit = d.max_prefix_len < d.cache_capacity ? d.max_prefix_len : d.cache_capacity;
   p.nb_max = (limit + d.block_size - 1) / d.block_size;
-  // chunk of blocks per scoring workgroup: about two workgroups per CU,
-  // never below 64 blocks (each workgroup also folds or loads the queries)
+  // blocks per thread of the selection workgroup (keys live in registers)
+  static_assert(32 * kSelThreads == TV_MAX_SELECT_BLOCKS, "selection capacity");
+  p.kpt = p.nb_max <= 4 * kSelThreads ? 4 : p.nb_max <= 16 * kSelThreads ? 16
+        : p.nb_max <= 32 * kSelThreads ? 32 : 0;
+  // chunk of blocks per scoring workgroup: about one workgroup per CU, never
+  // below 64 blocks (each workgroup also folds or loads the queries)
   const int64_t groups = (int64_t)d.batch * d.n_kv_heads;
-  const int64_t want = groups > 0 ? (2LL * cu_count + groups - 1) / groups : 1;
+  const int64_t want = groups > 0 ? (cu_count + groups - 1) / groups : 1;
   int chunk = (int)((p.nb_max + want - 1) / (want > 0 ? want : 1));
   chunk = chunk < 64 ? 64 : chunk;
   p.chunk = (chunk + 15) & ~15;
   p.chunks = p.nb_max > 0 ? (p.nb_max + p.chunk - 1) / p.chunk : 0;
-  const size_t part = (size_t)d.batch * d.n_kv_heads * p.nb_cap * sizeof(float);
-  const size_t keys = (size_t)d.batch * p.nb_cap * sizeof(uint32_t);
+  p.part_stride = (p.nb_cap + 3) & ~3;
+  const size_t part = (size_t)d.batch * d.n_kv_heads * p.part_stride * sizeof(float);
   p.ws_part_bytes = (part + 255) & ~(size_t)255;
-  p.ws_keys_bytes = (keys + 255) & ~(size_t)255;
   return p;
 }
 
@@ -541,9 +614,7 @@ hipError_t launch_select(const tv_select_desc& d, const SelectPlan& plan, const 
                          const void* summaries, const int32_t* prefix_len, int32_t* block_idx,
                          int32_t* n_blocks, float* scores, void* workspace, int32_t* dev_err,
                          hipStream_t stream) {
-  char* ws = static_cast<char*>(workspace);
-  float* part = reinterpret_cast<float*>(ws);
-  uint32_t* keys = reinterpret_cast<uint32_t*>(ws + plan.ws_part_bytes);
+  float* part = static_cast<float*>(workspace);
   const int limit = d.max_prefix_len < d.cache_capacity ? d.max_prefix_len : d.cache_capacity;
   const int group = d.n_q_heads / d.n_kv_heads;
   if (plan.chunks > 0) {
@@ -558,6 +629,7 @@ hipError_t launch_select(const tv_select_desc& d, const SelectPlan& plan, const 
     sa.group = group;
     sa.bs = d.block_size;
     sa.nb_cap = plan.nb_cap;
+    sa.part_stride = plan.part_stride;
     sa.prefix_limit = limit;
     sa.chunk = plan.chunk;
     sa.last_only = d.reduction == TV_REDUCE_LAST;
@@ -578,7 +650,6 @@ hipError_t launch_select(const tv_select_desc& d, const SelectPlan& plan, const 
   }
   SelectArgs a{};
   a.part = part;
-  a.keys = keys;
   a.scores = scores;
   a.prefix_len = prefix_len;
   a.block_idx = block_idx;
@@ -586,6 +657,7 @@ hipError_t launch_select(const tv_select_desc& d, const SelectPlan& plan, const 
   a.dev_err = dev_err;
   a.hkv = d.n_kv_heads;
   a.nb_cap = plan.nb_cap;
+  a.part_stride = plan.part_stride;
   a.bs = d.block_size;
   a.prefix_limit = limit;
   a.cap = d.cache_capacity;
@@ -596,7 +668,12 @@ hipError_t launch_select(const tv_select_desc& d, const SelectPlan& plan, const 
   a.max_blocks = d.max_blocks;
   a.count = d.reduction == TV_REDUCE_MEAN ? (float)d.n_nodes * (float)d.n_q_heads
                                           : (float)d.n_q_heads;
-  hipLaunchKernelGGL(select_kernel, dim3(d.batch), dim3(kSelThreads), 0, stream, a);
+  if (plan.kpt == 4)
+    hipLaunchKernelGGL(select_kernel<4>, dim3(d.batch), dim3(kSelThreads), 0, stream, a);
+  else if (plan.kpt == 16)
+    hipLaunchKernelGGL(select_kernel<16>, dim3(d.batch), dim3(kSelThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(select_kernel<32>, dim3(d.batch), dim3(kSelThreads), 0, stream, a);
   return hipGetLastError();
 }
 
