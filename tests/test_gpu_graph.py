@@ -87,3 +87,84 @@ def test_step_graph_replays_match_eager(name):
         torch.cuda.synchronize()
         for k, (got, want) in enumerate(zip(graphed.results(), ref)):
             assert torch.equal(got, want), f"replay {rep}: output {k} differs from the eager step"
+
+
+def test_specpv_step_graph_replays_match_eager():
+    """select -> mask -> partial attention over the selected blocks -> accept
+    -> commit -> summary update, captured once and replayed."""
+    print("[graph] SpecPV step capture and replay", flush=True)
+    bs, n_sink, n_window, top_k = 16, 2, 4, 20
+    wl = W.make_select_case(81, batch=2, n_nodes=24, hq=8, hkv=2, d=128,
+                            prefix_lens=[1500, 977], block_size=bs, n_planted=4)
+
+    class SpecStep(_Step):
+        def __init__(self):
+            super().__init__(wl)
+            dw = self.dw
+            # records past the prefix are never written: start them equal
+            self.summ = torch.zeros(binding.summaries_shape(dw.k_cache, bs),
+                                    dtype=torch.bfloat16, device="cuda")
+            binding.block_summaries(dw.k_cache, dw.prefix_len, block_size=bs,
+                                    summaries=self.summ)
+            self.sel = (torch.empty((2, n_sink + n_window + top_k), dtype=torch.int32,
+                                    device="cuda"),
+                        torch.empty((2,), dtype=torch.int32, device="cuda"))
+            self.ws_sel = torch.empty(binding.select_workspace_size(binding.select_desc(
+                dw.q, self.summ, cache_capacity=wl.capacity, max_prefix_len=wl.max_prefix_len,
+                block_size=bs, n_sink=n_sink, n_window=n_window, top_k=top_k)),
+                dtype=torch.uint8, device="cuda")
+            self.desc = binding.attn_desc(dw.q, dw.k_cache, max_prefix_len=wl.max_prefix_len,
+                                          block_size=bs, max_blocks=n_sink + n_window + top_k)
+            self.ws_attn = torch.empty(binding.attention_workspace_size(self.desc),
+                                       dtype=torch.uint8, device="cuda")
+
+        def run(self):
+            dw = self.dw
+            b, n = wl.parents.shape
+            binding.select_blocks(dw.q, self.summ, dw.prefix_len, cache_capacity=wl.capacity,
+                                  max_prefix_len=wl.max_prefix_len, block_size=bs,
+                                  n_sink=n_sink, n_window=n_window, top_k=top_k,
+                                  outputs=self.sel, workspace=self.ws_sel, dev_err=self.err)
+            st = binding.lib().tv_build_tree_mask(binding._ptr(dw.parents), b, n,
+                                                  binding._ptr(self.mask), None,
+                                                  binding._ptr(self.err),
+                                                  binding._stream(dw.q.device))
+            assert st == 0
+            binding.tree_attention(dw.q, dw.k_cache, dw.v_cache, dw.k_tree, dw.v_tree,
+                                   dw.prefix_len, self.mask, max_prefix_len=wl.max_prefix_len,
+                                   block_idx=self.sel[0], n_blocks=self.sel[1], block_size=bs,
+                                   out=self.out, workspace=self.ws_attn, dev_err=self.err)
+            binding.greedy_accept(dw.logits, dw.parents, dw.draft, workspace=self.ws_acc,
+                                  dev_err=self.err, outputs=self.acc)
+            binding.commit_kv(dw.k_tree, dw.v_tree, self.acc[2], self.acc[1], dw.prefix_len,
+                              dw.k_cache, dw.v_cache, new_prefix_len=self.new_prefix,
+                              dev_err=self.err)
+            binding.block_summaries(dw.k_cache, self.new_prefix, block_size=bs,
+                                    first_token=dw.prefix_len, max_tokens=n,
+                                    summaries=self.summ, dev_err=self.err)
+
+        def results(self):
+            return super().results() + [*self.sel, self.summ.view(torch.int16)]
+
+        def scramble(self):
+            super().scramble()
+            for t in self.sel:
+                t.fill_(-7)
+
+    eager, graphed = SpecStep(), SpecStep()
+    eager.run()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in eager.results()]
+    assert int(eager.err.item()) == 0
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        graphed.run()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        graphed.scramble()
+        eager.run()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, (got, want) in enumerate(zip(graphed.results(), ref)):
+            assert torch.equal(got, want), f"replay {rep}: output {k} differs from the eager step"

@@ -65,6 +65,47 @@ __device__ __forceinline__ float f32_unkey(uint32_t k) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// ---- cross-lane steps on DPP and the gfx950 row-swap permutes -------------------
+// DPP controls: row_ror:n = 0x120 + n, row_shr:n = 0x110 + n, row_bcast:15 =
+// 0x142, row_bcast:31 = 0x143.
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t old, uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, CTRL, ROW_MASK, 0xF, false);
+}
+
+// sum over the 16 lanes of each row, in every lane of the row
+__device__ __forceinline__ float row_sum16(float x) {
+  x += __uint_as_float(dpp_u<0x128>(0u, __float_as_uint(x)));
+  x += __uint_as_float(dpp_u<0x124>(0u, __float_as_uint(x)));
+  x += __uint_as_float(dpp_u<0x122>(0u, __float_as_uint(x)));
+  x += __uint_as_float(dpp_u<0x121>(0u, __float_as_uint(x)));
+  return x;
+}
+
+// sum over lane pairs of rows (0,1) and (2,3), in every lane of both rows
+__device__ __forceinline__ float row_pair_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+
+// min and max over the wave, in every lane
+__device__ __forceinline__ void wave_minmax(uint32_t& mn, uint32_t& mx) {
+#define TV_STEP(C)                                   \
+  mn = min(mn, dpp_u<C>(0xFFFFFFFFu, mn));           \
+  mx = max(mx, dpp_u<C>(0u, mx));
+  TV_STEP(0x128) TV_STEP(0x124) TV_STEP(0x122) TV_STEP(0x121)
+#undef TV_STEP
+  auto a = __builtin_amdgcn_permlane16_swap(mn, mn, false, false);
+  mn = min(a[0], a[1]);
+  a = __builtin_amdgcn_permlane16_swap(mx, mx, false, false);
+  mx = max(a[0], a[1]);
+  a = __builtin_amdgcn_permlane32_swap(mn, mn, false, false);
+  mn = min(a[0], a[1]);
+  a = __builtin_amdgcn_permlane32_swap(mx, mx, false, false);
+  mx = max(a[0], a[1]);
+}
+
 __device__ __forceinline__ int effective_prefix(const int32_t* prefix_len, int b, int limit) {
   const int p = prefix_len[b];
   return p < 0 ? 0 : (p > limit ? limit : p);
@@ -249,8 +290,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_linear_kernel(ScoreArgs a
         acc = fmaf(bf16_lo(w[e]), qv[2 * e], acc);
         acc = fmaf(bf16_hi(w[e]), qv[2 * e + 1], acc);
       }
-#pragma unroll
-      for (int off = 1; off < L; off <<= 1) acc += __shfl_xor(acc, off);
+      acc = row_sum16(acc);
+      if (L == 32) acc = row_pair_sum(acc);
       const int j = jb + u * BPL + sub;
       if (li == 0 && j < j_end) part[j] = acc;
     }
@@ -376,13 +417,15 @@ struct SelectArgs {
   float count;             // divisor: query rows averaged
 };
 
+// inclusive prefix sum over the wave's 64 lanes: row_shr steps within each
+// row of 16, then row_bcast:15 and row_bcast:31 carry row totals upward
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = threadIdx.x % kWave;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const uint32_t o = __shfl_up(v, off);
-    if (lane >= off) v += o;
-  }
+  v += dpp_u<0x111>(0u, v);
+  v += dpp_u<0x112>(0u, v);
+  v += dpp_u<0x114>(0u, v);
+  v += dpp_u<0x118>(0u, v);
+  v += dpp_u<0x142, 0xA>(0u, v);
+  v += dpp_u<0x143, 0xC>(0u, v);
   return v;
 }
 
@@ -470,11 +513,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
         kmax = max(kmax, key[u]);
       }
     }
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      kmin = min(kmin, (uint32_t)__shfl_xor(kmin, off));
-      kmax = max(kmax, (uint32_t)__shfl_xor(kmax, off));
-    }
+    wave_minmax(kmin, kmax);
     if (lane == 0) {
       s_wmin[wave] = kmin;
       s_wmax[wave] = kmax;
