@@ -400,6 +400,40 @@ def specpv_line(steps, dev):
     return out
 
 
+def rectify_line(steps, dev):
+    """SpecPV's rectifying full verification at the long-context shape: the
+    tree is 21 buffered tokens (one more than the 20-token buffer) as a
+    chain, the current root and the 60-node draft tree, verified with full
+    attention over the 60000-token prefix."""
+    import numpy as np
+    import torch
+
+    from tree_verification_attention_tv_amd import binding
+    from tree_verification_attention_tv_amd import workloads as W
+    base = W.make_workload("long_context")
+    rng = np.random.Generator(np.random.PCG64(2024))
+    chain = rng.integers(0, base.vocab, size=21)
+    par, _ = binding.specpv_rectify_tree(chain, int(base.draft_tokens[0, 0]), base.parents[0],
+                                         base.draft_tokens[0])
+    wl = W.long_context_with_tree(par, "long_context_rectify")
+    r, step_us, _, eager_us, calls = measure(wl, False, steps, 5, False, 0, dev)
+    _, kv, attn_bytes, _ = r.bytes()
+    out = {
+        "mode": "specpv_rectify",
+        "n_nodes": int(par.shape[0]),
+        "step_us": round(step_us, 3),
+        "eager_step_us": round(eager_us, 3),
+        "attention_us": round(calls["attention"], 3),
+        "kv_gbps": round(kv / (calls["attention"] * 1e-6) / 1e9, 1),
+        "hbm_frac": round(attn_bytes / (calls["attention"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "cache_rotation": r.rot,
+        "call_us": {k: round(v, 3) for k, v in calls.items()},
+    }
+    del r
+    torch.cuda.empty_cache()
+    return out
+
+
 def read_traffic():
     """HBM bytes per attention call from the committed counter summary, or
     None when it is missing or was taken on another kernel source."""
@@ -515,6 +549,7 @@ def main():
             "long_context_full": secondary_line("long_context", False, 40, dev),
             "long_context_partial": secondary_line("long_context", True, 100, dev),
             "long_context_specpv": specpv_line(100, dev),
+            "long_context_specpv_rectify": rectify_line(40, dev),
         }
     if not args.no_cpu_baseline and not specpv:
         result["cpu_baseline"] = cpu_baseline(wl, partial, first, acc_out, args.cpu_seconds)

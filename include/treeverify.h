@@ -16,6 +16,8 @@
  *   tv_block_summaries   per-block element-wise max/min keys (SpecPV retrieval)
  *   tv_select_blocks     score blocks against the tree's queries and pick the
  *                        sink + top-k + window list for partial attention
+ *   tv_specpv_*          host policy of the partial-verification buffer and
+ *                        the tree of a rectifying full verification
  *
  * Conventions shared by every call
  * --------------------------------
@@ -318,6 +320,43 @@ tv_status tv_select_blocks(const tv_select_desc* desc, const void* q, const void
                            const int32_t* prefix_len, int32_t* block_idx, int32_t* n_blocks,
                            float* scores, void* workspace, size_t workspace_bytes,
                            int32_t* dev_err, hipStream_t stream);
+
+/*
+ * SpecPV partial-verification buffer and rectification (host functions).
+ *
+ * Source: SpecPV Sec. 3.3 "Rectified with Full Verification": tokens
+ * accepted by partial verification are partially verified; when the partial
+ * cache's buffer overflows, a full verification re-checks them, prepended to
+ * the new candidates, over the full KV, and the partial cache is rebuilt.
+ * App. C sizes the buffer as one step's tokens plus 20; App. D: buffer 20.
+ *
+ * The buffer holds the step's candidates plus up to buffer_size partially
+ * verified tokens (the cache rows committed by partial steps since the last
+ * full verification).  These functions take HOST pointers, touch no device
+ * and enqueue nothing.
+ *
+ * tv_specpv_needs_rectification: 1 if the next step must be a rectifying full
+ *   verification (n_partial > buffer_size), 0 if it may be partial, -1 if a
+ *   count is negative.
+ *
+ * tv_specpv_rectify_tree: the tree a rectifying step verifies.  Node i <
+ *   n_buffer is buffered token i (oldest first; node 0, the last full
+ *   verification's bonus token, is the root), chained to node i-1; node
+ *   n_buffer is the current root (root_token, the last emitted token) under
+ *   node n_buffer-1; draft node j >= 1 becomes node n_buffer + j under node
+ *   n_buffer + parents[j].  parents_out and tokens_out have n_buffer + n_draft
+ *   entries.  The step then runs with full attention over the fully verified
+ *   prefix and commits at the fully verified length, replacing the partially
+ *   verified rows.
+ *   Errors: TV_ERR_NULL; TV_ERR_SHAPE if n_buffer < 1, n_draft < 1,
+ *   n_buffer + n_draft > TV_MAX_NODES, or the draft tree is not topologically
+ *   ordered with parents[0] == -1.
+ */
+int32_t tv_specpv_needs_rectification(int32_t n_partial, int32_t buffer_size);
+tv_status tv_specpv_rectify_tree(const int32_t* buffer_tokens, int32_t n_buffer,
+                                 int32_t root_token, const int32_t* parents,
+                                 const int32_t* draft_tokens, int32_t n_draft,
+                                 int32_t* parents_out, int32_t* tokens_out);
 
 /* human-readable name of a status code (static storage) */
 const char* tv_status_string(tv_status status);

@@ -164,3 +164,33 @@ def test_wrong_selection_rule_is_caught(monkeypatch, mut):
     caught = _fails(spins.test_p17_hand_worked_selection) or any(
         _fails(spins.test_p17_selection_equals_brute_force_counting, s) for s in range(30))
     assert caught
+
+
+# ---------------------------------------------------------------------------
+# SpecPV buffer and rectification
+# ---------------------------------------------------------------------------
+
+import oracle.specpv_policy as SPP  # noqa: E402
+from tests import test_oracle_specpv_pins as ppins  # noqa: E402
+
+
+def test_buffer_rule_off_by_one_is_caught(monkeypatch):
+    monkeypatch.setattr(SPP, "needs_rectification", lambda n, size: n >= size)
+    assert _fails(ppins.test_buffer_rule_from_the_pages)
+
+
+@pytest.mark.parametrize("mut", ["no_root", "reversed_chain"])
+def test_wrong_rectifying_tree_is_caught(monkeypatch, mut):
+    orig = SPP.rectify_tree
+
+    def broken(buffer_tokens, root_token, parents, draft_tokens):
+        if mut == "reversed_chain":
+            return orig(list(buffer_tokens)[::-1], root_token, parents, draft_tokens)
+        # the draft tree hung under the last buffered token, the root dropped
+        par, tok = orig(list(buffer_tokens)[:-1] or list(buffer_tokens), buffer_tokens[-1],
+                        parents, draft_tokens)
+        return par, tok
+    monkeypatch.setattr(SPP, "rectify_tree", broken)
+    caught = _fails(ppins.test_rectify_tree_hand_worked) or any(
+        _fails(ppins.test_rectifying_acceptance_equals_chain_then_tree, s) for s in range(40))
+    assert caught

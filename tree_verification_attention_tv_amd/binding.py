@@ -111,6 +111,10 @@ def lib() -> ctypes.CDLL:
             L.tv_select_blocks.argtypes = [ctypes.POINTER(SelectDesc), vp, vp, vp, vp, vp, vp, vp,
                                            sz, vp, vp]
             L.tv_select_blocks.restype = i32
+            L.tv_specpv_needs_rectification.argtypes = [i32, i32]
+            L.tv_specpv_needs_rectification.restype = i32
+            L.tv_specpv_rectify_tree.argtypes = [vp, i32, i32, vp, vp, i32, vp, vp]
+            L.tv_specpv_rectify_tree.restype = i32
             L.tv_status_string.argtypes = [i32]
             L.tv_status_string.restype = ctypes.c_char_p
             L.tv_version.argtypes = []
@@ -400,3 +404,41 @@ def select_blocks(q, summaries, prefix_len, *, cache_capacity, max_prefix_len, b
         _ptr(n_blocks), _ptr(scores), _ptr(workspace), workspace.numel(), _err_ptr(dev_err),
         _stream(dev)))
     return (block_idx, n_blocks, scores) if want_scores else (block_idx, n_blocks)
+
+
+# ---------------------------------------------------------------------------
+# SpecPV buffer policy (host functions of the library)
+# ---------------------------------------------------------------------------
+
+def _host_i32(name, a):
+    import numpy as np
+    arr = np.ascontiguousarray(a, dtype=np.int32)
+    if arr.ndim != 1:
+        raise ValueError(f"{name} must be one-dimensional")
+    return arr
+
+
+def specpv_needs_rectification(n_partial: int, buffer_size: int) -> bool:
+    r = int(lib().tv_specpv_needs_rectification(int(n_partial), int(buffer_size)))
+    if r < 0:
+        raise TVError("tv_specpv_needs_rectification", 2)
+    return r == 1
+
+
+def specpv_rectify_tree(buffer_tokens, root_token, parents, draft_tokens):
+    """Host arrays -> (parents, tokens) int32 numpy arrays of the rectifying
+    tree: the buffered tokens as a chain, the current root, the draft tree."""
+    import numpy as np
+    buf = _host_i32("buffer_tokens", buffer_tokens)
+    par = _host_i32("parents", parents)
+    dr = _host_i32("draft_tokens", draft_tokens)
+    if dr.shape != par.shape:
+        raise ValueError("parents and draft_tokens differ in length")
+    n = buf.shape[0] + par.shape[0]
+    par_out = np.empty(n, dtype=np.int32)
+    tok_out = np.empty(n, dtype=np.int32)
+    c = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+    _check("tv_specpv_rectify_tree", lib().tv_specpv_rectify_tree(
+        c(buf), buf.shape[0], int(root_token), c(par), c(dr), par.shape[0], c(par_out),
+        c(tok_out)))
+    return par_out, tok_out

@@ -253,15 +253,19 @@ def chain_tree(n_nodes: int) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def planted_logits(rng: np.random.Generator, rows: int, vocab: int, dtype: str,
-                   std: float, tie_fraction: float = _TIE_FRACTION):
+                   std: float, tie_fraction: float = _TIE_FRACTION, targets=None):
     """Logit rows with a planted maximum.
 
     Each row draws N(0, std^2), clipped just below a cap; the cap is written
-    at a uniform random index (and for ``tie_fraction`` of rows also at a
-    second, higher index).  Returns (logits [rows][vocab], planted int32
-    [rows]); the planted index is the lowest index holding the cap.
+    at a uniform random index (or at ``targets[r]`` when given) and, for
+    ``tie_fraction`` of rows, also at a second, higher index.  Returns
+    (logits [rows][vocab], planted int32 [rows]); the planted index is the
+    lowest index holding the cap.
     """
-    target = rng.integers(0, vocab, size=rows).astype(np.int32)
+    if targets is None:
+        target = rng.integers(0, vocab, size=rows).astype(np.int32)
+    else:
+        target = np.asarray(targets, dtype=np.int32).copy()
     x = rng.normal(0.0, std, size=(rows, vocab)).astype(np.float32)
     if dtype == "bf16":
         np.minimum(x, np.float32(_BF16_BELOW_CAP), out=x)
@@ -492,3 +496,59 @@ def make_select_case(seed: int, *, batch: int, n_nodes: int, hq: int, hkv: int, 
     wl.q = f32_to_bf16_bits(q)
     wl.block_idx, wl.n_blocks = planted, counts
     return wl
+
+
+# ---------------------------------------------------------------------------
+# SpecPV multi-step scenarios (partial steps and rectifying full steps)
+# ---------------------------------------------------------------------------
+
+def _step_rng(seed: int, step: int, stream: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, step, stream])))
+
+
+def specpv_draft(seed: int, step: int, n_nodes: int, vocab: int, p_match: float):
+    """The draft side of one step: a random recursive tree of ``n_nodes``, the
+    target token planted in each node's logits row, and draft tokens (a child
+    proposes its parent's planted token with probability ``p_match``).
+    Returns (parents, planted, draft_tokens); draft_tokens[0] is a placeholder
+    for the root."""
+    rng = _step_rng(seed, step, 0)
+    parents = random_tree(rng, n_nodes)
+    planted = rng.integers(0, vocab, size=n_nodes).astype(np.int32)
+    draft = draft_tokens_for(rng, parents, planted, vocab, p_match)
+    return parents, planted, draft
+
+
+def specpv_step_inputs(seed: int, step: int, tokens, n_chain: int, planted_draft, *, vocab: int,
+                       hq: int, hkv: int, d: int, p_keep: float):
+    """Queries, tree K/V and bf16 logits for the nodes of one step's tree.
+
+    ``tokens`` are the tree's node tokens; the first ``n_chain`` nodes are a
+    chain of previously emitted tokens (empty for a partial step) and the rest
+    is the draft tree, whose rows plant ``planted_draft``.  Chain row k plants
+    the token of node k + 1 with probability ``p_keep`` (the partial step's
+    choice survives re-verification), else a uniform random id."""
+    tokens = np.asarray(tokens, dtype=np.int32)
+    n = tokens.shape[0]
+    rng = _step_rng(seed, step, 1 + n_chain)
+    targets = np.empty(n, dtype=np.int32)
+    keep = rng.random(max(n_chain, 1)) < p_keep
+    other = rng.integers(0, vocab, size=max(n_chain, 1))
+    for k in range(n_chain):
+        targets[k] = tokens[k + 1] if keep[k] else other[k]
+    targets[n_chain:] = np.asarray(planted_draft, dtype=np.int32)
+    logits, _ = planted_logits(rng, n, vocab, "bf16", math.sqrt(2.0), targets=targets)
+    q = normal_bf16(rng, (1, n, hq, d))
+    k_tree = normal_bf16(rng, (1, n, hkv, d))
+    v_tree = normal_bf16(rng, (1, n, hkv, d))
+    return q, k_tree, v_tree, logits.reshape(1, n, vocab)
+
+
+def long_context_with_tree(parents, name: str = "long_context_tree") -> Workload:
+    """The long-context shape (batch 1, 60000-token prefix, 32 query / 8 KV
+    heads of 128, 128256-token bf16 logits) verifying the given tree, with
+    fresh seeded queries, tree K/V, logits and draft tokens for its nodes."""
+    parents = np.asarray(parents, dtype=np.int32)
+    rs = _streams(_SEED["long_context"] * 3 + parents.shape[0])
+    return _assemble(name, rs, [parents], 128256, "bf16", math.sqrt(2.0), 0.75, 32, 8, 128,
+                     [60000])
