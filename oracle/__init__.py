@@ -1,5 +1,5 @@
-"""fp64 CPU oracle for tree verification and SpecPV block selection -- test
-infrastructure only.
+"""fp64 CPU oracle for tree verification (greedy and stochastic), SpecPV block
+selection and SpecPV's buffer policy -- test infrastructure only.
 
 Only the tests, the smoke check and the benchmark's CPU-baseline leg may use
 this package.  The product path (the HIP library and its Python binding)
@@ -25,4 +25,9 @@ from .block_select import (  # noqa: F401
     select_blocks,
     specpv_select,
     ub_score,
+)
+from .stochastic import (  # noqa: F401
+    philox4x64_10,
+    stochastic_accept,
+    target_probs,
 )

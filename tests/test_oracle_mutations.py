@@ -194,3 +194,38 @@ def test_wrong_rectifying_tree_is_caught(monkeypatch, mut):
     caught = _fails(ppins.test_rectify_tree_hand_worked) or any(
         _fails(ppins.test_rectifying_acceptance_equals_chain_then_tree, s) for s in range(40))
     assert caught
+
+
+# ---------------------------------------------------------------------------
+# stochastic verification (T > 0)
+# ---------------------------------------------------------------------------
+
+import inspect  # noqa: E402
+
+import oracle.stochastic as STO  # noqa: E402
+from tests import test_oracle_stochastic_pins as spins2  # noqa: E402
+
+
+def _walk_with(old, new):
+    src = inspect.getsource(STO._walk)
+    assert old in src
+    ns = dict(STO.__dict__)
+    exec(src.replace(old, new), ns)
+    return ns["_walk"]
+
+
+@pytest.mark.parametrize("old,new", [
+    ("ok = unif * rest < px", "ok = unif < px"),                  # no renormalisation
+    ("resid[x] = 0.0", "pass"),                                   # rejected tokens kept
+    ("target = unif * rest", "target = unif"),                    # bonus draw unscaled
+    ("hits = np.nonzero(cum > target)[0]", "hits = np.array([int(np.argmax(resid))])"),
+])
+def test_wrong_speculative_sampling_is_caught(monkeypatch, old, new):
+    monkeypatch.setattr(STO, "_walk", _walk_with(old, new))
+    assert _fails(spins2.test_first_emitted_token_follows_the_target) or \
+        _fails(spins2.test_token_after_an_accepted_child_follows_its_row)
+
+
+def test_wrong_philox_constant_is_caught(monkeypatch):
+    monkeypatch.setattr(STO, "_M1", STO._M1 ^ 4)
+    assert _fails(spins2.test_philox_matches_numpy, 0)
