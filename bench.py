@@ -177,6 +177,11 @@ class StepRunner:
                         torch.empty((self.b,), dtype=torch.int32, device=dev),
                         torch.empty((self.b, self.n), dtype=torch.int32, device=dev),
                         torch.empty((self.b,), dtype=torch.int32, device=dev))
+        self.ws_sto = torch.empty(binding.stochastic_accept_workspace_size(self.b, self.n, wl.vocab),
+                                  dtype=torch.uint8, device=dev)
+        self.sto_out = (torch.empty((self.b,), dtype=torch.int32, device=dev),
+                        torch.empty((self.b, self.n), dtype=torch.int32, device=dev),
+                        torch.empty((self.b,), dtype=torch.int32, device=dev))
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
         self.stream = torch.cuda.current_stream(dev)
 
@@ -217,6 +222,12 @@ class StepRunner:
     def k_accept(self, s):
         self.binding.greedy_accept(s.logits, s.parents, s.draft, workspace=self.ws_acc,
                                    dev_err=self.err, outputs=self.acc_out)
+
+    def k_accept_stochastic(self, s):
+        # the same logits verified by sampling at T = 1 (counter-based uniforms)
+        self.binding.stochastic_accept(s.logits, s.parents, s.draft, 1.0, seed=(1, 2), step=0,
+                                       workspace=self.ws_sto, dev_err=self.err,
+                                       outputs=self.sto_out)
 
     def k_commit(self, s):
         self.binding.commit_kv(s.k_tree, s.v_tree, self.acc_out[2], self.acc_out[1], s.prefix_len,
@@ -262,6 +273,30 @@ class StepRunner:
         z.record(self.stream)
         torch.cuda.synchronize()
         return a.elapsed_time(z) * 1e3 / iters
+
+    def timed_graph(self, fn, per_graph=20, reps=5):
+        """Average microseconds of one call of `fn` on the GPU: `per_graph`
+        calls over the rotated input copies captured in one HIP graph, whose
+        replays are timed with HIP events on the library's stream.  No host
+        launch overhead enters; the dispatch gaps between the graph's kernels
+        do."""
+        import torch
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for k in range(per_graph):
+                fn(self.sets[k % self.rot])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(self.stream)
+        for _ in range(reps):
+            g.replay()
+        z.record(self.stream)
+        torch.cuda.synchronize()
+        del g
+        return a.elapsed_time(z) * 1e3 / (reps * per_graph)
 
     def check_errors(self):
         if int(self.err.item()) != 0:
@@ -329,13 +364,17 @@ def measure(wl, partial, steps, warmup, warm, num_splits, dev, graph=True, specp
         t0 = time.perf_counter()
         step_us = r.timed(r.replay, steps)
         wall_us = (time.perf_counter() - t0) * 1e6 / steps
-    iters = max(steps, 50)
-    calls = {"mask": r.timed(r.k_mask, iters), "attention": r.timed(r.k_attn, iters),
-             "accept": r.timed(r.k_accept, iters), "commit": r.timed(r.k_commit, iters)}
+    # per-call GPU time from graph replays (eager back-to-back calls would
+    # also measure the host's launch rate)
+    tm = r.timed_graph if graph else (lambda fn, **kw: r.timed(fn, max(steps, 50)))
+    calls = {"mask": tm(r.k_mask), "attention": tm(r.k_attn), "accept": tm(r.k_accept),
+             "commit": tm(r.k_commit)}
+    if not specpv and not partial:
+        calls["accept_stochastic"] = tm(r.k_accept_stochastic)
     if specpv:
-        calls["select"] = r.timed(r.k_select, iters)
-        calls["summaries_update"] = r.timed(r.k_summ_update, iters)
-        calls["summaries_full"] = r.timed(r.k_summ_full, max(iters // 5, 10))
+        calls["select"] = tm(r.k_select)
+        calls["summaries_update"] = tm(r.k_summ_update)
+        calls["summaries_full"] = tm(r.k_summ_full, per_graph=5)
     r.check_errors()
     return r, step_us, wall_us, eager_us, calls
 
@@ -526,6 +565,8 @@ def main():
         "kv_gbps": round(kv_bytes / (calls["attention"] * 1e-6) / 1e9, 1),
         "kv_hbm_frac": round(kv_bytes / (calls["attention"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "call_us": {k: round(v, 3) for k, v in calls.items()},
+        "accept_gbps": {k: round(logit_bytes / (calls[k] * 1e-6) / 1e9, 1)
+                        for k in ("accept", "accept_stochastic") if k in calls},
         "roofline": {
             "kernel": ("tv_tree_attention (attn_split_kernel + attn_combine_kernel)"
                        if dominant == "attention" else

@@ -12,6 +12,8 @@
  *                        (full, or a listed subset of KV blocks) and the tree
  *   tv_greedy_accept     per-node vocabulary argmax, longest accepted path,
  *                        accepted length and bonus token
+ *   tv_stochastic_accept the same at temperature > 0 (speculative sampling
+ *                        along the tree, counter-based random numbers)
  *   tv_commit_kv         copy the accepted nodes' K/V rows into the cache
  *   tv_block_summaries   per-block element-wise max/min keys (SpecPV retrieval)
  *   tv_select_blocks     score blocks against the tree's queries and pick the
@@ -201,6 +203,44 @@ tv_status tv_greedy_accept(const void* logits, tv_dtype dtype, int64_t vocab, in
                            int32_t n_nodes, int32_t* target_argmax, int32_t* accept_len,
                            int32_t* accept_path, int32_t* bonus_token, void* workspace,
                            size_t workspace_bytes, int32_t* dev_err, hipStream_t stream);
+
+/*
+ * tv_stochastic_accept -- acceptance at temperature T > 0 (sampling).
+ *
+ * Sources: SpecPV Sec. 2 "Related Work" (speculative sampling is equivalent
+ * to sampling from the target; tree-structured candidates as in SpecInfer);
+ * SpecPV App. D / App. E and SpecBlock Sec. 4 (sampling at T = 0.6, 0.7,
+ * 1.0).  Random numbers: Philox-4x64-10 (Salmon et al., SC 2011).
+ *
+ * p_u = softmax(logits_u / T) over the whole vocabulary (fp32).  Drafts are
+ * point masses.  Starting at the root, at accepted node u the children are
+ * tried in ascending node index: child c (token x) is accepted iff
+ *   U(step, b, u, k) * R < p_u(x)      (k = c's rank among u's children)
+ * where R is the mass of u's distribution not yet rejected (starts at 1;
+ * R -= p_u(x) on rejection); a token outside [0, vocab) or already rejected
+ * at u has probability 0.  The first accepted child becomes the next node.
+ * When no child is accepted the walk ends at u and the bonus token is the
+ * smallest y (vocabulary order) whose cumulative residual probability
+ * (p_u without the rejected tokens) exceeds U(step, b, u, 2^64-1) * R.
+ * U(c0, c1, c2, c3) = (first word of Philox-4x64-10 with counter
+ * (c0, c1, c2, c3) and key (seed0, seed1)) >> 40, times 2^-24.
+ * The emitted tokens (accepted drafts, then the bonus) are distributed as
+ * sampling from the target one token at a time.
+ *
+ * Layouts and outputs as tv_greedy_accept (no target_argmax).  temperature
+ * must be finite and > 0 (TV_ERR_SHAPE).  Fallbacks: a malformed parent
+ * array gives the root-only walk (bonus drawn from p_root) and
+ * TV_DERR_BAD_PARENT.  NaN/inf logits are outside the contract.
+ * Workspace: tv_stochastic_accept_workspace_size(...) bytes, 16-byte aligned.
+ */
+size_t tv_stochastic_accept_workspace_size(int32_t batch, int32_t n_nodes, int64_t vocab);
+tv_status tv_stochastic_accept(const void* logits, tv_dtype dtype, int64_t vocab,
+                               int64_t row_stride, const int32_t* parents,
+                               const int32_t* draft_tokens, int32_t batch, int32_t n_nodes,
+                               float temperature, uint64_t seed0, uint64_t seed1, uint64_t step,
+                               int32_t* accept_len, int32_t* accept_path, int32_t* bonus_token,
+                               void* workspace, size_t workspace_bytes, int32_t* dev_err,
+                               hipStream_t stream);
 
 /*
  * tv_commit_kv -- append the accepted path's K/V to the cache.

@@ -124,3 +124,21 @@ def test_selection_host_checks_enqueue_nothing():
     assert call(desc(n_q_heads=130, n_kv_heads=2, reduction=binding.REDUCE_MAX)) == 3
     assert call(desc(n_q_heads=130, n_kv_heads=2, reduction=binding.REDUCE_MEAN)) == 1
     assert L.tv_select_blocks(None, p, p, p, p, p, None, p, 1 << 20, None, None) == 1
+
+
+def test_stochastic_accept_host_checks():
+    L = binding.lib()
+    names = declared_functions()
+    assert "tv_stochastic_accept" in names and "tv_stochastic_accept_workspace_size" in names
+    p = ctypes.c_void_p(256)
+    assert binding.stochastic_accept_workspace_size(2, 60, 128256) > 0
+    assert binding.stochastic_accept_workspace_size(1, 0, 128256) == 0
+    args = lambda t: (p, 0, 100, 100, p, p, 1, 8, t, 1, 2, 3, p, p, p, p, 1 << 20, None, None)  # noqa
+    assert L.tv_stochastic_accept(*args(0.0)) == 2
+    assert L.tv_stochastic_accept(*args(-1.0)) == 2
+    assert L.tv_stochastic_accept(*args(float("inf"))) == 2
+    assert L.tv_stochastic_accept(*args(float("nan"))) == 2
+    assert L.tv_stochastic_accept(None, 0, 100, 100, p, p, 1, 8, 1.0, 1, 2, 3, p, p, p, p,
+                                  1 << 20, None, None) == 1
+    assert L.tv_stochastic_accept(p, 0, 100, 50, p, p, 1, 8, 1.0, 1, 2, 3, p, p, p, p, 1 << 20,
+                                  None, None) == 2

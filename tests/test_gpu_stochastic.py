@@ -1,0 +1,202 @@
+"""Stochastic verification (T > 0) on the GPU against the fp64 oracle.
+
+Both sides draw the same Philox-4x64-10 uniforms, so every accept/reject
+decision and the bonus draw are fixed numbers; they can differ only where a
+uniform falls within rounding distance of its threshold (the GPU computes
+p in fp32).  The comparison therefore replays the oracle with the GPU's
+choice at decisions closer than TOL to their threshold and requires:
+
+* identical accepted length and path;
+* the bonus equal to the oracle's, or, if the draw fell within TOL of a CDF
+  boundary, the GPU's token on the other side of that boundary.
+
+TOL = 1e-4 (absolute, on the probability scale): fp32 softmax sums over
+128256 terms and the chunked prefix sums of the bonus draw are off by at most
+a few 1e-6 in these inputs.
+
+A Monte Carlo check over 3000 keys also compares the GPU's first emitted
+token with the target distribution directly (chi-square), independent of the
+oracle.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+from scipy import stats
+
+import oracle
+import oracle.stochastic as ST
+from tree_verification_attention_tv_amd import binding
+from tree_verification_attention_tv_amd import workloads as W
+
+from .gpu_util import dev_bf16, dev_i32
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def gpu_run(parents, draft, logits, temperature, seed, step, dtype="bf16", stride_pad=0):
+    if dtype == "bf16":
+        lg = dev_bf16(logits)
+    else:
+        lg = torch.from_numpy(np.ascontiguousarray(logits)).cuda()
+    if stride_pad:
+        b, n, v = lg.shape
+        big = torch.zeros((b, n, v + stride_pad), dtype=lg.dtype, device="cuda")
+        big[:, :, :v] = lg
+        lg = big[:, :, :v]
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    alen, path, bonus = binding.stochastic_accept(lg, dev_i32(parents), dev_i32(draft),
+                                                  temperature, seed=seed, step=step, dev_err=err)
+    torch.cuda.synchronize()
+    return alen.cpu().numpy(), path.cpu().numpy(), bonus.cpu().numpy(), int(err.item())
+
+
+def check_against_oracle(parents, draft, logits, temperature, seed, step, got):
+    alen, path, bonus = got[:3]
+    bsz = parents.shape[0]
+
+    def decide(b, event, ok):
+        _, u, c, unif, rest, px = event
+        if abs(unif * rest - px) > TOL:
+            return ok
+        # near the threshold: follow the GPU (accepted c iff c is on its path after u)
+        gp = list(path[b, :alen[b] + 1])
+        return u in gp and gp.index(u) + 1 < len(gp) and gp[gp.index(u) + 1] == c
+
+    a, p, y, events = ST.stochastic_accept(logits, parents, draft, temperature, seed, step,
+                                           return_events=True, decide=decide)
+    assert np.array_equal(alen, a), f"accept_len {alen} vs oracle {a}"
+    assert np.array_equal(path, p)
+    for b in range(bsz):
+        if bonus[b] == y[b]:
+            continue
+        # only a draw within TOL of the boundary between the two tokens may differ
+        _, u, _, unif, rest, target = events[b][-1]
+        probs = ST.target_probs(logits[b, u], temperature)
+        removed = {int(draft[b, c]) for (kind, uu, c, *_r) in events[b][:-1]
+                   if kind == "child" and uu == u and 0 <= int(draft[b, c]) < probs.shape[0]}
+        resid = probs.copy()
+        for x in removed:
+            resid[x] = 0.0
+        cum = np.cumsum(resid)
+        g = int(bonus[b])
+        assert resid[g] > 0.0, f"seq {b}: bonus {g} is not an eligible token"
+        lo_edge = cum[g] - resid[g]
+        assert lo_edge - TOL <= target <= cum[g] + TOL, (
+            f"seq {b}: bonus {g} (cdf {lo_edge:.6g}..{cum[g]:.6g}) vs oracle {y[b]}, "
+            f"target {target:.6g}")
+
+
+CASES = [
+    # seed, batch, n_nodes, vocab, dtype, temperature, tree
+    (1, 4, 60, 128256, "bf16", 0.6, "eagle"),
+    (2, 4, 60, 128256, "bf16", 1.0, "eagle"),
+    (3, 3, 96, 32000, "bf16", 0.7, "random"),
+    (4, 2, 17, 1000, "f32", 0.7, "chain"),
+    (5, 16, 32, 50000, "bf16", 1.0, "eagle"),
+    (6, 1, 1, 128256, "bf16", 1.0, "eagle"),
+    (7, 2, 256, 4099, "f32", 0.6, "random"),
+]
+
+
+@pytest.mark.parametrize("step", [0, 7])
+@pytest.mark.parametrize("case", CASES)
+def test_stochastic_matches_oracle(case, step):
+    seed, batch, n, vocab, dtype, temp, tree = case
+    _say(f"[stochastic] seed {seed} batch {batch} N {n} V {vocab} {dtype} T {temp} {tree} "
+         f"step {step}")
+    parents, draft, logits = W.make_sampling_case(seed, batch=batch, n_nodes=n, vocab=vocab,
+                                                  dtype=dtype, tree=tree)
+    got = gpu_run(parents, draft, logits, temp, (seed, 99), step, dtype)
+    assert got[3] == 0
+    check_against_oracle(parents, draft, logits, temp, (seed, 99), step, got)
+
+
+def test_strided_rows_and_out_of_range_tokens():
+    _say("[stochastic] strided rows, tokens out of range, repeated siblings")
+    parents, draft, logits = W.make_sampling_case(11, batch=3, n_nodes=40, vocab=5003,
+                                                  dtype="bf16", tree="random")
+    draft[0, 5] = -1
+    draft[1, 7] = 5003
+    # repeated sibling tokens
+    kids = [j for j in range(1, 40) if parents[2, j] == 0]
+    for j in kids[1:]:
+        draft[2, j] = draft[2, kids[0]]
+    got = gpu_run(parents, draft, logits, 0.7, (5, 6), 3, "bf16", stride_pad=13)
+    assert got[3] == 0
+    check_against_oracle(parents, draft, logits, 0.7, (5, 6), 3, got)
+
+
+def test_malformed_tree_falls_back_to_the_root():
+    _say("[stochastic] malformed tree")
+    parents, draft, logits = W.make_sampling_case(12, batch=2, n_nodes=10, vocab=777,
+                                                  dtype="f32", tree="chain")
+    parents[1, 4] = 7
+    alen, path, bonus, err = gpu_run(parents, draft, logits, 1.0, (1, 1), 0, "f32")
+    assert err & binding.DERR_BAD_PARENT
+    assert alen[1] == 0 and path[1, 0] == 0 and np.all(path[1, 1:] == -1)
+    # the root-only walk draws the bonus from the root's row
+    root_only = ST.stochastic_accept(logits[1:2, :1], parents[1:2, :1], draft[1:2, :1], 1.0,
+                                     (1, 1), 0, return_events=True)
+    tgt = root_only[3][0][-1][-1]
+    cum = np.cumsum(ST.target_probs(logits[1, 0], 1.0))
+    g = int(bonus[1])
+    assert cum[g] - (cum[g] - (cum[g - 1] if g else 0.0)) - TOL <= tgt <= cum[g] + TOL
+
+
+def test_host_checks():
+    parents, draft, logits = W.make_sampling_case(13, batch=1, n_nodes=4, vocab=64, dtype="f32")
+    for bad_t in (0.0, -1.0, float("inf"), float("nan")):
+        with pytest.raises(binding.TVError):
+            gpu_run(parents, draft, logits, bad_t, (0, 0), 0, "f32")
+
+
+def test_first_token_is_distributed_as_the_target():
+    # independent of the oracle: 3000 keys, chi-square against softmax(l/T)
+    _say("[stochastic] Monte Carlo of the first emitted token")
+    vocab, temp = 8, 0.8
+    rng = np.random.default_rng(21)
+    rows = rng.normal(0, 1.5, size=(4, vocab)).astype(np.float32)
+    parents = np.array([[-1, 0, 0, 0]], dtype=np.int32)
+    draft = np.array([[0, 3, 5, 3]], dtype=np.int32)
+    lg = torch.from_numpy(rows.copy()).cuda().view(1, 4, vocab)
+    par_d, dr_d = dev_i32(parents), dev_i32(draft)
+    ws = torch.empty(binding.stochastic_accept_workspace_size(1, 4, vocab), dtype=torch.uint8,
+                     device="cuda")
+    outs = (torch.empty(1, dtype=torch.int32, device="cuda"),
+            torch.empty((1, 4), dtype=torch.int32, device="cuda"),
+            torch.empty(1, dtype=torch.int32, device="cuda"))
+    firsts = []
+    trials = 3000
+    res = torch.empty((trials, 3), dtype=torch.int32, device="cuda")
+    for k in range(trials):
+        binding.stochastic_accept(lg, par_d, dr_d, temp, seed=(k, 4242), step=0, workspace=ws,
+                                  outputs=outs)
+        res[k, 0] = outs[0][0]
+        res[k, 1] = outs[1][0, 1]
+        res[k, 2] = outs[2][0]
+    r = res.cpu().numpy()
+    for alen, node1, bonus in r:
+        firsts.append(int(draft[0, node1]) if alen >= 1 else int(bonus))
+    z = rows[0].astype(np.float64) / temp
+    p = np.exp(z - z.max())
+    p /= p.sum()
+    counts = np.bincount(firsts, minlength=vocab)
+    assert stats.chisquare(counts, p * trials).pvalue > 1e-4
+    # the repeated sibling (node 3) is never accepted
+    assert not np.any((r[:, 0] >= 1) & (r[:, 1] == 3))

@@ -115,6 +115,12 @@ def lib() -> ctypes.CDLL:
             L.tv_specpv_needs_rectification.restype = i32
             L.tv_specpv_rectify_tree.argtypes = [vp, i32, i32, vp, vp, i32, vp, vp]
             L.tv_specpv_rectify_tree.restype = i32
+            L.tv_stochastic_accept_workspace_size.argtypes = [i32, i32, i64]
+            L.tv_stochastic_accept_workspace_size.restype = sz
+            L.tv_stochastic_accept.argtypes = [vp, i32, i64, i64, vp, vp, i32, i32,
+                                               ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64,
+                                               ctypes.c_uint64, vp, vp, vp, vp, sz, vp, vp]
+            L.tv_stochastic_accept.restype = i32
             L.tv_status_string.argtypes = [i32]
             L.tv_status_string.restype = ctypes.c_char_p
             L.tv_version.argtypes = []
@@ -266,7 +272,7 @@ def greedy_accept(logits, parents, draft_tokens, *, vocab=None, workspace=None, 
     _on_gpu("draft_tokens", draft_tokens, torch.int32)
     bsz, n = parents.shape
     if logits.shape[:2] != (bsz, n) or logits.stride(2) != 1 or \
-            logits.stride(0) != n * logits.stride(1):
+            (bsz > 1 and logits.stride(0) != n * logits.stride(1)):
         raise ValueError("logits must be [B][N][V] with unit vocab stride and uniform row stride")
     v = logits.shape[2] if vocab is None else int(vocab)
     dt = TV_BF16 if logits.dtype == torch.bfloat16 else TV_F32
@@ -287,6 +293,43 @@ def greedy_accept(logits, parents, draft_tokens, *, vocab=None, workspace=None, 
         _ptr(amax), _ptr(alen), _ptr(path), _ptr(bonus), _ptr(workspace), workspace.numel(),
         _err_ptr(dev_err), _stream(dev)))
     return amax, alen, path, bonus
+
+
+def stochastic_accept_workspace_size(batch, n_nodes, vocab) -> int:
+    return int(lib().tv_stochastic_accept_workspace_size(int(batch), int(n_nodes), int(vocab)))
+
+
+def stochastic_accept(logits, parents, draft_tokens, temperature, *, seed=(0, 0), step=0,
+                      vocab=None, workspace=None, dev_err=None, outputs=None):
+    """Speculative sampling along the tree at temperature > 0 ->
+    (accept_len [B], accept_path [B][N], bonus [B]), int32."""
+    _on_gpu("logits", logits, (torch.bfloat16, torch.float32), contiguous=False)
+    _on_gpu("parents", parents, torch.int32)
+    _on_gpu("draft_tokens", draft_tokens, torch.int32)
+    bsz, n = parents.shape
+    if logits.shape[:2] != (bsz, n) or logits.stride(2) != 1 or \
+            (bsz > 1 and logits.stride(0) != n * logits.stride(1)):
+        raise ValueError("logits must be [B][N][V] with unit vocab stride and uniform row stride")
+    v = logits.shape[2] if vocab is None else int(vocab)
+    dt = TV_BF16 if logits.dtype == torch.bfloat16 else TV_F32
+    dev = parents.device
+    if outputs is None:
+        outputs = (torch.empty((bsz,), dtype=torch.int32, device=dev),
+                   torch.empty((bsz, n), dtype=torch.int32, device=dev),
+                   torch.empty((bsz,), dtype=torch.int32, device=dev))
+    alen, path, bonus = outputs
+    ws_bytes = stochastic_accept_workspace_size(bsz, n, v)
+    if ws_bytes == 0:
+        raise TVError("tv_stochastic_accept_workspace_size", 2)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    mask64 = (1 << 64) - 1
+    _check("tv_stochastic_accept", lib().tv_stochastic_accept(
+        _ptr(logits), dt, v, int(logits.stride(1)), _ptr(parents), _ptr(draft_tokens), bsz, n,
+        float(temperature), int(seed[0]) & mask64, int(seed[1]) & mask64, int(step) & mask64,
+        _ptr(alen), _ptr(path), _ptr(bonus), _ptr(workspace), workspace.numel(),
+        _err_ptr(dev_err), _stream(dev)))
+    return alen, path, bonus
 
 
 def commit_kv(k_tree, v_tree, accept_path, accept_len, prefix_len, k_cache, v_cache, *,

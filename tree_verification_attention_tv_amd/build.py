@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtreeverify.so")
 
 SOURCES = ["tv_api.cpp", "tv_mask.hip", "tv_attention.hip", "tv_accept.hip", "tv_commit.hip",
-           "tv_select.hip", "tv_specpv.cpp"]
+           "tv_select.hip", "tv_specpv.cpp", "tv_stochastic.hip"]
 ARCH = "gfx950"
 
 

@@ -60,6 +60,15 @@ hipError_t launch_commit(const void* k_tree, const void* v_tree, const int32_t* 
                          int64_t seq_stride, int cap, int batch, int n, int hkv, int d,
                          int32_t* dev_err, hipStream_t stream);
 
+AcceptPlan plan_stochastic(int batch, int n, int64_t vocab);
+
+hipError_t launch_stochastic(const void* logits, tv_dtype dt, int64_t vocab, int64_t row_stride,
+                             const int32_t* parents, const int32_t* draft, int batch, int n,
+                             float temperature, uint64_t seed0, uint64_t seed1, uint64_t step,
+                             int32_t* accept_len, int32_t* accept_path, int32_t* bonus,
+                             void* workspace, const AcceptPlan& plan, int32_t* dev_err,
+                             hipStream_t stream);
+
 struct SelectPlan {
   int nb_cap;        // summary records per (sequence, kv head): ceil(capacity / block_size)
   int nb_max;        // blocks that can hold prefix tokens: ceil(min(max_prefix, cap) / bs)

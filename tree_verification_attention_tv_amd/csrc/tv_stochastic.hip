@@ -1,0 +1,566 @@
+// Stochastic (temperature > 0) acceptance of a verified draft tree.
+//
+// Sources: SpecPV Sec. 2 "Related Work" (speculative sampling is equivalent
+// to sampling from the target; tree-structured candidates), SpecPV App. D
+// and App. E and SpecBlock Sec. 4 (sampling at T = 0.6, 0.7, 1.0).  Random
+// numbers: Philox-4x64-10 (Salmon et al., SC 2011) on counters, so every
+// decision has a fixed uniform.
+//
+// Node u's target distribution is p_u = softmax(l_u / T).  Drafts are point
+// masses: at an accepted node the children are tried in ascending node
+// index, child c (token x) is accepted with probability p_u(x) / R, R the
+// mass not yet rejected at u (a token already rejected at u has probability
+// 0).  When every child is rejected the bonus token is drawn from the
+// residual by inverse CDF in vocabulary order.
+//
+// Two kernels:
+//  1. softmax_stats_kernel: one workgroup per (row chunk, logits row), the
+//     same streaming layout as the greedy argmax: each thread's 16-byte loads
+//     are all in flight at once.  Per chunk it writes (m, s): the chunk's max
+//     logit and sum_v 2^((l_v - m) c), c = log2(e) / T, summed in a fixed
+//     order (thread, then DPP/lane tree, then waves in order).  HBM-bound:
+//     the B*N*V logits are read once.
+//  2. stochastic_walk_kernel: one workgroup per sequence.  Every input of
+//     the walk is fetched in parallel first: each node's row statistics
+//     (M, Z), the probability of its draft token at its parent and its
+//     uniform.  One thread then walks the tree out of LDS.  The bonus draw
+//     finds its chunk from the chunk masses (minus the rejected tokens) and
+//     scans that chunk's logits, loaded with 16-byte loads, with a
+//     workgroup prefix sum.
+#include "tv_internal.h"
+
+#include <limits.h>
+
+namespace tv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kUnroll = 8;  // 16-byte vectors of bf16 per thread per chunk (fp32: twice as many)
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr int kWalkThreads = 1024;  // walk kernel: 16 waves, four per SIMD
+constexpr int kWalkWaves = kWalkThreads / kWave;
+constexpr int kPer = 16;    // tokens per walk thread in the bonus scan: chunk_len <= kWalkThreads * kPer
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T x);
+template <>
+__device__ __forceinline__ float to_f32<bf16>(bf16 x) {
+  return (float)x;
+}
+template <>
+__device__ __forceinline__ float to_f32<float>(float x) {
+  return x;
+}
+
+// ---- cross-lane helpers (DPP row ops and the gfx950 row swaps) ---------------------
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f(float old, float x) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(x), CTRL, ROW_MASK, 0xF, false));
+}
+
+// every lane gets the wave's maximum
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_f<0x128>(-INFINITY, x));
+  x = fmaxf(x, dpp_f<0x124>(-INFINITY, x));
+  x = fmaxf(x, dpp_f<0x122>(-INFINITY, x));
+  x = fmaxf(x, dpp_f<0x121>(-INFINITY, x));
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+
+// every lane gets the wave's sum (a fixed tree: the same order every call)
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp_f<0x128>(0.f, x);
+  x += dpp_f<0x124>(0.f, x);
+  x += dpp_f<0x122>(0.f, x);
+  x += dpp_f<0x121>(0.f, x);
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+
+// inclusive prefix sum over the wave (row_shr steps, then row_bcast 15 / 31)
+__device__ __forceinline__ float wave_incl_scan(float v) {
+  v += dpp_f<0x111>(0.f, v);
+  v += dpp_f<0x112>(0.f, v);
+  v += dpp_f<0x114>(0.f, v);
+  v += dpp_f<0x118>(0.f, v);
+  v += dpp_f<0x142, 0xA>(0.f, v);
+  v += dpp_f<0x143, 0xC>(0.f, v);
+  return v;
+}
+
+// ---- Philox-4x64-10 ----------------------------------------------------------------
+// 128-bit product of two 64-bit words from four 32x32 -> 64 products
+__device__ __forceinline__ void mul_64x64(uint64_t a, uint64_t b, uint64_t& hi, uint64_t& lo) {
+  const uint64_t a0 = (uint32_t)a, a1 = a >> 32, b0 = (uint32_t)b, b1 = b >> 32;
+  const uint64_t p00 = a0 * b0, p01 = a0 * b1, p10 = a1 * b0, p11 = a1 * b1;
+  const uint64_t mid = (p00 >> 32) + (uint32_t)p01 + (uint32_t)p10;
+  hi = p11 + (p01 >> 32) + (p10 >> 32) + (mid >> 32);
+  lo = (mid << 32) | (uint32_t)p00;
+}
+
+// Round: with products M0*c0 and M1*c2 (128-bit), the new state is
+// (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)); the key
+// advances by the Weyl increments between rounds.
+__device__ __forceinline__ uint64_t philox_first_word(uint64_t c0, uint64_t c1, uint64_t c2,
+                                                      uint64_t c3, uint64_t k0, uint64_t k1) {
+  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll 1
+  for (int r = 0; r < 10; ++r) {  // rolled: this kernel's code runs once per call
+    uint64_t hi0, lo0, hi1, lo1;
+    mul_64x64(M0, c0, hi0, lo0);
+    mul_64x64(M1, c2, hi1, lo1);
+    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+    k0 += W0;
+    k1 += W1;
+  }
+  return c0;
+}
+
+// uniform in [0, 1) from the 24 high bits (exact in fp32)
+__device__ __forceinline__ float philox_uniform(uint64_t step, uint64_t seq, uint64_t node,
+                                                uint64_t slot, uint64_t k0, uint64_t k1) {
+  return (float)(uint32_t)(philox_first_word(step, seq, node, slot, k0, k1) >> 40) * 0x1.0p-24f;
+}
+
+// ---- kernel 1: per-chunk softmax statistics ---------------------------------------------
+template <typename T, bool kVector>
+__global__ __launch_bounds__(kThreads) void softmax_stats_kernel(const T* __restrict__ logits,
+                                                                 int64_t vocab, int64_t row_stride,
+                                                                 int64_t chunk_len, int chunks,
+                                                                 float c2,
+                                                                 float2* __restrict__ stats) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int U = kUnroll * 8 / VEC;
+  __shared__ float s_red[kWaves];
+  const int chunk = blockIdx.x;
+  const int64_t row = blockIdx.y;
+  const T* src = logits + row * row_stride;
+  const int64_t begin = (int64_t)chunk * chunk_len;
+  const int64_t end = begin + chunk_len < vocab ? begin + chunk_len : vocab;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+
+  // every value of the thread's share, in registers (vector u of thread t
+  // covers begin + (u * kThreads + t) * VEC .. +VEC-1)
+  float v[U][VEC];
+  if (kVector) {
+    typedef T vec_t __attribute__((ext_vector_type(VEC)));
+    vec_t x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t base = begin + ((int64_t)u * kThreads + threadIdx.x) * VEC;
+      if (base + VEC <= end) x[u] = *reinterpret_cast<const vec_t*>(src + base);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t base = begin + ((int64_t)u * kThreads + threadIdx.x) * VEC;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e)
+        v[u][e] = base + VEC <= end ? to_f32<T>(x[u][e])
+                                    : (base + e < end ? to_f32<T>(src[base + e]) : -INFINITY);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const int64_t k = begin + ((int64_t)u * kThreads + threadIdx.x) * VEC + e;
+        v[u][e] = k < end ? to_f32<T>(src[k]) : -INFINITY;
+      }
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) m = fmaxf(m, v[u][e]);
+  m = wave_max(m);
+  if (lane == 0) s_red[wave] = m;
+  __syncthreads();
+  m = s_red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) m = fmaxf(m, s_red[w]);
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) s += exp2f((v[u][e] - m) * c2);  // -inf -> 0
+  s = wave_sum(s);
+  if (lane == 0) s_red[wave] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = s_red[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) t += s_red[w];
+    stats[row * chunks + chunk] = make_float2(m, t);
+  }
+}
+
+// ---- kernel 2: the walk ------------------------------------------------------------------
+struct WalkArgs {
+  const void* logits;
+  int64_t vocab, row_stride, chunk_len;
+  int chunks;
+  float c2;
+  const float2* stats;
+  const int32_t* parents;
+  const int32_t* draft;
+  int n;
+  uint64_t k0, k1, step;
+  int32_t* accept_len;
+  int32_t* accept_path;
+  int32_t* bonus;
+  int32_t* dev_err;
+};
+
+// kPer logits from..from+kPer-1 of one row as floats (-inf past `to`);
+// 16-byte loads when the span is whole and aligned
+template <typename T, bool kVector>
+__device__ __forceinline__ void load_span(const T* row, int64_t from, int64_t to,
+                                          float (&q)[kPer]) {
+  constexpr int VEC = 16 / sizeof(T);
+  if (kVector && from + kPer <= to) {
+    typedef T vec_t __attribute__((ext_vector_type(VEC)));
+    vec_t x[kPer / VEC];
+#pragma unroll
+    for (int u = 0; u < kPer / VEC; ++u) x[u] = *reinterpret_cast<const vec_t*>(row + from + u * VEC);
+#pragma unroll
+    for (int u = 0; u < kPer / VEC; ++u)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) q[u * VEC + e] = to_f32<T>(x[u][e]);
+  } else {
+    // ragged or unaligned: clamped addresses keep every load in bounds and
+    // branch-free, so all of them are in flight together
+    const int64_t last = to - 1;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) q[e] = to_f32<T>(row[from + e < to ? from + e : last]);
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) q[e] = from + e < to ? q[e] : -INFINITY;
+  }
+}
+
+template <typename T, bool kVector>
+__global__ __launch_bounds__(kWalkThreads) void stochastic_walk_kernel(WalkArgs a) {
+  __shared__ __attribute__((aligned(16))) int s_par[TV_MAX_NODES];
+  __shared__ __attribute__((aligned(16))) int s_tok[TV_MAX_NODES];
+  __shared__ int s_first[TV_MAX_NODES], s_next[TV_MAX_NODES], s_path[TV_MAX_NODES];
+  __shared__ float s_M[TV_MAX_NODES], s_Z[TV_MAX_NODES];  // row statistics of every node
+  __shared__ float s_p[TV_MAX_NODES];  // node j: p_parent(token_j), 0 if invalid or repeated
+  __shared__ float s_u[TV_MAX_NODES];  // node j: its acceptance uniform
+  __shared__ float s_ub[TV_MAX_NODES]; // node j: the bonus uniform if the walk ends at j
+  __shared__ int s_bad, s_depth, s_end, s_pick, s_last, s_chunk;
+  __shared__ float s_target, s_before;
+  __shared__ float s_wsum[kWalkWaves];
+
+  const int b = blockIdx.x, t = threadIdx.x, n = a.n;
+  const int lane = t % kWave, wave = t / kWave;
+  const int64_t row0 = (int64_t)b * n;
+  const T* logits = reinterpret_cast<const T*>(a.logits);
+  if (t == 0) s_bad = 0;
+  // every input of the walk is requested at once: tree, chunk statistics
+  int par = 0, tok = 0;
+  float2 st[8];
+  if (t < n) {
+    par = a.parents[row0 + t];
+    tok = a.draft[row0 + t];
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      if (c < a.chunks) st[c] = a.stats[(row0 + t) * a.chunks + c];
+  }
+  __syncthreads();
+  static_assert(kWalkThreads >= TV_MAX_NODES, "one thread per node slot");
+  if (t < TV_MAX_NODES) {
+    s_par[t] = t < n ? par : -2;  // slots past n match no parent
+    s_tok[t] = tok;
+  }
+  if (t < n) {
+    s_first[t] = INT_MAX;
+    const bool ok = t == 0 ? par == -1 : (par >= 0 && par < t);
+    if (!ok) s_bad = 1;
+    // row statistics (M, Z) of node t's row
+    float m = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      if (c < a.chunks) m = fmaxf(m, st[c].x);
+    for (int c = 8; c < a.chunks; ++c) m = fmaxf(m, a.stats[(row0 + t) * a.chunks + c].x);
+    float z = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      if (c < a.chunks) z += st[c].y * exp2f((st[c].x - m) * a.c2);
+    for (int c = 8; c < a.chunks; ++c) {
+      const float2 sc = a.stats[(row0 + t) * a.chunks + c];
+      z += sc.y * exp2f((sc.x - m) * a.c2);
+    }
+    s_M[t] = m;
+    s_Z[t] = z;
+  }
+  __syncthreads();
+  const bool bad = s_bad != 0;
+  // sibling links, sibling rank, the probability of each node's token at its
+  // parent and its uniform -- all nodes in parallel
+  if (t < n && t > 0 && !bad) {
+    atomicMin(&s_first[par], t);
+    // siblings before t (rank, repeated token) and the next sibling, 16
+    // slots per batch of 16-byte LDS reads
+    int nx = INT_MAX, rank = 0;
+    bool repeated = false;
+    for (int j0 = 0; j0 < n; j0 += 16) {
+      int4 pp[4], tt[4];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        pp[q4] = *reinterpret_cast<const int4*>(&s_par[j0 + 4 * q4]);
+        tt[q4] = *reinterpret_cast<const int4*>(&s_tok[j0 + 4 * q4]);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int j = j0 + e;
+        const int pj = e % 4 == 0 ? pp[e / 4].x : e % 4 == 1 ? pp[e / 4].y
+                     : e % 4 == 2 ? pp[e / 4].z : pp[e / 4].w;
+        const int tj = e % 4 == 0 ? tt[e / 4].x : e % 4 == 1 ? tt[e / 4].y
+                     : e % 4 == 2 ? tt[e / 4].z : tt[e / 4].w;
+        // arithmetic, not short-circuit logic: no branches per slot
+        const int before = (pj == par) & (j < t);
+        const int after = (pj == par) & (j > t);
+        rank += before;
+        repeated |= (before & (tj == tok)) != 0;
+        nx = min(nx, after ? j : INT_MAX);
+      }
+    }
+    s_next[t] = nx;
+    const bool valid = tok >= 0 && (int64_t)tok < a.vocab && !repeated;
+    const float l = valid ? to_f32<T>(logits[(row0 + par) * a.row_stride + tok]) : 0.f;
+    s_p[t] = valid ? exp2f((l - s_M[par]) * a.c2) / s_Z[par] : 0.f;
+    s_u[t] = philox_uniform(a.step, (uint64_t)b, (uint64_t)par, (uint64_t)rank, a.k0, a.k1);
+  }
+  // the bonus uniforms on other waves (other SIMDs) than the acceptance ones:
+  // node j's on thread (j + 128) mod 256
+  {
+    const int j = t - 512;  // waves 8.. (other SIMD slots than the acceptance draws)
+    if (j >= 0 && j < n) s_ub[j] = philox_uniform(a.step, (uint64_t)b, (uint64_t)j, ~0ull, a.k0, a.k1);
+  }
+  __syncthreads();
+  // the walk itself, from LDS
+  if (t == 0) {
+    int u = 0, depth = 0;
+    float rest = 1.f;
+    s_path[0] = 0;
+    for (;;) {
+      rest = 1.f;
+      int next = -1;
+      if (!bad)
+        for (int c = s_first[u]; c != INT_MAX; c = s_next[c]) {
+          if (s_u[c] * rest < s_p[c]) {
+            next = c;
+            break;
+          }
+          rest -= s_p[c];
+        }
+      if (next < 0) break;
+      s_path[++depth] = next;
+      u = next;
+    }
+    s_depth = depth;
+    s_end = u;
+    s_target = s_ub[u] * rest;
+  }
+  __syncthreads();
+
+  // ---- bonus draw from the residual of the last node's row ----
+  const int u = s_end;
+  const int64_t row = row0 + u;
+  const float M = s_M[u], Z = s_Z[u];
+  const float inv_z = 1.f / Z;
+  if (wave == 0) {
+    // chunk masses minus the rejected children's tokens (lane = chunk), an
+    // inclusive prefix in chunk order, and the first chunk whose prefix
+    // passes the target
+    const float target = s_target;
+    float base = 0.f;
+    int pick = -1, last_pos = 0;
+    float before = 0.f;
+    for (int c0 = 0; c0 < a.chunks && pick < 0; c0 += kWave) {
+      const int c = c0 + lane;
+      float w = 0.f;
+      if (c < a.chunks) {
+        const float2 sc = a.stats[row * a.chunks + c];
+        w = sc.y * exp2f((sc.x - M) * a.c2) * inv_z;
+        const int64_t lo = (int64_t)c * a.chunk_len, hi = lo + a.chunk_len;
+        if (!bad)
+          for (int k = s_first[u]; k != INT_MAX; k = s_next[k])
+            if (s_p[k] > 0.f && s_tok[k] >= lo && s_tok[k] < hi) w -= s_p[k];
+      }
+      const float incl = base + wave_incl_scan(w);
+      const uint64_t over = __ballot(c < a.chunks && incl > target);
+      const uint64_t pos = __ballot(c < a.chunks && w > 0.f);
+      if (pos) last_pos = c0 + 63 - __builtin_clzll(pos);
+      if (over) {
+        const int l = __builtin_ctzll(over);
+        pick = c0 + l;
+        before = __shfl(incl - w, l);
+      }
+      base = __shfl(incl, kWave - 1);
+    }
+    if (lane == 0) {
+      if (pick < 0) {   // rounding left the target past the end: last chunk with mass,
+        pick = last_pos;  // whose scan then never crosses and takes its last eligible token
+        before = -INFINITY;
+      }
+      s_chunk = pick;
+      s_before = before;
+      s_pick = INT_MAX;
+      s_last = -1;
+    }
+  }
+  __syncthreads();
+  const int64_t lo = (int64_t)s_chunk * a.chunk_len;
+  const int64_t hi = lo + a.chunk_len < a.vocab ? lo + a.chunk_len : a.vocab;
+  const int64_t my0 = lo + (int64_t)t * kPer;
+  float q[kPer];
+  load_span<T, kVector>(logits + row * a.row_stride, my0, hi, q);
+  const float c2 = a.c2;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) q[e] = my0 + e < hi ? exp2f((q[e] - M) * c2) * inv_z : 0.f;
+  // rejected children's tokens leave the residual
+  if (!bad)
+    for (int k = s_first[u]; k != INT_MAX; k = s_next[k]) {
+      const int64_t d = (int64_t)s_tok[k] - my0;
+      if (s_p[k] > 0.f && d >= 0 && d < kPer) {
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) q[e] = e == d ? 0.f : q[e];
+      }
+    }
+  float mine = 0.f;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) mine += q[e];
+  // exclusive prefix of the threads' sums, in token order
+  const float incl = wave_incl_scan(mine);
+  if (lane == kWave - 1) s_wsum[wave] = incl;
+  __syncthreads();
+  float off = s_before;
+#pragma unroll
+  for (int w = 0; w < kWalkWaves; ++w) off += w < wave ? s_wsum[w] : 0.f;
+  const float target = s_target;
+  // the running sum never decreases, so the first token whose running sum
+  // passes the target comes after exactly `le` tokens whose sum does not
+  float run = off + incl - mine;
+  int le = 0, last_e = -1;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    run += q[e];
+    le += run <= target ? 1 : 0;
+    last_e = q[e] > 0.f ? e : last_e;
+  }
+  const int found = le < kPer ? (int)(my0 + le) : INT_MAX;
+  const int last_ok = last_e >= 0 ? (int)(my0 + last_e) : -1;
+  // both are monotone in thread order: one lane per wave reports
+  const uint64_t fb = __ballot(found != INT_MAX);
+  if (fb && lane == __builtin_ctzll(fb)) atomicMin(&s_pick, found);
+  const uint64_t lb = __ballot(last_ok >= 0);
+  if (lb && lane == 63 - __builtin_clzll(lb)) atomicMax(&s_last, last_ok);
+  __syncthreads();
+  if (t == 0) {
+    int y = s_pick;
+    if (y == INT_MAX) y = s_last;  // rounding: the last eligible token of the chunk
+    if (y < 0) y = 0;              // nothing eligible at all (cannot happen for R > 0)
+    a.accept_len[b] = s_depth;
+    a.bonus[b] = y;
+    if (bad) raise_err(a.dev_err, TV_DERR_BAD_PARENT);
+  }
+  int32_t* path = a.accept_path + row0;
+  if (t < n) path[t] = t <= s_depth ? s_path[t] : -1;
+}
+
+}  // namespace
+
+AcceptPlan plan_stochastic(int batch, int n, int64_t vocab) {
+  AcceptPlan p;
+  const int64_t per_pass = (int64_t)kThreads * 8;
+  int64_t chunk = per_pass * kUnroll;
+  if (chunk > vocab) chunk = ((vocab + per_pass - 1) / per_pass) * per_pass;
+  if (chunk < per_pass) chunk = per_pass;
+  static_assert((int64_t)kThreads * 8 * kUnroll <= (int64_t)kWalkThreads * kPer, "bonus scan size");
+  p.chunk_len = chunk;
+  p.chunks = (int)((vocab + chunk - 1) / chunk);
+  p.ws_bytes = (size_t)batch * n * p.chunks * sizeof(float2) + 256;
+  return p;
+}
+
+hipError_t launch_stochastic(const void* logits, tv_dtype dt, int64_t vocab, int64_t row_stride,
+                             const int32_t* parents, const int32_t* draft, int batch, int n,
+                             float temperature, uint64_t seed0, uint64_t seed1, uint64_t step,
+                             int32_t* accept_len, int32_t* accept_path, int32_t* bonus,
+                             void* workspace, const AcceptPlan& plan, int32_t* dev_err,
+                             hipStream_t stream) {
+  float2* stats = reinterpret_cast<float2*>(workspace);
+  const float c2 = kLog2e / temperature;
+  const dim3 grid(plan.chunks, (unsigned)((size_t)batch * n));
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(logits);
+  if (dt == TV_BF16) {
+    if ((addr % 16 == 0) && (row_stride % 8 == 0))
+      hipLaunchKernelGGL((softmax_stats_kernel<bf16, true>), grid, dim3(kThreads), 0, stream,
+                         (const bf16*)logits, vocab, row_stride, plan.chunk_len, plan.chunks, c2,
+                         stats);
+    else
+      hipLaunchKernelGGL((softmax_stats_kernel<bf16, false>), grid, dim3(kThreads), 0, stream,
+                         (const bf16*)logits, vocab, row_stride, plan.chunk_len, plan.chunks, c2,
+                         stats);
+  } else {
+    if ((addr % 16 == 0) && (row_stride % 4 == 0))
+      hipLaunchKernelGGL((softmax_stats_kernel<float, true>), grid, dim3(kThreads), 0, stream,
+                         (const float*)logits, vocab, row_stride, plan.chunk_len, plan.chunks, c2,
+                         stats);
+    else
+      hipLaunchKernelGGL((softmax_stats_kernel<float, false>), grid, dim3(kThreads), 0, stream,
+                         (const float*)logits, vocab, row_stride, plan.chunk_len, plan.chunks, c2,
+                         stats);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  WalkArgs w{};
+  w.logits = logits;
+  w.vocab = vocab;
+  w.row_stride = row_stride;
+  w.chunk_len = plan.chunk_len;
+  w.chunks = plan.chunks;
+  w.c2 = c2;
+  w.stats = stats;
+  w.parents = parents;
+  w.draft = draft;
+  w.n = n;
+  w.k0 = seed0;
+  w.k1 = seed1;
+  w.step = step;
+  w.accept_len = accept_len;
+  w.accept_path = accept_path;
+  w.bonus = bonus;
+  w.dev_err = dev_err;
+  if (dt == TV_BF16) {
+    if ((addr % 16 == 0) && (row_stride % 8 == 0))
+      hipLaunchKernelGGL((stochastic_walk_kernel<bf16, true>), dim3(batch), dim3(kWalkThreads), 0,
+                         stream, w);
+    else
+      hipLaunchKernelGGL((stochastic_walk_kernel<bf16, false>), dim3(batch), dim3(kWalkThreads),
+                         0, stream, w);
+  } else {
+    if ((addr % 16 == 0) && (row_stride % 4 == 0))
+      hipLaunchKernelGGL((stochastic_walk_kernel<float, true>), dim3(batch), dim3(kWalkThreads),
+                         0, stream, w);
+    else
+      hipLaunchKernelGGL((stochastic_walk_kernel<float, false>), dim3(batch), dim3(kWalkThreads),
+                         0, stream, w);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tv

@@ -552,3 +552,45 @@ def long_context_with_tree(parents, name: str = "long_context_tree") -> Workload
     rs = _streams(_SEED["long_context"] * 3 + parents.shape[0])
     return _assemble(name, rs, [parents], 128256, "bf16", math.sqrt(2.0), 0.75, 32, 8, 128,
                      [60000])
+
+
+# ---------------------------------------------------------------------------
+# sampling (temperature > 0) cases
+# ---------------------------------------------------------------------------
+
+def sampling_logits(rng: np.random.Generator, rows: int, vocab: int, dtype: str, targets,
+                    lean=(9.0, 16.0)) -> np.ndarray:
+    """Logit rows shaped like a language model's at sampling time: N(0, 1)
+    background, the planted target token at U[lean] above 0 and a runner-up
+    token 0.5-3 below it, so that the target's probability ranges from a few
+    percent to nearly one.  bf16 (uint16 bits) or fp32 [rows][vocab]."""
+    x = rng.standard_normal(size=(rows, vocab), dtype=np.float32)
+    top = rng.uniform(lean[0], lean[1], size=rows).astype(np.float32)
+    gap = rng.uniform(0.5, 3.0, size=rows).astype(np.float32)
+    other = rng.integers(0, vocab, size=rows)
+    for r in range(rows):
+        x[r, other[r]] = top[r] - gap[r]
+        x[r, int(targets[r])] = top[r]
+    return f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+def make_sampling_case(seed: int, *, batch: int, n_nodes: int, vocab: int, dtype: str = "bf16",
+                       p_match: float = 0.8, tree: str = "eagle", lean=(9.0, 16.0)):
+    """Trees, draft tokens and logits for stochastic verification.  Returns
+    (parents [B][N], draft_tokens [B][N], logits [B][N][V])."""
+    rs = _streams(seed * 13 + 5)
+    trees = []
+    for _ in range(batch):
+        if tree == "chain" or n_nodes == 1:
+            trees.append(chain_tree(n_nodes))
+        elif tree == "random":
+            trees.append(random_tree(rs[0], n_nodes))
+        else:
+            depth = max(1, min(8, n_nodes - 1))
+            trees.append(eagle_tree(rs[0], depth, 4, n_nodes, depth))
+    parents = np.stack(trees).astype(np.int32)
+    planted = rs[1].integers(0, vocab, size=(batch, n_nodes)).astype(np.int32)
+    logits = sampling_logits(rs[2], batch * n_nodes, vocab, dtype, planted.reshape(-1), lean)
+    draft = np.stack([draft_tokens_for(rs[3], parents[b], planted[b], vocab, p_match)
+                      for b in range(batch)])
+    return parents, draft, logits.reshape(batch, n_nodes, vocab)
