@@ -117,7 +117,8 @@ tv_status tv_build_tree_mask(const int32_t* parents, int32_t batch, int32_t n_no
  *   k_tree   bf16 [batch][n_nodes][n_kv_heads][head_dim]    (v_tree the same)
  *   k_cache  bf16, sequence b at k_cache + b * cache_seq_stride elements, then
  *            [n_kv_heads][cache_capacity][head_dim]          (v_cache the same)
- *   prefix_len int32 [batch]; mask as produced by tv_build_tree_mask
+ *   prefix_len int32 [batch]; mask as produced by tv_build_tree_mask (or the
+ *            parent array, see tv_attn_ptrs)
  *   block_idx int32 [batch][max_blocks], n_blocks int32 [batch] (partial mode)
  *   out      bf16 [batch][n_nodes][n_q_heads][head_dim]
  *   lse      fp32 [batch][n_nodes][n_q_heads] or NULL
@@ -157,11 +158,19 @@ typedef struct {
   const void* k_cache;
   const void* v_cache;
   const int32_t* prefix_len;
-  const uint32_t* mask;
+  const uint32_t* mask;     /* as produced by tv_build_tree_mask; or NULL with parents */
   const int32_t* block_idx; /* NULL in full mode */
   const int32_t* n_blocks;  /* NULL in full mode */
   void* out;
   float* lse;               /* may be NULL */
+  /* Instead of `mask`: the parent array int32 [batch][n_nodes].  The
+     workgroups that attend to the tree then build their mask rows
+     themselves, by the rule and fallback of tv_build_tree_mask, and write
+     that call's outputs to mask_out / depth_out when these are not NULL
+     (both ignored when `mask` is given).  Exactly one of mask / parents. */
+  const int32_t* parents;
+  uint32_t* mask_out;
+  int32_t* depth_out;
 } tv_attn_ptrs;
 
 size_t tv_tree_attention_workspace_size(const tv_attn_desc* desc);

@@ -142,3 +142,17 @@ def test_stochastic_accept_host_checks():
                                   1 << 20, None, None) == 1
     assert L.tv_stochastic_accept(p, 0, 100, 50, p, p, 1, 8, 1.0, 1, 2, 3, p, p, p, p, 1 << 20,
                                   None, None) == 2
+
+
+def test_attention_needs_exactly_one_of_mask_and_parents():
+    L = binding.lib()
+    d = binding.AttnDesc(batch=1, n_nodes=8, n_q_heads=4, n_kv_heads=1, head_dim=128,
+                         cache_capacity=64, max_prefix_len=32)
+    p = 256
+    ptrs = binding.AttnPtrs(q=p, k_tree=p, v_tree=p, k_cache=p, v_cache=p, prefix_len=p,
+                            mask=None, out=p, parents=None)
+    assert L.tv_tree_attention(ctypes.byref(d), ctypes.byref(ptrs), ctypes.c_void_p(p), 1 << 20,
+                               None, None) == 1
+    ptrs.mask, ptrs.parents = p, p
+    assert L.tv_tree_attention(ctypes.byref(d), ctypes.byref(ptrs), ctypes.c_void_p(p), 1 << 20,
+                               None, None) == 2

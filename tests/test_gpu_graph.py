@@ -37,17 +37,25 @@ class _Step:
         self.ws_acc = torch.empty(binding.accept_workspace_size(b, n, wl.vocab), dtype=torch.uint8,
                                   device=dev)
 
+    fused = False
+
     def run(self):
         dw, wl = self.dw, self.dw.wl
         b, n = wl.parents.shape
-        st = binding.lib().tv_build_tree_mask(binding._ptr(dw.parents), b, n,
-                                              binding._ptr(self.mask), None,
-                                              binding._ptr(self.err),
-                                              binding._stream(dw.q.device))
-        assert st == 0
-        binding.tree_attention(dw.q, dw.k_cache, dw.v_cache, dw.k_tree, dw.v_tree, dw.prefix_len,
-                               self.mask, max_prefix_len=wl.max_prefix_len, out=self.out,
-                               workspace=self.ws_attn, dev_err=self.err)
+        if self.fused:   # the attention builds and writes the mask itself
+            binding.tree_attention(dw.q, dw.k_cache, dw.v_cache, dw.k_tree, dw.v_tree,
+                                   dw.prefix_len, None, max_prefix_len=wl.max_prefix_len,
+                                   out=self.out, workspace=self.ws_attn, dev_err=self.err,
+                                   parents=dw.parents, mask_out=self.mask)
+        else:
+            st = binding.lib().tv_build_tree_mask(binding._ptr(dw.parents), b, n,
+                                                  binding._ptr(self.mask), None,
+                                                  binding._ptr(self.err),
+                                                  binding._stream(dw.q.device))
+            assert st == 0
+            binding.tree_attention(dw.q, dw.k_cache, dw.v_cache, dw.k_tree, dw.v_tree,
+                                   dw.prefix_len, self.mask, max_prefix_len=wl.max_prefix_len,
+                                   out=self.out, workspace=self.ws_attn, dev_err=self.err)
         binding.greedy_accept(dw.logits, dw.parents, dw.draft, workspace=self.ws_acc,
                               dev_err=self.err, outputs=self.acc)
         binding.commit_kv(dw.k_tree, dw.v_tree, self.acc[2], self.acc[1], dw.prefix_len,
@@ -64,11 +72,13 @@ class _Step:
             t.fill_(-7)
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("name", ["8b_layer", "batched"])
-def test_step_graph_replays_match_eager(name):
-    print(f"[graph] {name} step capture and replay", flush=True)
+def test_step_graph_replays_match_eager(name, fused):
+    print(f"[graph] {name} step capture and replay (mask fused: {fused})", flush=True)
     wl = W.make_workload(name)
     eager, graphed = _Step(wl), _Step(wl)
+    eager.fused = graphed.fused = fused
     eager.run()
     torch.cuda.synchronize()
     ref = [t.clone() for t in eager.results()]

@@ -440,3 +440,58 @@ def test_attention_first_block_invalid_then_valid():
     ref, _ = oracle_attention(wl, partial=True)
     check_attention_close(out, ref, "first-block-invalid")
     assert int(err.item()) & binding.DERR_BAD_BLOCK
+
+
+# ---------------------------------------------------------------------------
+# a1 fused into a2/a3: the mask built by the attention's tree workgroups
+# ---------------------------------------------------------------------------
+
+def _fused_vs_standalone(dw, partial, parents=None, label=""):
+    wl = dw.wl
+    par = dw.parents if parents is None else parents
+    err1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    mask, depth = binding.build_tree_mask(par, dev_err=err1)
+    ref = dw.attention(mask, partial=partial)
+    b, n = par.shape
+    mask_out = torch.full((b, n, (n + 31) // 32), -5, dtype=torch.int32, device="cuda")
+    depth_out = torch.full((b, n), -5, dtype=torch.int32, device="cuda")
+    err2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = binding.tree_attention(
+        dw.q, dw.k_cache, dw.v_cache, dw.k_tree, dw.v_tree, dw.prefix_len, None,
+        max_prefix_len=wl.max_prefix_len, block_idx=dw.block_idx if partial else None,
+        n_blocks=dw.n_blocks if partial else None, block_size=wl.block_size if partial else 0,
+        parents=par, mask_out=mask_out, depth_out=depth_out, dev_err=err2)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"{label}: outputs differ"
+    assert torch.equal(mask_out, mask), f"{label}: mask_out differs"
+    assert torch.equal(depth_out, depth), f"{label}: depth_out differs"
+    assert int(err1.item()) == int(err2.item())
+    return int(err2.item())
+
+
+@pytest.mark.parametrize("name", NAMED)
+def test_fused_mask_matches_standalone(workloads, name):
+    _say(f"[fused mask] {name}")
+    dw = workloads(name)
+    assert _fused_vs_standalone(dw, False, label=name) == 0
+    if dw.wl.block_idx is not None:
+        assert _fused_vs_standalone(dw, True, label=name + " partial") == 0
+
+
+def test_fused_mask_rectifying_tree_two_row_groups():
+    # 81 nodes x 4 heads = 324 rows: two row groups of the attention grid
+    _say("[fused mask] 81-node tree, two row groups")
+    wl = W.make_random_case(31, batch=2, n_nodes=81, hq=8, hkv=2, d=128,
+                            prefix_lens=[700, 1300], tree="random")
+    assert _fused_vs_standalone(DevWorkload(wl), False, label="81 nodes") == 0
+
+
+def test_fused_mask_malformed_tree_fallback():
+    _say("[fused mask] malformed tree")
+    wl = W.make_random_case(32, batch=3, n_nodes=20, hq=4, hkv=2, d=64,
+                            prefix_lens=[100, 50, 77])
+    dw = DevWorkload(wl)
+    bad = wl.parents.copy()
+    bad[1, 7] = 9
+    err = _fused_vs_standalone(dw, False, parents=dev_i32(bad), label="malformed")
+    assert err & binding.DERR_BAD_PARENT

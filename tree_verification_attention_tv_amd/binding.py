@@ -48,6 +48,8 @@ class AttnPtrs(ctypes.Structure):
         ("prefix_len", ctypes.c_void_p), ("mask", ctypes.c_void_p),
         ("block_idx", ctypes.c_void_p), ("n_blocks", ctypes.c_void_p),
         ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("parents", ctypes.c_void_p), ("mask_out", ctypes.c_void_p),
+        ("depth_out", ctypes.c_void_p),
     ]
 
 
@@ -218,8 +220,11 @@ def attention_num_splits(desc: AttnDesc) -> int:
 def tree_attention(q, k_cache, v_cache, k_tree, v_tree, prefix_len, mask, *, max_prefix_len,
                    block_idx=None, n_blocks=None, block_size=0, scale=0.0, num_splits=0,
                    tree_placement=TREE_AUTO,
-                   want_lse=False, out=None, lse=None, workspace=None, dev_err=None):
-    """bf16 tree-masked GQA attention.  Returns out (and lse if asked)."""
+                   want_lse=False, out=None, lse=None, workspace=None, dev_err=None,
+                   parents=None, mask_out=None, depth_out=None):
+    """bf16 tree-masked GQA attention.  Returns out (and lse if asked).
+    With mask=None and ``parents`` given, the kernel builds the tree mask
+    itself and writes it to ``mask_out`` / ``depth_out`` when given."""
     bf = torch.bfloat16
     _on_gpu("q", q, bf)
     _on_gpu("k_cache", k_cache, bf)
@@ -227,7 +232,15 @@ def tree_attention(q, k_cache, v_cache, k_tree, v_tree, prefix_len, mask, *, max
     _on_gpu("k_tree", k_tree, bf)
     _on_gpu("v_tree", v_tree, bf)
     _on_gpu("prefix_len", prefix_len, torch.int32)
-    _on_gpu("mask", mask, torch.int32)
+    if (mask is None) == (parents is None):
+        raise ValueError("give exactly one of mask and parents")
+    if mask is not None:
+        _on_gpu("mask", mask, torch.int32)
+    else:
+        _on_gpu("parents", parents, torch.int32)
+        for name, t in (("mask_out", mask_out), ("depth_out", depth_out)):
+            if t is not None:
+                _on_gpu(name, t, torch.int32)
     if v_cache.shape != k_cache.shape or v_cache.stride() != k_cache.stride():
         raise ValueError("k_cache and v_cache must have the same shape and strides")
     partial = block_idx is not None
@@ -249,10 +262,14 @@ def tree_attention(q, k_cache, v_cache, k_tree, v_tree, prefix_len, mask, *, max
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ptrs = AttnPtrs(q=q.data_ptr(), k_tree=k_tree.data_ptr(), v_tree=v_tree.data_ptr(),
                     k_cache=k_cache.data_ptr(), v_cache=v_cache.data_ptr(),
-                    prefix_len=prefix_len.data_ptr(), mask=mask.data_ptr(),
+                    prefix_len=prefix_len.data_ptr(),
+                    mask=mask.data_ptr() if mask is not None else None,
                     block_idx=block_idx.data_ptr() if partial else None,
                     n_blocks=n_blocks.data_ptr() if partial else None,
-                    out=out.data_ptr(), lse=lse.data_ptr() if lse is not None else None)
+                    out=out.data_ptr(), lse=lse.data_ptr() if lse is not None else None,
+                    parents=parents.data_ptr() if parents is not None else None,
+                    mask_out=mask_out.data_ptr() if mask_out is not None else None,
+                    depth_out=depth_out.data_ptr() if depth_out is not None else None)
     _check("tv_tree_attention", lib().tv_tree_attention(
         ctypes.byref(desc), ctypes.byref(ptrs), _ptr(workspace), workspace.numel(),
         _err_ptr(dev_err), _stream(q.device)))

@@ -36,16 +36,43 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
-__device__ __forceinline__ ValIdx wave_argmax(ValIdx a) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(a.v, off);
-    const int oi = __shfl_xor(a.i, off);
-    if (better(ov, oi, a.v, a.i)) {
-      a.v = ov;
-      a.i = oi;
-    }
+template <int CTRL>
+__device__ __forceinline__ void dpp_take(ValIdx& a) {
+  // row rotation: every lane of a 16-lane row sees another lane of the row
+  const float ov = __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(a.v), __float_as_int(a.v), CTRL, 0xF, 0xF, false));
+  const int oi = __builtin_amdgcn_update_dpp(a.i, a.i, CTRL, 0xF, 0xF, false);
+  if (better(ov, oi, a.v, a.i)) {
+    a.v = ov;
+    a.i = oi;
   }
+}
+
+__device__ __forceinline__ void swap_take16(ValIdx& a) {
+  const auto v = __builtin_amdgcn_permlane16_swap(__float_as_uint(a.v), __float_as_uint(a.v), false, false);
+  const auto i = __builtin_amdgcn_permlane16_swap((unsigned)a.i, (unsigned)a.i, false, false);
+  // each lane now holds its own value and its partner row's in (v[0], v[1])
+  ValIdx x{__uint_as_float(v[0]), (int)i[0]}, y{__uint_as_float(v[1]), (int)i[1]};
+  a = better(y.v, y.i, x.v, x.i) ? y : x;
+}
+
+__device__ __forceinline__ void swap_take32(ValIdx& a) {
+  const auto v = __builtin_amdgcn_permlane32_swap(__float_as_uint(a.v), __float_as_uint(a.v), false, false);
+  const auto i = __builtin_amdgcn_permlane32_swap((unsigned)a.i, (unsigned)a.i, false, false);
+  ValIdx x{__uint_as_float(v[0]), (int)i[0]}, y{__uint_as_float(v[1]), (int)i[1]};
+  a = better(y.v, y.i, x.v, x.i) ? y : x;
+}
+
+// every lane gets the wave's (largest value, smallest index) pair: row
+// rotations by 8, 4, 2, 1 (DPP), then the gfx950 row swaps across rows.
+// The order is total, so the result does not depend on the combining order.
+__device__ __forceinline__ ValIdx wave_argmax(ValIdx a) {
+  dpp_take<0x128>(a);
+  dpp_take<0x124>(a);
+  dpp_take<0x122>(a);
+  dpp_take<0x121>(a);
+  swap_take16(a);
+  swap_take32(a);
   return a;
 }
 

@@ -115,9 +115,11 @@ tv_status tv_tree_attention(const tv_attn_desc* desc, const tv_attn_ptrs* ptrs, 
   if (st != TV_OK) return st;
   if (!ptrs) return TV_ERR_NULL;
   const tv_attn_ptrs& p = *ptrs;
-  if (!p.q || !p.k_tree || !p.v_tree || !p.k_cache || !p.v_cache || !p.prefix_len || !p.mask ||
-      !p.out || !workspace)
+  if (!p.q || !p.k_tree || !p.v_tree || !p.k_cache || !p.v_cache || !p.prefix_len || !p.out ||
+      !workspace)
     return TV_ERR_NULL;
+  if (!p.mask && !p.parents) return TV_ERR_NULL;
+  if (p.mask && p.parents) return TV_ERR_SHAPE;
   if (desc->max_blocks > 0 && (!p.block_idx || !p.n_blocks)) return TV_ERR_NULL;
   if (!aligned(p.q, 16) || !aligned(p.k_tree, 16) || !aligned(p.v_tree, 16) ||
       !aligned(p.k_cache, 16) || !aligned(p.v_cache, 16) || !aligned(p.out, 16))

@@ -69,7 +69,10 @@ struct AttnArgs {
   const bf16* k_cache;
   const bf16* v_cache;
   const int32_t* prefix_len;
-  const uint32_t* mask;
+  const uint32_t* mask;      // null: built from `parents` by the tree workgroups
+  const int32_t* parents;    // [batch][n] when mask is null
+  uint32_t* mask_out;        // optional outputs of the in-kernel build (as tv_build_tree_mask)
+  int32_t* depth_out;
   const int32_t* block_idx;
   const int32_t* n_blocks;
   bf16* part_o;     // [batch][nparts][hkv][rows][D], normalised by the row's own sum
@@ -181,7 +184,8 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
   __shared__ __attribute__((aligned(1024))) char ring[kRing * SLOT_B];
   __shared__ uint32_t smask[TV_MAX_NODES * (TV_MAX_NODES / 32)];  // tree rows of this WG
   __shared__ int sblk[kBlkCache];                                 // partial: block ids
-  __shared__ int s_first;
+  __shared__ int s_par[TV_MAX_NODES];                             // parents (in-kernel mask)
+  __shared__ int s_first, s_bad;
 
   const int s = blockIdx.x;
   const int g = blockIdx.y / a.row_groups;
@@ -218,13 +222,16 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
   const int node1 = min(a.n, (wg_row0 + 16 * kWaves * RB + a.grp - 1) / a.grp);
   const int mcnt = (node1 - node0) * a.words;
   uint32_t mw[kMaskPer];
-  {
+  int par_t = 0;
+  if (a.mask) {
     const uint32_t* src = a.mask + ((int64_t)b * a.n + node0) * a.words;
 #pragma unroll
     for (int u = 0; u < kMaskPer; ++u) {
       const int k = tid + u * kSplitThreads;
       mw[u] = k < mcnt ? src[k] : 0u;
     }
+  } else if (tid < a.n) {
+    par_t = a.parents[(int64_t)b * a.n + tid];
   }
 
   int err = 0;
@@ -262,12 +269,42 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
   // ---- per-split tables staged in LDS --------------------------------------
   int bi0 = 0;         // partial: first block index of the split
   int fb_row = begin;  // a valid prefix row of this split (stands in for empty slots)
-  if (has_tree) {
+  if (has_tree && a.mask) {
 #pragma unroll
     for (int u = 0; u < kMaskPer; ++u) {
       const int k = tid + u * kSplitThreads;
       if (k < mcnt) smask[k] = mw[u];
     }
+  } else if (has_tree) {
+    // The mask from the parent array (SpecBlock App. A.2: a node sees its
+    // ancestors and itself), the rule tv_build_tree_mask applies: a malformed
+    // array gives self-only rows and depth 0.  Thread t owns node t's row.
+    if (tid == 0) s_bad = 0;
+    if (tid < a.n) s_par[tid] = par_t;
+    __syncthreads();
+    if (tid < a.n && !(tid == 0 ? par_t == -1 : (par_t >= 0 && par_t < tid))) s_bad = 1;
+    __syncthreads();
+    const bool bad = s_bad != 0;
+    // KV head 0 writes the a1 outputs: each row group its own nodes
+    const bool writer = g == 0 && (a.mask_out || a.depth_out);
+    if (tid >= node0 && tid < node1) {
+      uint32_t* row = &smask[(tid - node0) * a.words];
+      for (int w = 0; w < a.words; ++w) row[w] = 0u;
+      row[tid >> 5] |= 1u << (tid & 31);
+      int depth = 0;
+      if (!bad)
+        for (int j = s_par[tid]; j >= 0; j = s_par[j]) {
+          row[j >> 5] |= 1u << (j & 31);
+          ++depth;
+        }
+      if (writer) {
+        if (a.mask_out)
+          for (int w = 0; w < a.words; ++w)
+            a.mask_out[((int64_t)b * a.n + tid) * a.words + w] = row[w];
+        if (a.depth_out) a.depth_out[(int64_t)b * a.n + tid] = depth;
+      }
+    }
+    if (bad && g == 0 && rg == 0 && tid == 0) raise_err(a.dev_err, TV_DERR_BAD_PARENT);
   }
   if (PARTIAL && np > 0) {
     const int32_t* blist = a.block_idx + (int64_t)b * a.max_blocks;
@@ -927,6 +964,9 @@ hipError_t launch_attention(const tv_attn_desc& d, const AttnPlan& plan, const t
   a.v_cache = (const bf16*)p.v_cache;
   a.prefix_len = p.prefix_len;
   a.mask = p.mask;
+  a.parents = p.parents;
+  a.mask_out = p.mask_out;
+  a.depth_out = p.depth_out;
   a.block_idx = p.block_idx;
   a.n_blocks = p.n_blocks;
   a.part_o = reinterpret_cast<bf16*>(workspace);
