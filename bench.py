@@ -3,8 +3,9 @@
 A step is the whole hot path over one batch of synthetic input, back to back
 on one stream: one layer of tree attention over the verified-prefix KV (its
 tree workgroups build the tree mask from the parent array and write it out),
-greedy acceptance over the vocabulary, KV commit.  The standalone mask call
-is timed on its own in `call_us`.
+then greedy acceptance over the vocabulary with the KV commit of the
+accepted path done by the same walk workgroups.  The standalone mask, accept
+and commit calls are timed on their own in `call_us`.
 Default workload: the 8B-layer shape (batch 1, 32 query / 8 KV heads of 128,
 1000-token prefix, 60-node EAGLE-style tree, 128256-token bf16 logits).
 
@@ -234,6 +235,13 @@ class StepRunner:
                                        workspace=self.ws_sto, dev_err=self.err,
                                        outputs=self.sto_out)
 
+    def k_accept_commit(self, s):
+        # acceptance, and the commit of its path by the same walk workgroups
+        self.binding.greedy_accept_commit(s.logits, s.parents, s.draft, s.k_tree, s.v_tree,
+                                          s.prefix_len, s.k_cache, s.v_cache,
+                                          new_prefix_len=s.new_prefix, workspace=self.ws_acc,
+                                          dev_err=self.err, outputs=self.acc_out)
+
     def k_commit(self, s):
         self.binding.commit_kv(s.k_tree, s.v_tree, self.acc_out[2], self.acc_out[1], s.prefix_len,
                                s.k_cache, s.v_cache, new_prefix_len=s.new_prefix,
@@ -243,8 +251,7 @@ class StepRunner:
         if self.specpv:
             self.k_select(s)
         self.k_attn(s)
-        self.k_accept(s)
-        self.k_commit(s)
+        self.k_accept_commit(s)
         if self.specpv:
             self.k_summ_update(s)
 
@@ -372,7 +379,7 @@ def measure(wl, partial, steps, warmup, warm, num_splits, dev, graph=True, specp
     # also measure the host's launch rate)
     tm = r.timed_graph if graph else (lambda fn, **kw: r.timed(fn, max(steps, 50)))
     calls = {"mask": tm(r.k_mask), "attention": tm(r.k_attn), "accept": tm(r.k_accept),
-             "commit": tm(r.k_commit)}
+             "commit": tm(r.k_commit), "accept_commit": tm(r.k_accept_commit)}
     if not specpv and not partial:
         calls["accept_stochastic"] = tm(r.k_accept_stochastic)
     if specpv:

@@ -214,6 +214,28 @@ tv_status tv_greedy_accept(const void* logits, tv_dtype dtype, int64_t vocab, in
                            size_t workspace_bytes, int32_t* dev_err, hipStream_t stream);
 
 /*
+ * tv_greedy_accept_commit -- tv_greedy_accept followed by tv_commit_kv of
+ * its path, in one call: the workgroup that walks a sequence's tree also
+ * copies the accepted rows into the cache (SpecBlock App. A.5: the longest
+ * accepted prefix is committed before the next iteration).
+ *
+ * Outputs, cache contents, new_prefix_len, device error bits and fallbacks
+ * are exactly those of the two calls made in a row with the same arguments
+ * (tv_greedy_accept's workspace size applies).  new_prefix_len may alias
+ * prefix_len.
+ */
+tv_status tv_greedy_accept_commit(const void* logits, tv_dtype dtype, int64_t vocab,
+                                  int64_t row_stride, const int32_t* parents,
+                                  const int32_t* draft_tokens, int32_t batch, int32_t n_nodes,
+                                  int32_t* target_argmax, int32_t* accept_len,
+                                  int32_t* accept_path, int32_t* bonus_token, void* workspace,
+                                  size_t workspace_bytes, const void* k_tree, const void* v_tree,
+                                  const int32_t* prefix_len, int32_t* new_prefix_len,
+                                  void* k_cache, void* v_cache, int64_t cache_seq_stride,
+                                  int32_t cache_capacity, int32_t n_kv_heads, int32_t head_dim,
+                                  int32_t* dev_err, hipStream_t stream);
+
+/*
  * tv_stochastic_accept -- acceptance at temperature T > 0 (sampling).
  *
  * Sources: SpecPV Sec. 2 "Related Work" (speculative sampling is equivalent

@@ -56,11 +56,17 @@ class _Step:
             binding.tree_attention(dw.q, dw.k_cache, dw.v_cache, dw.k_tree, dw.v_tree,
                                    dw.prefix_len, self.mask, max_prefix_len=wl.max_prefix_len,
                                    out=self.out, workspace=self.ws_attn, dev_err=self.err)
-        binding.greedy_accept(dw.logits, dw.parents, dw.draft, workspace=self.ws_acc,
-                              dev_err=self.err, outputs=self.acc)
-        binding.commit_kv(dw.k_tree, dw.v_tree, self.acc[2], self.acc[1], dw.prefix_len,
-                          dw.k_cache, dw.v_cache, new_prefix_len=self.new_prefix,
-                          dev_err=self.err)
+        if self.fused:   # acceptance and the commit of its path in one call
+            binding.greedy_accept_commit(dw.logits, dw.parents, dw.draft, dw.k_tree, dw.v_tree,
+                                         dw.prefix_len, dw.k_cache, dw.v_cache,
+                                         new_prefix_len=self.new_prefix, workspace=self.ws_acc,
+                                         dev_err=self.err, outputs=self.acc)
+        else:
+            binding.greedy_accept(dw.logits, dw.parents, dw.draft, workspace=self.ws_acc,
+                                  dev_err=self.err, outputs=self.acc)
+            binding.commit_kv(dw.k_tree, dw.v_tree, self.acc[2], self.acc[1], dw.prefix_len,
+                              dw.k_cache, dw.v_cache, new_prefix_len=self.new_prefix,
+                              dev_err=self.err)
 
     def results(self):
         return [self.mask, self.out.view(torch.int16), *self.acc, self.new_prefix,
@@ -75,7 +81,8 @@ class _Step:
 @pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("name", ["8b_layer", "batched"])
 def test_step_graph_replays_match_eager(name, fused):
-    print(f"[graph] {name} step capture and replay (mask fused: {fused})", flush=True)
+    print(f"[graph] {name} step capture and replay (mask and commit fused: {fused})",
+          flush=True)
     wl = W.make_workload(name)
     eager, graphed = _Step(wl), _Step(wl)
     eager.fused = graphed.fused = fused

@@ -495,3 +495,53 @@ def test_fused_mask_malformed_tree_fallback():
     bad[1, 7] = 9
     err = _fused_vs_standalone(dw, False, parents=dev_i32(bad), label="malformed")
     assert err & binding.DERR_BAD_PARENT
+
+
+# ---------------------------------------------------------------------------
+# a6 + a7 in one call: the walk workgroup commits the accepted rows
+# ---------------------------------------------------------------------------
+
+def _accept_commit_vs_two_calls(dw, prefix=None, parents=None, alias=False, label=""):
+    wl = dw.wl
+    par = dw.parents if parents is None else parents
+    pre = dw.prefix_len if prefix is None else prefix
+    kc1, vc1 = dw.k_cache.clone(), dw.v_cache.clone()
+    kc2, vc2 = dw.k_cache.clone(), dw.v_cache.clone()
+    e1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    e2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    amax, alen, path, bonus = binding.greedy_accept(dw.logits, par, dw.draft, dev_err=e1)
+    newp1 = binding.commit_kv(dw.k_tree, dw.v_tree, path, alen, pre, kc1, vc1, dev_err=e1)
+    pre2 = pre.clone()
+    got = binding.greedy_accept_commit(dw.logits, par, dw.draft, dw.k_tree, dw.v_tree, pre2, kc2,
+                                       vc2, new_prefix_len=pre2 if alias else None, dev_err=e2)
+    torch.cuda.synchronize()
+    for k, (x, y) in enumerate(zip(got[:4], (amax, alen, path, bonus))):
+        assert torch.equal(x, y), f"{label}: acceptance output {k} differs"
+    assert torch.equal(got[4], newp1), f"{label}: new prefix differs"
+    assert torch.equal(kc1.view(torch.int16), kc2.view(torch.int16)), f"{label}: K cache differs"
+    assert torch.equal(vc1.view(torch.int16), vc2.view(torch.int16)), f"{label}: V cache differs"
+    assert int(e1.item()) == int(e2.item()), f"{label}: error bits differ"
+    return int(e2.item())
+
+
+@pytest.mark.parametrize("name", NAMED)
+def test_accept_commit_matches_two_calls(workloads, name):
+    _say(f"[accept+commit] {name}")
+    assert _accept_commit_vs_two_calls(workloads(name), label=name) == 0
+
+
+def test_accept_commit_edge_cases(workloads):
+    _say("[accept+commit] aliasing, overflow, bad prefix, malformed tree")
+    dw = workloads("batched")
+    wl = dw.wl
+    assert _accept_commit_vs_two_calls(dw, alias=True, label="alias") == 0
+    cap = wl.capacity
+    full = dev_i32([cap - 1] + [int(x) for x in wl.prefix_len[1:]])
+    assert _accept_commit_vs_two_calls(dw, prefix=full, label="overflow") & binding.DERR_CAPACITY
+    badp = dev_i32([-3] + [int(x) for x in wl.prefix_len[1:]])
+    assert _accept_commit_vs_two_calls(dw, prefix=badp, label="bad prefix") & \
+        binding.DERR_BAD_PREFIX
+    par = wl.parents.copy()
+    par[2, 5] = 17
+    assert _accept_commit_vs_two_calls(dw, parents=dev_i32(par), label="malformed") & \
+        binding.DERR_BAD_PARENT

@@ -117,6 +117,10 @@ def lib() -> ctypes.CDLL:
             L.tv_specpv_needs_rectification.restype = i32
             L.tv_specpv_rectify_tree.argtypes = [vp, i32, i32, vp, vp, i32, vp, vp]
             L.tv_specpv_rectify_tree.restype = i32
+            L.tv_greedy_accept_commit.argtypes = [vp, i32, i64, i64, vp, vp, i32, i32, vp, vp,
+                                                  vp, vp, vp, sz, vp, vp, vp, vp, vp, vp, i64,
+                                                  i32, i32, i32, vp, vp]
+            L.tv_greedy_accept_commit.restype = i32
             L.tv_stochastic_accept_workspace_size.argtypes = [i32, i32, i64]
             L.tv_stochastic_accept_workspace_size.restype = sz
             L.tv_stochastic_accept.argtypes = [vp, i32, i64, i64, vp, vp, i32, i32,
@@ -310,6 +314,50 @@ def greedy_accept(logits, parents, draft_tokens, *, vocab=None, workspace=None, 
         _ptr(amax), _ptr(alen), _ptr(path), _ptr(bonus), _ptr(workspace), workspace.numel(),
         _err_ptr(dev_err), _stream(dev)))
     return amax, alen, path, bonus
+
+
+def greedy_accept_commit(logits, parents, draft_tokens, k_tree, v_tree, prefix_len, k_cache,
+                         v_cache, *, new_prefix_len=None, vocab=None, workspace=None,
+                         dev_err=None, outputs=None):
+    """tv_greedy_accept then tv_commit_kv of its path, in one call.  Returns
+    (target_argmax, accept_len, accept_path, bonus, new_prefix_len)."""
+    _on_gpu("logits", logits, (torch.bfloat16, torch.float32), contiguous=False)
+    _on_gpu("parents", parents, torch.int32)
+    _on_gpu("draft_tokens", draft_tokens, torch.int32)
+    for name, t in (("k_tree", k_tree), ("v_tree", v_tree)):
+        _on_gpu(name, t, torch.bfloat16)
+    _on_gpu("k_cache", k_cache, torch.bfloat16, contiguous=False)
+    _on_gpu("v_cache", v_cache, torch.bfloat16, contiguous=False)
+    _on_gpu("prefix_len", prefix_len, torch.int32)
+    bsz, n = parents.shape
+    if logits.shape[:2] != (bsz, n) or logits.stride(2) != 1 or \
+            (bsz > 1 and logits.stride(0) != n * logits.stride(1)):
+        raise ValueError("logits must be [B][N][V] with unit vocab stride and uniform row stride")
+    _, hkv, cap, d = k_cache.shape
+    if k_cache.stride()[1:] != (cap * d, d, 1) or v_cache.stride() != k_cache.stride():
+        raise ValueError("caches must be [B][Hkv][cap][D] with contiguous rows per sequence")
+    v = logits.shape[2] if vocab is None else int(vocab)
+    dt = TV_BF16 if logits.dtype == torch.bfloat16 else TV_F32
+    dev = parents.device
+    if outputs is None:
+        outputs = (torch.empty((bsz, n), dtype=torch.int32, device=dev),
+                   torch.empty((bsz,), dtype=torch.int32, device=dev),
+                   torch.empty((bsz, n), dtype=torch.int32, device=dev),
+                   torch.empty((bsz,), dtype=torch.int32, device=dev))
+    amax, alen, path, bonus = outputs
+    if new_prefix_len is None:
+        new_prefix_len = torch.empty_like(prefix_len)
+    ws_bytes = accept_workspace_size(bsz, n, v)
+    if ws_bytes == 0:
+        raise TVError("tv_greedy_accept_workspace_size", 2)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    _check("tv_greedy_accept_commit", lib().tv_greedy_accept_commit(
+        _ptr(logits), dt, v, int(logits.stride(1)), _ptr(parents), _ptr(draft_tokens), bsz, n,
+        _ptr(amax), _ptr(alen), _ptr(path), _ptr(bonus), _ptr(workspace), workspace.numel(),
+        _ptr(k_tree), _ptr(v_tree), _ptr(prefix_len), _ptr(new_prefix_len), _ptr(k_cache),
+        _ptr(v_cache), int(k_cache.stride(0)), cap, hkv, d, _err_ptr(dev_err), _stream(dev)))
+    return amax, alen, path, bonus, new_prefix_len
 
 
 def stochastic_accept_workspace_size(batch, n_nodes, vocab) -> int:

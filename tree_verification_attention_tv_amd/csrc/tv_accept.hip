@@ -27,6 +27,18 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kUnroll = 8;  // 16-byte bf16 vectors per thread per chunk (fp32: twice as many)
 
+// Optional commit done by the walk (tv_greedy_accept_commit); k_cache == null: none
+struct CommitArgs {
+  const uint4* k_tree;
+  const uint4* v_tree;
+  const int32_t* prefix_len;
+  int32_t* new_prefix_len;
+  uint4* k_cache;
+  uint4* v_cache;
+  int64_t seq_stride_vec;
+  int cap, hkv, vec_per_row;
+};
+
 struct ValIdx {
   float v;
   int i;
@@ -163,8 +175,11 @@ __global__ __launch_bounds__(kThreads) void path_walk_kernel(
     const float* __restrict__ part_v, const int* __restrict__ part_i, int chunks,
     const int32_t* __restrict__ parents, const int32_t* __restrict__ draft, int n,
     int32_t* __restrict__ target_argmax, int32_t* __restrict__ accept_len,
-    int32_t* __restrict__ accept_path, int32_t* __restrict__ bonus, int32_t* __restrict__ dev_err) {
+    int32_t* __restrict__ accept_path, int32_t* __restrict__ bonus, int32_t* __restrict__ dev_err,
+    CommitArgs cm) {
   __shared__ int par[TV_MAX_NODES];
+  __shared__ int s_path[TV_MAX_NODES];
+  __shared__ int s_prefix, s_ok;
   __shared__ int amax[TV_MAX_NODES];
   __shared__ int dtok[TV_MAX_NODES];
   __shared__ int bad;
@@ -240,12 +255,49 @@ __global__ __launch_bounds__(kThreads) void path_walk_kernel(
     int j = end_node;
     for (int k = depth; k >= 0; --k) {
       path[k] = j;
+      s_path[k] = j;
       j = par[j];
     }
     accept_len[b] = depth;
     bonus[b] = amax[end_node];
     if (bad) raise_err(dev_err, TV_DERR_BAD_PARENT);
+    if (cm.k_cache) {
+      // the commit's checks (tv_commit_kv): the path is valid by construction
+      const int p = cm.prefix_len[b];
+      int ok = 1;
+      if (p < 0 || p > cm.cap) {
+        raise_err(dev_err, TV_DERR_BAD_PREFIX);
+        ok = 0;
+      } else if ((int64_t)p + depth + 1 > cm.cap) {
+        raise_err(dev_err, TV_DERR_CAPACITY);
+        ok = 0;
+      }
+      s_prefix = p;
+      s_ok = ok;
+    }
   }
+  if (!cm.k_cache) return;
+  __syncthreads();
+  // copy the accepted nodes' K/V rows into the cache, 16 bytes per item
+  const int p = s_prefix;
+  if (s_ok) {
+    const int per_row = cm.vec_per_row, hkv = cm.hkv;
+    const int items = (depth + 1) * hkv * per_row;
+    const uint4* __restrict__ kt = cm.k_tree + (int64_t)b * n * hkv * per_row;
+    const uint4* __restrict__ vt = cm.v_tree + (int64_t)b * n * hkv * per_row;
+    uint4* __restrict__ kc = cm.k_cache + b * cm.seq_stride_vec;
+    uint4* __restrict__ vc = cm.v_cache + b * cm.seq_stride_vec;
+#pragma unroll 4
+    for (int it = i; it < items; it += kThreads) {
+      const int c = it % per_row, rh = it / per_row;
+      const int h = rh % hkv, r = rh / hkv;
+      const int64_t src = ((int64_t)s_path[r] * hkv + h) * per_row + c;
+      const int64_t dst = ((int64_t)h * cm.cap + p + r) * per_row + c;
+      kc[dst] = kt[src];
+      vc[dst] = vt[src];
+    }
+  }
+  if (i == 0) cm.new_prefix_len[b] = s_ok ? p + depth + 1 : p;
 }
 
 }  // namespace
@@ -269,7 +321,7 @@ hipError_t launch_accept(const void* logits, tv_dtype dt, int64_t vocab, int64_t
                          const int32_t* parents, const int32_t* draft, int batch, int n,
                          int32_t* target_argmax, int32_t* accept_len, int32_t* accept_path,
                          int32_t* bonus, void* workspace, const AcceptPlan& plan,
-                         int32_t* dev_err, hipStream_t stream) {
+                         int32_t* dev_err, hipStream_t stream, const CommitTarget* commit) {
   const size_t rows = (size_t)batch * n;
   float* part_v = reinterpret_cast<float*>(workspace);
   int* part_i = reinterpret_cast<int*>(
@@ -299,9 +351,22 @@ hipError_t launch_accept(const void* logits, tv_dtype dt, int64_t vocab, int64_t
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  CommitArgs cm{};
+  if (commit) {
+    cm.k_tree = (const uint4*)commit->k_tree;
+    cm.v_tree = (const uint4*)commit->v_tree;
+    cm.prefix_len = commit->prefix_len;
+    cm.new_prefix_len = commit->new_prefix_len;
+    cm.k_cache = (uint4*)commit->k_cache;
+    cm.v_cache = (uint4*)commit->v_cache;
+    cm.seq_stride_vec = commit->seq_stride / 8;
+    cm.cap = commit->cap;
+    cm.hkv = commit->hkv;
+    cm.vec_per_row = commit->d / 8;
+  }
   hipLaunchKernelGGL(path_walk_kernel, dim3(batch), dim3(kThreads), 0, stream, part_v, part_i,
                      plan.chunks, parents, draft, n, target_argmax, accept_len, accept_path, bonus,
-                     dev_err);
+                     dev_err, cm);
   return hipGetLastError();
 }
 

@@ -158,6 +158,41 @@ tv_status tv_greedy_accept(const void* logits, tv_dtype dtype, int64_t vocab, in
                                          bonus_token, workspace, plan, dev_err, stream));
 }
 
+tv_status tv_greedy_accept_commit(const void* logits, tv_dtype dtype, int64_t vocab,
+                                  int64_t row_stride, const int32_t* parents,
+                                  const int32_t* draft_tokens, int32_t batch, int32_t n_nodes,
+                                  int32_t* target_argmax, int32_t* accept_len,
+                                  int32_t* accept_path, int32_t* bonus_token, void* workspace,
+                                  size_t workspace_bytes, const void* k_tree, const void* v_tree,
+                                  const int32_t* prefix_len, int32_t* new_prefix_len,
+                                  void* k_cache, void* v_cache, int64_t cache_seq_stride,
+                                  int32_t cache_capacity, int32_t n_kv_heads, int32_t head_dim,
+                                  int32_t* dev_err, hipStream_t stream) {
+  if (!logits || !parents || !draft_tokens || !target_argmax || !accept_len || !accept_path ||
+      !bonus_token || !workspace || !k_tree || !v_tree || !prefix_len || !new_prefix_len ||
+      !k_cache || !v_cache)
+    return TV_ERR_NULL;
+  if (dtype != TV_BF16 && dtype != TV_F32) return TV_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return TV_ERR_UNSUPPORTED;
+  if (batch < 0 || n_nodes < 1 || n_nodes > TV_MAX_NODES || n_kv_heads < 1 || cache_capacity < 0)
+    return TV_ERR_SHAPE;
+  if (vocab < 1 || vocab >= INT_MAX || row_stride < vocab) return TV_ERR_SHAPE;
+  const int64_t min_stride = (int64_t)n_kv_heads * cache_capacity * head_dim;
+  if (cache_seq_stride == 0) cache_seq_stride = min_stride;
+  if (cache_seq_stride < min_stride || cache_seq_stride % 8) return TV_ERR_SHAPE;
+  if (!aligned(k_tree, 16) || !aligned(v_tree, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16))
+    return TV_ERR_UNSUPPORTED;
+  if (batch == 0) return TV_OK;
+  const tv::AcceptPlan plan = tv::plan_accept(batch, n_nodes, vocab);
+  if (!aligned(workspace, 16) || workspace_bytes < plan.ws_bytes) return TV_ERR_WORKSPACE;
+  const tv::CommitTarget ct{k_tree,  v_tree,           prefix_len,     new_prefix_len, k_cache,
+                            v_cache, cache_seq_stride, cache_capacity, n_kv_heads,     head_dim};
+  return launch_status(tv::launch_accept(logits, dtype, vocab, row_stride, parents, draft_tokens,
+                                         batch, n_nodes, target_argmax, accept_len, accept_path,
+                                         bonus_token, workspace, plan, dev_err, stream, &ct));
+}
+
 size_t tv_stochastic_accept_workspace_size(int32_t batch, int32_t n_nodes, int64_t vocab) {
   if (batch < 0 || n_nodes < 1 || n_nodes > TV_MAX_NODES || vocab < 1 || vocab >= INT_MAX)
     return 0;

@@ -48,11 +48,24 @@ struct AcceptPlan {
 
 AcceptPlan plan_accept(int batch, int n, int64_t vocab);
 
+// commit of the accepted rows folded into the acceptance's walk kernel
+struct CommitTarget {
+  const void* k_tree;
+  const void* v_tree;
+  const int32_t* prefix_len;
+  int32_t* new_prefix_len;
+  void* k_cache;
+  void* v_cache;
+  int64_t seq_stride;  // elements
+  int cap, hkv, d;
+};
+
 hipError_t launch_accept(const void* logits, tv_dtype dt, int64_t vocab, int64_t row_stride,
                          const int32_t* parents, const int32_t* draft, int batch, int n,
                          int32_t* target_argmax, int32_t* accept_len, int32_t* accept_path,
                          int32_t* bonus, void* workspace, const AcceptPlan& plan,
-                         int32_t* dev_err, hipStream_t stream);
+                         int32_t* dev_err, hipStream_t stream,
+                         const CommitTarget* commit = nullptr);
 
 hipError_t launch_commit(const void* k_tree, const void* v_tree, const int32_t* path,
                          const int32_t* accept_len, const int32_t* prefix_len,
