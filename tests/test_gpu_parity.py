@@ -545,3 +545,14 @@ def test_accept_commit_edge_cases(workloads):
     par[2, 5] = 17
     assert _accept_commit_vs_two_calls(dw, parents=dev_i32(par), label="malformed") & \
         binding.DERR_BAD_PARENT
+
+
+@pytest.mark.parametrize("case", [c for c in ATTN_CASES if c[0] in (3, 4, 5, 6, 8, 12)],
+                         ids=lambda c: f"case{c[0]}")
+def test_fused_mask_random_cases(case):
+    # 1 to 4 row groups, empty prefixes, partial mode with ragged blocks
+    seed, bsz, n, hq, hkv, d, plens, bs, bps, tree = case
+    _say(f"[fused mask] random case {case}")
+    wl = W.make_random_case(seed, batch=bsz, n_nodes=n, hq=hq, hkv=hkv, d=d, prefix_lens=plens,
+                            block_size=bs, blocks_per_seq=bps, tree=tree)
+    assert _fused_vs_standalone(DevWorkload(wl), bool(bs), label=f"case{seed}") == 0
