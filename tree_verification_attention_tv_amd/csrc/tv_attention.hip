@@ -202,6 +202,83 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
   const bool active = row0 < a.rows;
   const int node0 = wg_row0 / a.grp;
 
+  // ---- sources --------------------------------------------------------------
+  const int begin = s * a.chunk;  // first prefix slot of this split
+  const char* kc = reinterpret_cast<const char*>(a.k_cache + b * a.seq_stride + (int64_t)g * a.cap * D);
+  const char* vc = reinterpret_cast<const char*>(a.v_cache + b * a.seq_stride + (int64_t)g * a.cap * D);
+  const char* kt = reinterpret_cast<const char*>(a.k_tree + ((int64_t)b * a.n * a.hkv + g) * D);
+  const char* vt = reinterpret_cast<const char*>(a.v_tree + ((int64_t)b * a.n * a.hkv + g) * D);
+  const int64_t tree_rowb = (int64_t)a.hkv * ROWB;  // bytes between tree nodes
+
+  // ---- tile layout in LDS and its DMA ------------------------------------
+  // A K (or V) tile is stored as D/16 column blocks of 1 KB; block cb holds
+  // columns 16cb..16cb+15 of the 32 tokens, 32 bytes per token.  The
+  // 16-byte K reads of a wave then cover two contiguous 512-byte runs and
+  // the transposing V reads 128 contiguous bytes per 16 lanes, both at the
+  // full LDS rate on gfx950 (measured: 16-byte reads at ~250 B/clk per CU,
+  // transposing 8-byte reads at ~125), and every operand read is one
+  // per-lane base plus an immediate.  DMA instruction cb of a tensor fills
+  // block cb: lane i writes 16-byte slot i, i.e. token i/2, half i&1.
+  const uint32_t ring_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)ring;
+  const int dtok = lane >> 1;                               // token of this lane's DMA slot
+  const int dhalf = lane & 1;                               // 16-byte half it carries
+  int dt[DPT];        // tensor of the instruction (0 = K, 1 = V)
+  uint32_t ddst[DPT]; // slot-relative LDS byte offset of the instruction
+  uint32_t dcol[DPT]; // byte offset of the lane's 16 bytes within the source row
+#pragma unroll
+  for (int k = 0; k < DPT; ++k) {
+    const int inst = wave * DPT + k;  // 0 .. 2*IPT-1
+    const int cb = inst % IPT;
+    dt[k] = inst / IPT;
+    ddst[k] = dt[k] * TILE_B + cb * 1024;
+    dcol[k] = 16u * (2 * cb + dhalf);
+  }
+  // Whole prefix tiles of full mode read 32 consecutive rows: a scalar base
+  // per tile plus a fixed per-lane offset.
+  uint32_t fvoff[DPT];      // per-lane offset within the tile's rows
+  const char* fbase[DPT];   // source of tile 0 (wave-uniform)
+  uint32_t fdst[DPT];       // LDS address in slot 0 (wave-uniform)
+#pragma unroll
+  for (int k = 0; k < DPT; ++k) {
+    fvoff[k] = dtok * ROWB + dcol[k];
+    fbase[k] = (dt[k] ? vc : kc) + (int64_t)begin * ROWB;
+    fdst[k] = __builtin_amdgcn_readfirstlane(ring_base + ddst[k]);
+  }
+
+  // ---- first tiles, requested before the prefix length is known -----------
+  // Their rows do not depend on it: whole prefix tiles below the declared
+  // maximum prefix (full mode), or the tree tiles of a workgroup that holds
+  // only the tree.  They share the memory round trip of the loads below;
+  // once the prefix length is known, the run keeps those that are its own
+  // first tiles (all of them unless the prefix is shorter than the maximum)
+  // and requests the others again.
+  const bool tree_own = a.tree_sep && s == a.splits;
+  int spec = 0;
+  if (!PARTIAL) {
+    if (tree_own) {
+      spec = min(kRing, (a.n + kTile - 1) / kTile);
+#pragma unroll
+      for (int t = 0; t < kRing; ++t)
+        if (t < spec) {
+          const int64_t off = (int64_t)min(t * kTile + dtok, a.n - 1) * tree_rowb;
+#pragma unroll
+          for (int k = 0; k < DPT; ++k)
+            dma16(__builtin_amdgcn_readfirstlane(ring_base + t * SLOT_B + ddst[k]),
+                  (dt[k] ? vt : kt) + off + dcol[k]);
+        }
+    } else {
+      const int lim = min(begin + a.chunk, a.max_prefix);
+      spec = begin < lim ? min(kRing, (lim - begin) / kTile) : 0;
+#pragma unroll
+      for (int t = 0; t < kRing; ++t)
+        if (t < spec) {
+#pragma unroll
+          for (int k = 0; k < DPT; ++k)
+            dma16s(fdst[k] + t * SLOT_B, fbase[k] + (int64_t)t * (kTile * ROWB), fvoff[k]);
+        }
+    }
+  }
+
   // ---- loads that do not depend on the prefix length ------------------------
   // Issued first so that they share one memory round trip with prefix_len:
   // the Q^T fragments (B operand of S^T = K Q^T) and this workgroup's mask
@@ -237,9 +314,9 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
   int err = 0;
   const int p_len = clamped_prefix(a, b, &err);
   const int slots = prefix_slots(a, b, p_len, &err);
-  // Wait for all of the above here, on every path: the compiler's own wait
-  // would otherwise be placed inside the loop (vmcnt(0), draining the tile
-  // DMA each step).
+  // Wait for all of the above (and the first tiles) here, on every path: the
+  // compiler's own wait would otherwise be placed inside the loop (vmcnt(0),
+  // draining the tile DMA each step).
   __builtin_amdgcn_s_waitcnt(0x0F70);  // gfx9 encoding: vmcnt(0)
   if (err && s == 0 && g == 0 && rg == 0 && tid == 0) raise_err(a.dev_err, err);
   err = 0;
@@ -249,18 +326,10 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
   // last non-empty split (split 0 when the prefix is empty).
   const int ns = (slots + a.chunk - 1) / a.chunk;
   const bool has_tree = a.tree_sep ? s == a.splits : s == max(ns - 1, 0);
-  const int begin = s * a.chunk;
   const int end = min(begin + a.chunk, slots);
   int np = begin < end ? (end - begin + kTile - 1) / kTile : 0;  // prefix tiles
   const int nt = has_tree ? (a.n + kTile - 1) / kTile : 0;       // tree tiles
   if (np == 0 && nt == 0) return;  // uniform over the workgroup
-
-  // ---- sources --------------------------------------------------------------
-  const char* kc = reinterpret_cast<const char*>(a.k_cache + b * a.seq_stride + (int64_t)g * a.cap * D);
-  const char* vc = reinterpret_cast<const char*>(a.v_cache + b * a.seq_stride + (int64_t)g * a.cap * D);
-  const char* kt = reinterpret_cast<const char*>(a.k_tree + ((int64_t)b * a.n * a.hkv + g) * D);
-  const char* vt = reinterpret_cast<const char*>(a.v_tree + ((int64_t)b * a.n * a.hkv + g) * D);
-  const int64_t tree_rowb = (int64_t)a.hkv * ROWB;  // bytes between tree nodes
 
   // partial rows of this (sequence, split, kv head) are consecutive, in row
   // order m = node * grp + head within the group
@@ -338,6 +407,10 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
     }
   }
   const int ntiles = np + nt;
+  // whole prefix tiles (full mode): 32 consecutive rows each
+  const int nfull = PARTIAL ? 0 : (end - begin) / kTile;
+  // requested tiles that are this split's own first tiles
+  const int skip = tree_own ? spec : max(0, min(spec, nfull));
   // cache row of prefix slot u, fb_row when the slot is empty
   auto slot_row = [&](int u, bool& valid) -> int {
     if (u >= end) {
@@ -355,43 +428,8 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
     return valid ? row : fb_row;
   };
 
-  // ---- tile layout in LDS and its DMA ------------------------------------
-  // A K (or V) tile is stored as D/16 column blocks of 1 KB; block cb holds
-  // columns 16cb..16cb+15 of the 32 tokens, 32 bytes per token.  The
-  // 16-byte K reads of a wave then cover two contiguous 512-byte runs and
-  // the transposing V reads 128 contiguous bytes per 16 lanes, both at the
-  // full LDS rate on gfx950 (measured: 16-byte reads at ~250 B/clk per CU,
-  // transposing 8-byte reads at ~125), and every operand read is one
-  // per-lane base plus an immediate.  DMA instruction cb of a tensor fills
-  // block cb: lane i writes 16-byte slot i, i.e. token i/2, half i&1.
-  const uint32_t ring_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)ring;
-  const int dtok = lane >> 1;                               // token of this lane's DMA slot
-  const int dhalf = lane & 1;                               // 16-byte half it carries
-  int dt[DPT];        // tensor of the instruction (0 = K, 1 = V)
-  uint32_t ddst[DPT]; // slot-relative LDS byte offset of the instruction
-  uint32_t dcol[DPT]; // byte offset of the lane's 16 bytes within the source row
-#pragma unroll
-  for (int k = 0; k < DPT; ++k) {
-    const int inst = wave * DPT + k;  // 0 .. 2*IPT-1
-    const int cb = inst % IPT;
-    dt[k] = inst / IPT;
-    ddst[k] = dt[k] * TILE_B + cb * 1024;
-    dcol[k] = 16u * (2 * cb + dhalf);
-  }
-  // Whole prefix tiles of full mode read 32 consecutive rows: a scalar base
-  // per tile plus a fixed per-lane offset.
-  const int nfull = PARTIAL ? 0 : (end - begin) / kTile;
-  uint32_t fvoff[DPT];      // per-lane offset within the tile's rows
-  const char* fbase[DPT];   // source of tile 0 (wave-uniform)
-  uint32_t fdst[DPT];       // LDS address in slot 0 (wave-uniform)
-#pragma unroll
-  for (int k = 0; k < DPT; ++k) {
-    fvoff[k] = dtok * ROWB + dcol[k];
-    fbase[k] = (dt[k] ? vc : kc) + (int64_t)begin * ROWB;
-    fdst[k] = __builtin_amdgcn_readfirstlane(ring_base + ddst[k]);
-  }
-  // Tile it of the split: prefix tiles 0..np-1, then tree tiles.  Tiles past
-  // the end (prefetched, then discarded) re-read the last tree node.
+  // Tile it of the split: prefix tiles 0..np-1, then tree tiles.  Lanes past
+  // the tree's last node re-read that node.
   auto dma_tile = [&](int slot, int it) {
     if (it < nfull) {
 #pragma unroll
@@ -537,31 +575,40 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
   };
 
   // ---- pipeline -------------------------------------------------------------
-  // Tile t lives in ring slot t % 4.  Three tiles are requested before the
-  // loop; step s waits for tile s+1 (the older of its two outstanding
-  // tiles), passes the workgroup barrier (after which the slot of tile s-1 is
-  // free) and asks for tile s+3.  The math of a tile is split in two halves:
+  // Tile t lives in ring slot t % 4.  Tiles 0-2 are requested before the
+  // loop (or earlier, see above); step s waits for tile s+1 (the older of
+  // its two outstanding tiles, or the last one), passes the workgroup
+  // barrier (after which the slot of tile s-1 is free) and asks for tile
+  // s+3.  No tile past the last is requested: a short split ends without a
+  // memory round trip for data it never uses.  The math of a tile is split
+  // in two halves:
   //   R(s): read the operands of M(s) from LDS (K of tile s+1, V of tile s),
   //         mask and softmax the scores S(s);
   //   M(s): QK of tile s+1 -> S(s+1), then PV of tile s.
   // Waves 0-3 (one per SIMD) run R(s) then M(s) in step s; waves 4-7 run
   // M(s-1) then R(s).  On every SIMD one wave is then on the matrix core
   // while the other uses LDS and the VALU.  All LDS reads of tile s finish
-  // before the barrier of step s+1, so the slot reuse above is safe.  Tiles
-  // past the end are prefetched (from valid rows) and never used.
+  // before the barrier of step s+1, so the slot reuse above is safe.
   const bool lead = wave < kWaves / 2;
 
-  auto run = [&]() {
+  auto run = [&](int skip) {
 #pragma unroll
     for (int mb = 0; mb < RB; ++mb) {
       lpart[mb] = 0.f;
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[mb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    dma_tile(0, 0);
-    dma_tile(1, 1);
-    dma_tile(2, 2);
-    vm_wait<2 * DPT>();
+    // The first `skip` tiles were requested before the prefix length was
+    // known and have landed.  Otherwise wait for tile 0, the oldest of the
+    // min(3, ntiles) requests.
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+      if (t >= skip && t < ntiles) dma_tile(t, t);
+    if (skip == 0) {
+      if (ntiles >= 3) vm_wait<2 * DPT>();
+      else if (ntiles == 2) vm_wait<DPT>();
+      else vm_wait<0>();
+    }
     lds_barrier();
 
     f32x4 sA[2][RB], sB[2][RB];
@@ -592,9 +639,12 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
 #define TV_SCHED_FENCE __builtin_amdgcn_sched_barrier(0)
     // b1: tile s+1 has landed for every wave; the slot of tile s-1 is free
     auto sync = [&](int s) {
-      vm_wait<DPT>();
+      // requests are in tile order, so tile s+1 has landed once at most the
+      // requests of tile s+2 (if there is one) are outstanding
+      if (s + 2 < ntiles) vm_wait<DPT>();
+      else vm_wait<0>();
       lds_barrier();
-      dma_tile((s + 3) % kRing, s + 3);
+      if (s + 3 < ntiles && s + 3 >= skip) dma_tile((s + 3) % kRing, s + 3);
     };
     // b2: mid-step barrier that only keeps the two groups half a step apart
     // (no data hand-off: outstanding LDS reads may cross it)
@@ -617,7 +667,7 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
     // M(s): the softmax of S(s) interleaved with the QK products of tile s+1
     // (one MFMA, then a few VALU instructions that issue while it runs), then
     // the PV products of tile s.  The QK of the tile after the last one reads
-    // a prefetched slot of valid rows; its result is never used.
+    // whatever its slot holds; its result is never used.
     auto M = [&](auto track_tag, f32x4 (&cur)[2][RB], f32x4 (&nxt)[2][RB]) {
       TV_SCHED_FENCE;
 #pragma unroll
@@ -667,13 +717,12 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
       }
     }
 #undef TV_SCHED_FENCE
-    vm_wait<0>();   // the requests past the last tile
     lds_barrier();
   };
 
 #pragma unroll
   for (int mb = 0; mb < RB; ++mb) mref[mb] = -INFINITY;
-  run();
+  run(skip);
 
   // ---- overflow check; exact two-pass recompute when needed --------------
   __shared__ int s_redo;
@@ -684,11 +733,18 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
 #pragma unroll
     for (int mb = 0; mb < RB; ++mb) {
       const float l = xsum16_32(lpart[mb]);
-      bool fin = true;
+      // One finiteness test of the sum of the lane's outputs: it is not
+      // finite if any output is (or if the sum overflows, which only asks
+      // for the exact recompute).  A compare per element would put 16 DB
+      // VALU-to-scalar dependencies in series here.
+      float acc[4];
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int e = 0; e < 4; ++e) {
+        acc[e] = o[mb][0][e];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) fin = fin && __builtin_isfinite(o[mb][db][e]);
+        for (int db = 1; db < DB; ++db) acc[e] += o[mb][db][e];
+      }
+      const bool fin = __builtin_isfinite((acc[0] + acc[1]) + (acc[2] + acc[3]));
       const bool real = row0 + 16 * mb + col < a.rows;
       // a row whose first tile was fully masked used 0 as its reference:
       // recompute it with the exact max as well
@@ -721,7 +777,7 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
       }
       lds_barrier();
     }
-    run();
+    run(0);
   }
   if (err) raise_err(a.dev_err, err);
 
@@ -892,12 +948,16 @@ void launch_split_rb(int rb, const AttnArgs& args, dim3 grid, hipStream_t stream
 
 }  // namespace
 
-AttnPlan plan_attention(const tv_attn_desc& d, int cu_count) {
+namespace {
+
+// Plan with at most `max_rb` 16-row blocks per wave; *crit receives the
+// tiles of the longest workgroup.
+AttnPlan plan_rows(const tv_attn_desc& d, int cu_count, int max_rb, int* crit) {
   AttnPlan p{};
   const int grp = d.n_q_heads / d.n_kv_heads;
   p.rows = d.n_nodes * grp;
   // a workgroup covers 16 * kWaves * RB rows, RB in {1, 2}
-  p.row_groups = (p.rows + 16 * kWaves * 2 - 1) / (16 * kWaves * 2);
+  p.row_groups = (p.rows + 16 * kWaves * max_rb - 1) / (16 * kWaves * max_rb);
   const int per_group = (p.rows + p.row_groups - 1) / p.row_groups;
   p.row_blocks = per_group <= 16 * kWaves ? 1 : 2;
   p.prefix_slots = d.max_blocks ? d.max_blocks * d.block_size : d.max_prefix_len;
@@ -948,10 +1008,28 @@ AttnPlan plan_attention(const tv_attn_desc& d, int cu_count) {
   if (d.tree_placement != TV_TREE_AUTO) sep = d.tree_placement == TV_TREE_OWN_WORKGROUP;
   else if ((int64_t)units * (p.splits + 1) > std::max(cu_count, units * 2)) sep = false;
   p.tree_sep = sep ? 1 : 0;
+  *crit = critical(splits, sep);
   const size_t parts = (size_t)d.batch * (p.splits + p.tree_sep) * d.n_nodes * d.n_q_heads;
   p.ws_o_bytes = ((parts * d.head_dim * sizeof(uint16_t) + 255) / 256) * 256;  // bf16
   p.ws_ml_bytes = ((parts * sizeof(float2) + 255) / 256) * 256;
   return p;
+}
+
+}  // namespace
+
+// Rows per wave: two 16-row blocks halve the LDS operand bytes per MFMA and
+// the workgroups that read each K/V tile, one block halves a tile's matrix
+// work per wave.  With one block a 32-token tile takes a workgroup about
+// 0.65 as long (measured on MI355X: 15.2 vs 17.4 us for the 1000-token
+// prefix of an 8B layer, where each workgroup has 4 tiles either way; at a
+// 60000-token prefix, where the grid is already full, the doubled
+// workgroups lose).  The plan with the shorter longest workgroup wins.
+AttnPlan plan_attention(const tv_attn_desc& d, int cu_count) {
+  int crit2 = 0, crit1 = 0;
+  const AttnPlan p2 = plan_rows(d, cu_count, 2, &crit2);
+  if (p2.row_blocks == 1) return p2;
+  const AttnPlan p1 = plan_rows(d, cu_count, 1, &crit1);
+  return 13 * crit1 < 20 * crit2 ? p1 : p2;
 }
 
 hipError_t launch_attention(const tv_attn_desc& d, const AttnPlan& plan, const tv_attn_ptrs& p,
