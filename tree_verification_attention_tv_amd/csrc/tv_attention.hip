@@ -329,11 +329,18 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
   const int end = min(begin + a.chunk, slots);
   int np = begin < end ? (end - begin + kTile - 1) / kTile : 0;  // prefix tiles
   const int nt = has_tree ? (a.n + kTile - 1) / kTile : 0;       // tree tiles
-  if (np == 0 && nt == 0) return;  // uniform over the workgroup
-
   // partial rows of this (sequence, split, kv head) are consecutive, in row
   // order m = node * grp + head within the group
   const int64_t prow0 = (((int64_t)b * a.nparts + s) * a.hkv + g) * a.rows;
+  if (np == 0 && nt == 0) {
+    // nothing to attend (uniform over the workgroup): an empty partial, so
+    // that the combine reads every split without the prefix length
+    for (int mb = 0; mb < RB; ++mb) {
+      const int m = row0 + 16 * mb + col;
+      if (active && m < a.rows && grp4 == 0) a.part_ml[prow0 + m] = make_float2(-INFINITY, 0.f);
+    }
+    return;
+  }
 
   // ---- per-split tables staged in LDS --------------------------------------
   int bi0 = 0;         // partial: first block index of the split
@@ -845,17 +852,13 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
   const int g = h / a.grp;
   const int m_row = i * a.grp + h % a.grp;
 
-  int err = 0;
-  const int p_len = clamped_prefix(a, b, &err);
-  const int slots = prefix_slots(a, b, p_len, &err);
-  // Partials: prefix splits 0..ns-1, then the tree's own split (index
-  // `splits`) when it has one; otherwise splits 0..max(ns, 1)-1, the last of
-  // which includes the tree.
-  const int ns = (slots + a.chunk - 1) / a.chunk;
-  const int cnt = a.tree_sep ? ns + 1 : max(ns, 1);
+  // Every split writes a partial for every row (an empty one, m = -inf,
+  // where it sees no key), so all of them are merged and the prefix length
+  // is not needed here: the partial loads are this kernel's first and only
+  // memory round trip.
+  const int cnt = a.nparts;
   const int64_t stride = (int64_t)a.hkv * a.rows;  // partial rows between splits
   const int64_t p0 = ((int64_t)b * a.nparts * a.hkv + g) * a.rows + m_row;
-  auto split_of = [&](int k) { return (a.tree_sep && k == ns) ? a.splits : k; };
 
   float mx = -INFINITY, l = 0.f;
   float acc[8];
@@ -868,7 +871,7 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
     for (int u = 0; u < U; ++u) {
       const int k = k0 + u * T;
       if (k < cnt) {
-        const int64_t pi = p0 + split_of(k) * stride;
+        const int64_t pi = p0 + k * stride;
         ml[u] = a.part_ml[pi];
         ov[u] = *reinterpret_cast<const bf16x8*>(a.part_o + pi * D + 8 * c);
       } else {
