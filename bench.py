@@ -20,8 +20,10 @@ Prints one JSON line (rank 0):
   entry for the dominant call (HIP-event timing of its own launches on the
   stream they run on, algorithmic bytes, and the HBM traffic measured with
   rocprofv3 counters when those were taken on the current kernel source);
-  the long-context (60K prefix) full and partial lines; the fp64 CPU oracle
-  timed on a bounded sample of the same workload.
+  the long-context (60K prefix) full and partial lines; a 32-layer step of
+  the 8B shape (each layer's attention, then one layer-batched acceptance and
+  commit, against per-layer commit launches); the fp64 CPU oracle timed on a
+  bounded sample of the same workload.
 
 Helper modes (used to produce the committed profile summaries):
   --copy-calibration      plain 256 MiB device copies, for scaling counters
@@ -484,6 +486,122 @@ def rectify_line(steps, dev):
     return out
 
 
+def multi_layer_line(steps, dev, layers=32):
+    """A verify step over all attention layers of the 8B shape (32 layers):
+    each layer's tree attention over its own KV cache, then acceptance and
+    the commit of the accepted rows into every layer's cache.  Fused: the
+    layer-batched acceptance-and-commit call (one walk-and-copy launch for
+    all layers).  Separate: acceptance, then one commit launch per layer.
+    Both are captured in HIP graphs over two copies of the inputs (more than
+    the Infinity Cache holds) and replayed."""
+    import torch
+
+    from tree_verification_attention_tv_amd import binding
+    from tree_verification_attention_tv_amd import workloads as W
+    wl = W.make_workload("8b_layer")
+    b, n, hq, hkv, d = wl.batch, wl.n_nodes, wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+    cap = wl.capacity
+    g = torch.Generator(device=dev)
+    g.manual_seed(4242)
+    bf = torch.bfloat16
+
+    def rnd(*shape, scale=1.0):
+        return (torch.randn(shape, generator=g, device=dev) * scale).to(bf)
+
+    class LayerSet:
+        def __init__(self):
+            self.q = rnd(layers, b, n, hq, d, scale=d ** -0.5)
+            self.k_tree = rnd(layers, b, n, hkv, d)
+            self.v_tree = rnd(layers, b, n, hkv, d)
+            self.k_cache = rnd(layers, b, hkv, cap, d)
+            self.v_cache = rnd(layers, b, hkv, cap, d)
+            self.out = torch.empty_like(self.q)
+            self.logits = torch.from_numpy(wl.logits.view("int16")).to(dev).view(bf)
+            self.parents = torch.from_numpy(wl.parents).to(dev)
+            self.draft = torch.from_numpy(wl.draft_tokens).to(dev)
+            self.prefix = torch.from_numpy(wl.prefix_len).to(dev)
+            self.new_prefix = torch.empty_like(self.prefix)
+            self.mask = torch.empty((b, n, (n + 31) // 32), dtype=torch.int32, device=dev)
+
+    sets = [LayerSet(), LayerSet()]
+    desc = binding.attn_desc(sets[0].q[0], sets[0].k_cache[0], max_prefix_len=wl.max_prefix_len)
+    ws_attn = torch.empty(binding.attention_workspace_size(desc), dtype=torch.uint8, device=dev)
+    ws_acc = torch.empty(binding.accept_workspace_size(b, n, wl.vocab), dtype=torch.uint8,
+                         device=dev)
+    acc_out = (torch.empty((b, n), dtype=torch.int32, device=dev),
+               torch.empty((b,), dtype=torch.int32, device=dev),
+               torch.empty((b, n), dtype=torch.int32, device=dev),
+               torch.empty((b,), dtype=torch.int32, device=dev))
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def attention(st):
+        for l in range(layers):
+            binding.tree_attention(
+                st.q[l], st.k_cache[l], st.v_cache[l], st.k_tree[l], st.v_tree[l], st.prefix,
+                None, max_prefix_len=wl.max_prefix_len, out=st.out[l], workspace=ws_attn,
+                dev_err=err, parents=st.parents, mask_out=st.mask if l == 0 else None)
+
+    def fused(st):
+        attention(st)
+        binding.greedy_accept_commit_layers(st.logits, st.parents, st.draft, st.k_tree,
+                                            st.v_tree, st.prefix, st.k_cache, st.v_cache,
+                                            new_prefix_len=st.new_prefix, workspace=ws_acc,
+                                            dev_err=err, outputs=acc_out)
+
+    def separate(st):
+        attention(st)
+        binding.greedy_accept(st.logits, st.parents, st.draft, workspace=ws_acc, dev_err=err,
+                              outputs=acc_out)
+        for l in range(layers):
+            binding.commit_kv(st.k_tree[l], st.v_tree[l], acc_out[2], acc_out[1], st.prefix,
+                              st.k_cache[l], st.v_cache[l], new_prefix_len=st.new_prefix,
+                              dev_err=err)
+
+    def graph_us(fn):
+        graphs = []
+        torch.cuda.synchronize()
+        for st in sets:
+            fn(st)   # warm-up outside the capture
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                fn(st)
+            graphs.append(gr)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream(dev)
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for k in range(4):
+            graphs[k % 2].replay()
+        torch.cuda.synchronize()
+        a.record(stream)
+        for k in range(steps):
+            graphs[k % 2].replay()
+        z.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(z) * 1e3 / steps
+
+    fused_us = graph_us(fused)
+    separate_us = graph_us(separate)
+    attn_us = graph_us(attention)
+    if int(err.item()) != 0:
+        print(f"device error bits {int(err.item())} (multi-layer step)", file=sys.stderr)
+        sys.exit(1)
+    out = {
+        "mode": "multi_layer",
+        "layers": layers,
+        "step_us": round(fused_us, 3),
+        "step_us_per_layer_commits": round(separate_us, 3),
+        "attention_us": round(attn_us, 3),
+        "attention_us_per_layer": round(attn_us / layers, 3),
+        "accept_commit_us": round(fused_us - attn_us, 3),
+        "accept_and_commits_us": round(separate_us - attn_us, 3),
+        "launches_per_step": {"fused": 2 * layers + 2, "separate": 3 * layers + 2},
+        "cache_rotation": len(sets),
+    }
+    del sets
+    torch.cuda.empty_cache()
+    return out
+
+
 def read_traffic():
     """HBM bytes per attention call from the committed counter summary, or
     None when it is missing or was taken on another kernel source."""
@@ -602,6 +720,7 @@ def main():
             "long_context_partial": secondary_line("long_context", True, 100, dev),
             "long_context_specpv": specpv_line(100, dev),
             "long_context_specpv_rectify": rectify_line(40, dev),
+            "multi_layer_8b": multi_layer_line(50, dev),
         }
     if not args.no_cpu_baseline and not specpv:
         result["cpu_baseline"] = cpu_baseline(wl, partial, first, acc_out, args.cpu_seconds)

@@ -75,6 +75,7 @@ typedef enum { TV_BF16 = 0, TV_F32 = 1 } tv_dtype;
 #define TV_DERR_BAD_PATH 16   /* accept_len or an accept_path entry out of range */
 
 #define TV_MAX_NODES 256
+#define TV_MAX_LAYERS 4096  /* layers of one multi-layer commit */
 
 /*
  * tv_build_tree_mask -- ancestor-or-self visibility of every tree node.
@@ -236,6 +237,23 @@ tv_status tv_greedy_accept_commit(const void* logits, tv_dtype dtype, int64_t vo
                                   int32_t* dev_err, hipStream_t stream);
 
 /*
+ * tv_greedy_accept_commit_layers -- tv_greedy_accept followed by
+ * tv_commit_kv_layers of its path, in one call (the multi-layer form of
+ * tv_greedy_accept_commit; same sources as those two calls).  Layer
+ * arguments and their errors as tv_commit_kv_layers; outputs, caches,
+ * new_prefix_len and device error bits exactly those of the two calls in a
+ * row.  One walk-and-copy workgroup per (sequence, layer).
+ */
+tv_status tv_greedy_accept_commit_layers(
+    const void* logits, tv_dtype dtype, int64_t vocab, int64_t row_stride, const int32_t* parents,
+    const int32_t* draft_tokens, int32_t batch, int32_t n_nodes, int32_t* target_argmax,
+    int32_t* accept_len, int32_t* accept_path, int32_t* bonus_token, void* workspace,
+    size_t workspace_bytes, const void* k_tree, const void* v_tree, const int32_t* prefix_len,
+    int32_t* new_prefix_len, void* k_cache, void* v_cache, int64_t cache_seq_stride,
+    int32_t cache_capacity, int32_t n_kv_heads, int32_t head_dim, int32_t n_layers,
+    int64_t tree_layer_stride, int64_t cache_layer_stride, int32_t* dev_err, hipStream_t stream);
+
+/*
  * tv_stochastic_accept -- acceptance at temperature T > 0 (sampling).
  *
  * Sources: SpecPV Sec. 2 "Related Work" (speculative sampling is equivalent
@@ -296,6 +314,39 @@ tv_status tv_commit_kv(const void* k_tree, const void* v_tree, const int32_t* ac
                        int64_t cache_seq_stride, int32_t cache_capacity, int32_t batch,
                        int32_t n_nodes, int32_t n_kv_heads, int32_t head_dim, int32_t* dev_err,
                        hipStream_t stream);
+
+/*
+ * tv_commit_kv_layers -- tv_commit_kv for the n_layers attention layers of a
+ * model in one launch.
+ *
+ * Sources: SpecBlock App. A.5 (the accepted prefix is committed before the
+ * next iteration: every layer's cache receives the same accepted nodes) and
+ * "Dynamic Speculative Decoding", the section on fusing target decode and
+ * draft extension into one CUDA graph (per-step launch overhead matters at
+ * batch 1).
+ *
+ * Layer l (0 <= l < n_layers) has its tree K/V at k_tree + l *
+ * tree_layer_stride (v_tree likewise) and its cache at k_cache + l *
+ * cache_layer_stride (v_cache likewise), strides in bf16 elements, each
+ * laid out as for tv_commit_kv; the layers' caches must not overlap.  The
+ * result is that of tv_commit_kv called once per layer with the same path,
+ * lengths and prefix lengths: every layer receives the same rows at the
+ * same positions, and new_prefix_len is written once.  One workgroup per
+ * (sequence, layer).
+ * Errors: n_layers outside [1, TV_MAX_LAYERS] (TV_ERR_SHAPE); with
+ *   n_layers > 1, a stride that is not a positive multiple of 8 elements
+ *   (TV_ERR_SHAPE) or new_prefix_len overlapping prefix_len
+ *   (TV_ERR_UNSUPPORTED: layer 0 may write the new lengths before another
+ *   layer has read the old ones).  Device fallbacks as tv_commit_kv, for
+ *   all layers alike.
+ */
+tv_status tv_commit_kv_layers(const void* k_tree, const void* v_tree, const int32_t* accept_path,
+                              const int32_t* accept_len, const int32_t* prefix_len,
+                              int32_t* new_prefix_len, void* k_cache, void* v_cache,
+                              int64_t cache_seq_stride, int32_t cache_capacity, int32_t batch,
+                              int32_t n_nodes, int32_t n_kv_heads, int32_t head_dim,
+                              int32_t n_layers, int64_t tree_layer_stride,
+                              int64_t cache_layer_stride, int32_t* dev_err, hipStream_t stream);
 
 /*
  * tv_block_summaries -- element-wise max and min key of every KV block.

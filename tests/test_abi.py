@@ -156,3 +156,33 @@ def test_attention_needs_exactly_one_of_mask_and_parents():
     ptrs.mask, ptrs.parents = p, p
     assert L.tv_tree_attention(ctypes.byref(d), ctypes.byref(ptrs), ctypes.c_void_p(p), 1 << 20,
                                None, None) == 2
+
+
+def test_multi_layer_commit_host_checks():
+    L = binding.lib()
+    names = declared_functions()
+    assert "tv_commit_kv_layers" in names and "tv_greedy_accept_commit_layers" in names
+    p = ctypes.c_void_p(256)
+    a, b = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
+
+    def commit(n_layers, ts, cs, prefix=a, new_prefix=b):
+        return L.tv_commit_kv_layers(p, p, p, p, prefix, new_prefix, p, p, 0, 64, 2, 8, 1, 128,
+                                     n_layers, ts, cs, None, None)
+    assert commit(0, 1024, 8192) == 2                       # no layers
+    assert commit(binding.MAX_LAYERS + 1, 1024, 8192) == 2  # too many
+    assert commit(2, 1020, 8192) == 2                       # tree stride not whole vectors
+    assert commit(2, 1024, 0) == 2                          # zero cache stride
+    assert commit(2, 1024, 8192, a, a) == 3                 # new_prefix_len aliases prefix_len
+    assert commit(2, 1024, 8192, a, ctypes.c_void_p(4100)) == 3  # partial overlap
+    assert L.tv_commit_kv_layers(p, p, p, p, a, b, p, p, 0, 64, 1, 8, 1, 80, 2, 1024, 8192,
+                                 None, None) == 3           # head_dim
+    assert L.tv_commit_kv_layers(None, p, p, p, a, b, p, p, 0, 64, 1, 8, 1, 128, 2, 1024, 8192,
+                                 None, None) == 1
+
+    def accept_commit(n_layers, ts, cs, new_prefix=b):
+        return L.tv_greedy_accept_commit_layers(
+            p, 0, 100, 100, p, p, 1, 8, p, p, p, p, p, 1 << 20, p, p, a, new_prefix, p, p, 0, 64,
+            1, 128, n_layers, ts, cs, None, None)
+    assert accept_commit(0, 1024, 8192) == 2
+    assert accept_commit(3, 1024, 8188) == 2
+    assert accept_commit(3, 1024, 8192, a) == 3

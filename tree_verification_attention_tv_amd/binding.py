@@ -21,6 +21,7 @@ _lib = None
 TV_BF16, TV_F32 = 0, 1
 DERR_BAD_PARENT, DERR_BAD_BLOCK, DERR_CAPACITY, DERR_BAD_PREFIX, DERR_BAD_PATH = 1, 2, 4, 8, 16
 MAX_NODES = 256
+MAX_LAYERS = 4096
 
 
 class TVError(RuntimeError):
@@ -105,6 +106,9 @@ def lib() -> ctypes.CDLL:
             L.tv_commit_kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32,
                                        i32, vp, vp]
             L.tv_commit_kv.restype = i32
+            L.tv_commit_kv_layers.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32,
+                                              i32, i32, i32, i64, i64, vp, vp]
+            L.tv_commit_kv_layers.restype = i32
             L.tv_block_summaries.argtypes = [vp, i64, i32, i32, i32, i32, i32, vp, vp, i32, vp,
                                              vp, vp]
             L.tv_block_summaries.restype = i32
@@ -121,6 +125,10 @@ def lib() -> ctypes.CDLL:
                                                   vp, vp, vp, sz, vp, vp, vp, vp, vp, vp, i64,
                                                   i32, i32, i32, vp, vp]
             L.tv_greedy_accept_commit.restype = i32
+            L.tv_greedy_accept_commit_layers.argtypes = [
+                vp, i32, i64, i64, vp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp,
+                i64, i32, i32, i32, i32, i64, i64, vp, vp]
+            L.tv_greedy_accept_commit_layers.restype = i32
             L.tv_stochastic_accept_workspace_size.argtypes = [i32, i32, i64]
             L.tv_stochastic_accept_workspace_size.restype = sz
             L.tv_stochastic_accept.argtypes = [vp, i32, i64, i64, vp, vp, i32, i32,
@@ -357,6 +365,95 @@ def greedy_accept_commit(logits, parents, draft_tokens, k_tree, v_tree, prefix_l
         _ptr(amax), _ptr(alen), _ptr(path), _ptr(bonus), _ptr(workspace), workspace.numel(),
         _ptr(k_tree), _ptr(v_tree), _ptr(prefix_len), _ptr(new_prefix_len), _ptr(k_cache),
         _ptr(v_cache), int(k_cache.stride(0)), cap, hkv, d, _err_ptr(dev_err), _stream(dev)))
+    return amax, alen, path, bonus, new_prefix_len
+
+
+def _layer_views(k_tree, v_tree, k_cache, v_cache):
+    """Checks the [L][B][N][Hkv][D] tree and [L][B][Hkv][cap][D] cache views of
+    the multi-layer calls; returns (layers, tree stride, cache stride,
+    cache sequence stride) in elements."""
+    bf = torch.bfloat16
+    for name, t in (("k_tree", k_tree), ("v_tree", v_tree), ("k_cache", k_cache),
+                    ("v_cache", v_cache)):
+        _on_gpu(name, t, bf, contiguous=False)
+        if t.dim() != 5:
+            raise ValueError(f"{name} must have a leading layer dimension")
+    nl, bsz, n, hkv, d = k_tree.shape
+    if v_tree.shape != k_tree.shape or v_tree.stride() != k_tree.stride() or \
+            k_tree.stride()[1:] != (n * hkv * d, hkv * d, d, 1):
+        raise ValueError("k_tree/v_tree must be [L][B][N][Hkv][D], contiguous within a layer")
+    if k_cache.shape[:2] != (nl, bsz) or k_cache.shape[2] != hkv or k_cache.shape[4] != d:
+        raise ValueError("caches must be [L][B][Hkv][cap][D] matching the tree")
+    cap = k_cache.shape[3]
+    if v_cache.shape != k_cache.shape or v_cache.stride() != k_cache.stride() or \
+            k_cache.stride()[2:] != (cap * d, d, 1):
+        raise ValueError("caches must have contiguous rows per (layer, sequence)")
+    return nl, int(k_tree.stride(0)), int(k_cache.stride(0)), int(k_cache.stride(1))
+
+
+def commit_kv_layers(k_tree, v_tree, accept_path, accept_len, prefix_len, k_cache, v_cache, *,
+                     new_prefix_len=None, dev_err=None):
+    """tv_commit_kv_layers: the same accepted rows into every layer's cache,
+    one launch.  k_tree/v_tree [L][B][N][Hkv][D], caches [L][B][Hkv][cap][D]
+    (layer and sequence strides free).  Returns new_prefix_len (a fresh
+    tensor unless one is given; with L > 1 it may not be prefix_len)."""
+    nl, t_stride, c_stride, seq_stride = _layer_views(k_tree, v_tree, k_cache, v_cache)
+    for name, t in (("accept_path", accept_path), ("accept_len", accept_len),
+                    ("prefix_len", prefix_len)):
+        _on_gpu(name, t, torch.int32)
+    _, bsz, n, hkv, d = k_tree.shape
+    cap = k_cache.shape[3]
+    if new_prefix_len is None:
+        new_prefix_len = torch.empty_like(prefix_len)
+    _check("tv_commit_kv_layers", lib().tv_commit_kv_layers(
+        _ptr(k_tree), _ptr(v_tree), _ptr(accept_path), _ptr(accept_len), _ptr(prefix_len),
+        _ptr(new_prefix_len), _ptr(k_cache), _ptr(v_cache), seq_stride, cap, bsz, n, hkv, d,
+        nl, t_stride, c_stride, _err_ptr(dev_err), _stream(k_cache.device)))
+    return new_prefix_len
+
+
+def greedy_accept_commit_layers(logits, parents, draft_tokens, k_tree, v_tree, prefix_len,
+                                k_cache, v_cache, *, new_prefix_len=None, vocab=None,
+                                workspace=None, dev_err=None, outputs=None):
+    """tv_greedy_accept_commit_layers: acceptance, then the accepted rows
+    into every layer's cache, in one call.  Tree and cache views as
+    commit_kv_layers.  Returns (target_argmax, accept_len, accept_path,
+    bonus, new_prefix_len)."""
+    nl, t_stride, c_stride, seq_stride = _layer_views(k_tree, v_tree, k_cache, v_cache)
+    _on_gpu("logits", logits, (torch.bfloat16, torch.float32), contiguous=False)
+    _on_gpu("parents", parents, torch.int32)
+    _on_gpu("draft_tokens", draft_tokens, torch.int32)
+    _on_gpu("prefix_len", prefix_len, torch.int32)
+    bsz, n = parents.shape
+    if logits.shape[:2] != (bsz, n) or logits.stride(2) != 1 or \
+            (bsz > 1 and logits.stride(0) != n * logits.stride(1)):
+        raise ValueError("logits must be [B][N][V] with unit vocab stride and uniform row stride")
+    if k_tree.shape[1:3] != (bsz, n):
+        raise ValueError("k_tree must be [L][B][N][Hkv][D] for the parents' B and N")
+    _, _, _, hkv, d = k_tree.shape
+    cap = k_cache.shape[3]
+    v = logits.shape[2] if vocab is None else int(vocab)
+    dt = TV_BF16 if logits.dtype == torch.bfloat16 else TV_F32
+    dev = parents.device
+    if outputs is None:
+        outputs = (torch.empty((bsz, n), dtype=torch.int32, device=dev),
+                   torch.empty((bsz,), dtype=torch.int32, device=dev),
+                   torch.empty((bsz, n), dtype=torch.int32, device=dev),
+                   torch.empty((bsz,), dtype=torch.int32, device=dev))
+    amax, alen, path, bonus = outputs
+    if new_prefix_len is None:
+        new_prefix_len = torch.empty_like(prefix_len)
+    ws_bytes = accept_workspace_size(bsz, n, v)
+    if ws_bytes == 0:
+        raise TVError("tv_greedy_accept_workspace_size", 2)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    _check("tv_greedy_accept_commit_layers", lib().tv_greedy_accept_commit_layers(
+        _ptr(logits), dt, v, int(logits.stride(1)), _ptr(parents), _ptr(draft_tokens), bsz, n,
+        _ptr(amax), _ptr(alen), _ptr(path), _ptr(bonus), _ptr(workspace), workspace.numel(),
+        _ptr(k_tree), _ptr(v_tree), _ptr(prefix_len), _ptr(new_prefix_len), _ptr(k_cache),
+        _ptr(v_cache), seq_stride, cap, hkv, d, nl, t_stride, c_stride, _err_ptr(dev_err),
+        _stream(dev)))
     return amax, alen, path, bonus, new_prefix_len
 
 

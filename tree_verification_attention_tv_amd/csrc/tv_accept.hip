@@ -37,6 +37,7 @@ struct CommitArgs {
   uint4* v_cache;
   int64_t seq_stride_vec;
   int cap, hkv, vec_per_row;
+  int64_t tree_layer_vec, cache_layer_vec;  // 16-byte vectors between layers
 };
 
 struct ValIdx {
@@ -186,6 +187,10 @@ __global__ __launch_bounds__(kThreads) void path_walk_kernel(
   __shared__ unsigned red[kThreads / kWave];
 
   const int b = blockIdx.x;
+  // With several layers, one workgroup per (sequence, layer): each walks the
+  // (small) tree itself and copies its own layer's rows; layer 0 writes the
+  // acceptance outputs, the new prefix length and the error bits.
+  const bool lead = blockIdx.y == 0;
   const int i = threadIdx.x;
   if (i == 0) bad = 0;
   __syncthreads();
@@ -213,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void path_walk_kernel(
         }
     }
     amax[i] = bi;
-    target_argmax[row] = bi;
+    if (lead) target_argmax[row] = bi;
     par[i] = p;
     dtok[i] = dt;
     const bool ok = (i == 0) ? (p == -1) : (p >= 0 && p < i);
@@ -250,26 +255,29 @@ __global__ __launch_bounds__(kThreads) void path_walk_kernel(
   const int depth = (int)(best >> 16);
 
   int32_t* path = accept_path + (int64_t)b * n;
-  if (i < n && i > depth) path[i] = -1;
+  if (lead && i < n && i > depth) path[i] = -1;
+  int32_t* const err_out = lead ? dev_err : nullptr;
   if (i == 0) {
     int j = end_node;
     for (int k = depth; k >= 0; --k) {
-      path[k] = j;
+      if (lead) path[k] = j;
       s_path[k] = j;
       j = par[j];
     }
-    accept_len[b] = depth;
-    bonus[b] = amax[end_node];
-    if (bad) raise_err(dev_err, TV_DERR_BAD_PARENT);
+    if (lead) {
+      accept_len[b] = depth;
+      bonus[b] = amax[end_node];
+    }
+    if (bad) raise_err(err_out, TV_DERR_BAD_PARENT);
     if (cm.k_cache) {
       // the commit's checks (tv_commit_kv): the path is valid by construction
       const int p = cm.prefix_len[b];
       int ok = 1;
       if (p < 0 || p > cm.cap) {
-        raise_err(dev_err, TV_DERR_BAD_PREFIX);
+        raise_err(err_out, TV_DERR_BAD_PREFIX);
         ok = 0;
       } else if ((int64_t)p + depth + 1 > cm.cap) {
-        raise_err(dev_err, TV_DERR_CAPACITY);
+        raise_err(err_out, TV_DERR_CAPACITY);
         ok = 0;
       }
       s_prefix = p;
@@ -283,10 +291,11 @@ __global__ __launch_bounds__(kThreads) void path_walk_kernel(
   if (s_ok) {
     const int per_row = cm.vec_per_row, hkv = cm.hkv;
     const int items = (depth + 1) * hkv * per_row;
-    const uint4* __restrict__ kt = cm.k_tree + (int64_t)b * n * hkv * per_row;
-    const uint4* __restrict__ vt = cm.v_tree + (int64_t)b * n * hkv * per_row;
-    uint4* __restrict__ kc = cm.k_cache + b * cm.seq_stride_vec;
-    uint4* __restrict__ vc = cm.v_cache + b * cm.seq_stride_vec;
+    const int64_t lt = blockIdx.y * cm.tree_layer_vec, lc = blockIdx.y * cm.cache_layer_vec;
+    const uint4* __restrict__ kt = cm.k_tree + lt + (int64_t)b * n * hkv * per_row;
+    const uint4* __restrict__ vt = cm.v_tree + lt + (int64_t)b * n * hkv * per_row;
+    uint4* __restrict__ kc = cm.k_cache + lc + b * cm.seq_stride_vec;
+    uint4* __restrict__ vc = cm.v_cache + lc + b * cm.seq_stride_vec;
 #pragma unroll 4
     for (int it = i; it < items; it += kThreads) {
       const int c = it % per_row, rh = it / per_row;
@@ -297,7 +306,7 @@ __global__ __launch_bounds__(kThreads) void path_walk_kernel(
       vc[dst] = vt[src];
     }
   }
-  if (i == 0) cm.new_prefix_len[b] = s_ok ? p + depth + 1 : p;
+  if (i == 0 && lead) cm.new_prefix_len[b] = s_ok ? p + depth + 1 : p;
 }
 
 }  // namespace
@@ -352,7 +361,11 @@ hipError_t launch_accept(const void* logits, tv_dtype dt, int64_t vocab, int64_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   CommitArgs cm{};
+  int layers = 1;
   if (commit) {
+    layers = commit->layers;
+    cm.tree_layer_vec = commit->tree_layer_stride / 8;
+    cm.cache_layer_vec = commit->cache_layer_stride / 8;
     cm.k_tree = (const uint4*)commit->k_tree;
     cm.v_tree = (const uint4*)commit->v_tree;
     cm.prefix_len = commit->prefix_len;
@@ -364,7 +377,7 @@ hipError_t launch_accept(const void* logits, tv_dtype dt, int64_t vocab, int64_t
     cm.hkv = commit->hkv;
     cm.vec_per_row = commit->d / 8;
   }
-  hipLaunchKernelGGL(path_walk_kernel, dim3(batch), dim3(kThreads), 0, stream, part_v, part_i,
+  hipLaunchKernelGGL(path_walk_kernel, dim3(batch, layers), dim3(kThreads), 0, stream, part_v, part_i,
                      plan.chunks, parents, draft, n, target_argmax, accept_len, accept_path, bonus,
                      dev_err, cm);
   return hipGetLastError();

@@ -32,6 +32,24 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 tv_status launch_status(hipError_t e) { return e == hipSuccess ? TV_OK : TV_ERR_LAUNCH; }
 
+// Layer arguments of the commit calls.  With several layers the strides are
+// positive whole 16-byte vectors, and new_prefix_len may not overlap
+// prefix_len: a later layer's workgroup still reads prefix_len after layer
+// 0 has written the new lengths.
+tv_status check_layers(int32_t n_layers, int64_t tree_layer_stride, int64_t cache_layer_stride,
+                       const int32_t* prefix_len, const int32_t* new_prefix_len, int32_t batch) {
+  if (n_layers < 1 || n_layers > TV_MAX_LAYERS) return TV_ERR_SHAPE;
+  if (n_layers == 1) return TV_OK;
+  if (tree_layer_stride <= 0 || cache_layer_stride <= 0 || tree_layer_stride % 8 ||
+      cache_layer_stride % 8)
+    return TV_ERR_SHAPE;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(prefix_len);
+  const uintptr_t b = reinterpret_cast<uintptr_t>(new_prefix_len);
+  const uintptr_t len = (uintptr_t)batch * sizeof(int32_t);
+  if (a < b + len && b < a + len) return TV_ERR_UNSUPPORTED;
+  return TV_OK;
+}
+
 tv_status check_attn_desc(const tv_attn_desc* d) {
   if (!d) return TV_ERR_NULL;
   if (d->batch < 0 || d->n_nodes < 1 || d->n_nodes > TV_MAX_NODES) return TV_ERR_SHAPE;
@@ -168,6 +186,21 @@ tv_status tv_greedy_accept_commit(const void* logits, tv_dtype dtype, int64_t vo
                                   void* k_cache, void* v_cache, int64_t cache_seq_stride,
                                   int32_t cache_capacity, int32_t n_kv_heads, int32_t head_dim,
                                   int32_t* dev_err, hipStream_t stream) {
+  return tv_greedy_accept_commit_layers(
+      logits, dtype, vocab, row_stride, parents, draft_tokens, batch, n_nodes, target_argmax,
+      accept_len, accept_path, bonus_token, workspace, workspace_bytes, k_tree, v_tree, prefix_len,
+      new_prefix_len, k_cache, v_cache, cache_seq_stride, cache_capacity, n_kv_heads, head_dim, 1,
+      0, 0, dev_err, stream);
+}
+
+tv_status tv_greedy_accept_commit_layers(
+    const void* logits, tv_dtype dtype, int64_t vocab, int64_t row_stride, const int32_t* parents,
+    const int32_t* draft_tokens, int32_t batch, int32_t n_nodes, int32_t* target_argmax,
+    int32_t* accept_len, int32_t* accept_path, int32_t* bonus_token, void* workspace,
+    size_t workspace_bytes, const void* k_tree, const void* v_tree, const int32_t* prefix_len,
+    int32_t* new_prefix_len, void* k_cache, void* v_cache, int64_t cache_seq_stride,
+    int32_t cache_capacity, int32_t n_kv_heads, int32_t head_dim, int32_t n_layers,
+    int64_t tree_layer_stride, int64_t cache_layer_stride, int32_t* dev_err, hipStream_t stream) {
   if (!logits || !parents || !draft_tokens || !target_argmax || !accept_len || !accept_path ||
       !bonus_token || !workspace || !k_tree || !v_tree || !prefix_len || !new_prefix_len ||
       !k_cache || !v_cache)
@@ -183,11 +216,16 @@ tv_status tv_greedy_accept_commit(const void* logits, tv_dtype dtype, int64_t vo
   if (!aligned(k_tree, 16) || !aligned(v_tree, 16) || !aligned(k_cache, 16) ||
       !aligned(v_cache, 16))
     return TV_ERR_UNSUPPORTED;
+  const tv_status ls = check_layers(n_layers, tree_layer_stride, cache_layer_stride, prefix_len,
+                                    new_prefix_len, batch);
+  if (ls != TV_OK) return ls;
   if (batch == 0) return TV_OK;
   const tv::AcceptPlan plan = tv::plan_accept(batch, n_nodes, vocab);
   if (!aligned(workspace, 16) || workspace_bytes < plan.ws_bytes) return TV_ERR_WORKSPACE;
-  const tv::CommitTarget ct{k_tree,  v_tree,           prefix_len,     new_prefix_len, k_cache,
-                            v_cache, cache_seq_stride, cache_capacity, n_kv_heads,     head_dim};
+  const tv::CommitTarget ct{k_tree,           v_tree,         prefix_len, new_prefix_len,
+                            k_cache,          v_cache,        cache_seq_stride,
+                            cache_capacity,   n_kv_heads,     head_dim,
+                            n_layers,         tree_layer_stride, cache_layer_stride};
   return launch_status(tv::launch_accept(logits, dtype, vocab, row_stride, parents, draft_tokens,
                                          batch, n_nodes, target_argmax, accept_len, accept_path,
                                          bonus_token, workspace, plan, dev_err, stream, &ct));
@@ -228,6 +266,18 @@ tv_status tv_commit_kv(const void* k_tree, const void* v_tree, const int32_t* ac
                        int64_t cache_seq_stride, int32_t cache_capacity, int32_t batch,
                        int32_t n_nodes, int32_t n_kv_heads, int32_t head_dim, int32_t* dev_err,
                        hipStream_t stream) {
+  return tv_commit_kv_layers(k_tree, v_tree, accept_path, accept_len, prefix_len, new_prefix_len,
+                             k_cache, v_cache, cache_seq_stride, cache_capacity, batch, n_nodes,
+                             n_kv_heads, head_dim, 1, 0, 0, dev_err, stream);
+}
+
+tv_status tv_commit_kv_layers(const void* k_tree, const void* v_tree, const int32_t* accept_path,
+                              const int32_t* accept_len, const int32_t* prefix_len,
+                              int32_t* new_prefix_len, void* k_cache, void* v_cache,
+                              int64_t cache_seq_stride, int32_t cache_capacity, int32_t batch,
+                              int32_t n_nodes, int32_t n_kv_heads, int32_t head_dim,
+                              int32_t n_layers, int64_t tree_layer_stride,
+                              int64_t cache_layer_stride, int32_t* dev_err, hipStream_t stream) {
   if (!k_tree || !v_tree || !accept_path || !accept_len || !prefix_len || !new_prefix_len ||
       !k_cache || !v_cache)
     return TV_ERR_NULL;
@@ -240,10 +290,14 @@ tv_status tv_commit_kv(const void* k_tree, const void* v_tree, const int32_t* ac
   if (!aligned(k_tree, 16) || !aligned(v_tree, 16) || !aligned(k_cache, 16) ||
       !aligned(v_cache, 16))
     return TV_ERR_UNSUPPORTED;
+  const tv_status ls = check_layers(n_layers, tree_layer_stride, cache_layer_stride, prefix_len,
+                                    new_prefix_len, batch);
+  if (ls != TV_OK) return ls;
   if (batch == 0) return TV_OK;
   return launch_status(tv::launch_commit(k_tree, v_tree, accept_path, accept_len, prefix_len,
                                          new_prefix_len, k_cache, v_cache, cache_seq_stride,
                                          cache_capacity, batch, n_nodes, n_kv_heads, head_dim,
+                                         n_layers, tree_layer_stride, cache_layer_stride,
                                          dev_err, stream));
 }
 

@@ -58,6 +58,8 @@ struct CommitTarget {
   void* v_cache;
   int64_t seq_stride;  // elements
   int cap, hkv, d;
+  int layers;                 // >= 1; layer l's tensors at the strides below (elements)
+  int64_t tree_layer_stride, cache_layer_stride;
 };
 
 hipError_t launch_accept(const void* logits, tv_dtype dt, int64_t vocab, int64_t row_stride,
@@ -71,6 +73,7 @@ hipError_t launch_commit(const void* k_tree, const void* v_tree, const int32_t* 
                          const int32_t* accept_len, const int32_t* prefix_len,
                          int32_t* new_prefix_len, void* k_cache, void* v_cache,
                          int64_t seq_stride, int cap, int batch, int n, int hkv, int d,
+                         int layers, int64_t tree_layer_stride, int64_t cache_layer_stride,
                          int32_t* dev_err, hipStream_t stream);
 
 AcceptPlan plan_stochastic(int batch, int n, int64_t vocab);
