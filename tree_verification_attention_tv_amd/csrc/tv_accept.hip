@@ -194,10 +194,12 @@ __global__ __launch_bounds__(kThreads) void path_walk_kernel(
   const int i = threadIdx.x;
   if (i == 0) bad = 0;
   __syncthreads();
+  int p_commit = 0;  // the commit's prefix length, loaded with the partials
   if (i < n) {
     const int64_t row = (int64_t)b * n + i;
     const int p = parents[row];
     const int dt = draft[row];
+    if (i == 0 && cm.k_cache) p_commit = cm.prefix_len[b];
     // chunk partials in groups of 8, all loads of a group in flight at once
     float bv = -INFINITY;
     int bi = INT32_MAX;
@@ -271,7 +273,7 @@ __global__ __launch_bounds__(kThreads) void path_walk_kernel(
     if (bad) raise_err(err_out, TV_DERR_BAD_PARENT);
     if (cm.k_cache) {
       // the commit's checks (tv_commit_kv): the path is valid by construction
-      const int p = cm.prefix_len[b];
+      const int p = p_commit;
       int ok = 1;
       if (p < 0 || p > cm.cap) {
         raise_err(err_out, TV_DERR_BAD_PREFIX);
