@@ -89,6 +89,35 @@ __device__ __forceinline__ ValIdx wave_argmax(ValIdx a) {
   return a;
 }
 
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xF, 0xF, false);
+}
+
+// wave-wide max of a float and min of an int (every lane gets the result):
+// row rotations by 8, 4, 2, 1, then the row swaps
+__device__ __forceinline__ float wave_max_f(float x) {
+  x = fmaxf(x, __int_as_float(dpp_i<0x128>(__float_as_int(x))));
+  x = fmaxf(x, __int_as_float(dpp_i<0x124>(__float_as_int(x))));
+  x = fmaxf(x, __int_as_float(dpp_i<0x122>(__float_as_int(x))));
+  x = fmaxf(x, __int_as_float(dpp_i<0x121>(__float_as_int(x))));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ int wave_min_i(int x) {
+  x = min(x, dpp_i<0x128>(x));
+  x = min(x, dpp_i<0x124>(x));
+  x = min(x, dpp_i<0x122>(x));
+  x = min(x, dpp_i<0x121>(x));
+  const auto a = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+  x = min((int)a[0], (int)a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+  return min((int)b[0], (int)b[1]);
+}
+
 template <typename T>
 __device__ __forceinline__ float to_f32(T x);
 template <>
@@ -130,24 +159,59 @@ __global__ __launch_bounds__(kThreads) void vocab_argmax_kernel(const T* __restr
     // costs one memory round trip.  Vector u of thread t covers elements
     // begin + (u * kThreads + t) * VEC .. +VEC-1 (coalesced for each u).
     // chunk_len <= kThreads * 8 * kUnroll = kThreads * VEC * U elements, so
-    // U vectors per thread cover the chunk; only the last chunk is ragged.
+    // U vectors per thread cover the chunk; only the last chunk is ragged
+    // (elements past its end read as -inf and are never chosen).
     constexpr int U = kUnroll * 8 / VEC;
     vec_t x[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t base = begin + ((int64_t)u * kThreads + threadIdx.x) * VEC;
-      if (base + VEC <= end) x[u] = *reinterpret_cast<const vec_t*>(src + base);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t base = begin + ((int64_t)u * kThreads + threadIdx.x) * VEC;
       if (base + VEC <= end) {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) take(to_f32<T>(x[u][e]), base + e);
+        x[u] = *reinterpret_cast<const vec_t*>(src + base);
       } else {
-        for (int64_t k = base; k < end; ++k) take(to_f32<T>(src[k]), k);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) x[u][e] = base + e < end ? src[base + e] : (T)(-INFINITY);
       }
     }
+    // Two passes over the registers: the workgroup's largest value first
+    // (a max per element), then, only in the threads that hold it, the
+    // first index equal to it (values compare as reals, -0 == +0).  A
+    // running (value, index) update per element would cost three times the
+    // VALU work.
+    float m = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) m = fmaxf(m, to_f32<T>(x[u][e]));
+    __shared__ float s_max[kThreads / kWave];
+    const int w = threadIdx.x / kWave;
+    const float wm = wave_max_f(m);
+    if ((threadIdx.x & (kWave - 1)) == 0) s_max[w] = wm;
+    __syncthreads();
+    float big = s_max[0];
+#pragma unroll
+    for (int k = 1; k < kThreads / kWave; ++k) big = fmaxf(big, s_max[k]);
+    int first = INT32_MAX;
+    if (m == big) {
+#pragma unroll
+      for (int u = U - 1; u >= 0; --u) {
+        const int64_t base = begin + ((int64_t)u * kThreads + threadIdx.x) * VEC;
+#pragma unroll
+        for (int e = VEC - 1; e >= 0; --e)
+          if (to_f32<T>(x[u][e]) == big && base + e < end) first = (int)(base + e);
+      }
+    }
+    __shared__ int s_first[kThreads / kWave];
+    const int wf = wave_min_i(first);
+    if ((threadIdx.x & (kWave - 1)) == 0) s_first[w] = wf;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int f = s_first[0];
+      for (int k = 1; k < kThreads / kWave; ++k) f = min(f, s_first[k]);
+      part_v[row * chunks + chunk] = big;
+      part_i[row * chunks + chunk] = f;
+    }
+    return;
   } else {
     for (int64_t k = begin + threadIdx.x; k < end; k += kThreads) take(to_f32<T>(src[k]), k);
   }
