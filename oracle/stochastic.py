@@ -22,7 +22,15 @@ Sources:
 Readings (listed in the design notes):
 
 * Node u's target distribution is p_u = softmax(logits_u / T) over the whole
-  vocabulary (top-k / top-p filtering is not part of this function).
+  vocabulary, optionally filtered (SpecPV App. D: Qwen3 thinking mode samples
+  at T = 0.6 with top-p 0.95 and top-k 20; App. E: T = 0.7 and 1.0 with
+  top-k off and top-p 0.9).  Filters, in this order:
+  - top-k (k > 0): token x is kept iff fewer than k tokens have a strictly
+    larger logit (tokens tied with the k-th largest are all kept);
+  - top-p (p < 1): among the tokens top-k kept, with their probabilities
+    renormalised, x is kept iff the tokens with a strictly larger logit hold
+    less than p of that mass (so the most likely token is always kept);
+  - the kept tokens' probabilities are renormalised to sum to 1.
 * The pages give no draft distributions, so a draft token is a point mass:
   at an accepted node u the children are tried in ascending node index;
   child c with token x is accepted with probability p_u(x) / R, R the
@@ -83,15 +91,53 @@ def _row_f64(row) -> np.ndarray:
     return bf16_to_f64(r) if r.dtype == np.uint16 else r.astype(np.float64)
 
 
-def target_probs(row, temperature: float) -> np.ndarray:
-    """softmax(logits / T) in fp64."""
+def target_probs(row, temperature: float, top_k: int = 0, top_p: float = 1.0) -> np.ndarray:
+    """softmax(logits / T) in fp64, then the top-k and top-p filters of the
+    module notes (top_k = 0 and top_p = 1 leave it unfiltered)."""
     if not temperature > 0:
         raise OracleInputError("temperature must be positive")
-    z = _row_f64(row) / float(temperature)
+    if top_k < 0 or not 0.0 < top_p <= 1.0:
+        raise OracleInputError("top_k must be >= 0 and top_p in (0, 1]")
+    l = _row_f64(row)
+    z = l / float(temperature)
     if not np.all(np.isfinite(z)):
         raise OracleInputError("non-finite logits")
     e = np.exp(z - z.max())
-    return e / e.sum()
+    p = e / e.sum()
+    keep = np.ones(p.shape, dtype=bool)
+    if top_k > 0:
+        # number of tokens with a strictly larger logit, for every token
+        keep &= _count_above(l) < top_k
+    if top_p < 1.0:
+        q = np.where(keep, p, 0.0)
+        q = q / q.sum()
+        mass_above = _mass_above(l, q)
+        keep &= mass_above < top_p
+    f = np.where(keep, p, 0.0)
+    return f / f.sum()
+
+
+def _count_above(l):
+    """For each entry, how many entries are strictly larger (via a sort)."""
+    s = np.sort(l)
+    return l.size - np.searchsorted(s, l, side="right")
+
+
+def _mass_above(l, q):
+    """For each entry, the total of q over entries with a strictly larger l."""
+    order = np.argsort(-l, kind="stable")
+    ls, qs = l[order], q[order]
+    out = np.empty_like(q)
+    run = 0.0
+    i = 0
+    while i < ls.size:
+        j = i
+        while j < ls.size and ls[j] == ls[i]:
+            j += 1
+        out[order[i:j]] = run          # mass strictly above this value
+        run += qs[i:j].sum()
+        i = j
+    return out
 
 
 def _walk(probs_of, parents_row, draft_row, vocab, key, step, seq, decide=None):
@@ -138,7 +184,8 @@ def _walk(probs_of, parents_row, draft_row, vocab, key, step, seq, decide=None):
 
 
 def stochastic_accept(logits, parents, draft_tokens, temperature: float, key, step: int = 0,
-                      return_events: bool = False, decide=None):
+                      return_events: bool = False, decide=None, top_k: int = 0,
+                      top_p: float = 1.0):
     """Stochastic verification of a draft tree (see the module notes).
 
     logits [B][N][V] (bf16 as uint16 bit patterns, or fp32); parents and
@@ -146,7 +193,8 @@ def stochastic_accept(logits, parents, draft_tokens, temperature: float, key, st
     root first and -1 padded, bonus [B]); with ``return_events`` also the
     per-sequence list of decisions.  ``decide(event, ok)`` may override an
     acceptance decision (used to follow another implementation's choice where
-    a uniform lies within rounding distance of its threshold).
+    a uniform lies within rounding distance of its threshold).  ``top_k`` /
+    ``top_p`` filter every node's distribution (module notes).
     """
     lg = np.asarray(logits)
     par = np.asarray(parents)
@@ -163,7 +211,7 @@ def stochastic_accept(logits, parents, draft_tokens, temperature: float, key, st
 
         def probs_of(u, b=b, cache=cache):
             if u not in cache:
-                cache[u] = target_probs(lg[b, u], temperature)
+                cache[u] = target_probs(lg[b, u], temperature, top_k, top_p)
             return cache[u]
         a, pth, y, ev = _walk(probs_of, par[b], dr[b], vocab, key, step, b,
                               None if decide is None else (lambda e, ok, b=b: decide(b, e, ok)))

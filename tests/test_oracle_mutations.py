@@ -229,3 +229,45 @@ def test_wrong_speculative_sampling_is_caught(monkeypatch, old, new):
 def test_wrong_philox_constant_is_caught(monkeypatch):
     monkeypatch.setattr(STO, "_M1", STO._M1 ^ 4)
     assert _fails(spins2.test_philox_matches_numpy, 0)
+
+
+def _filter_with(old, new):
+    src = inspect.getsource(STO.target_probs)
+    assert old in src
+    ns = dict(STO.__dict__)
+    exec(src.replace(old, new), ns)
+    return ns["target_probs"]
+
+
+def _mass_above_with(old, new):
+    src = inspect.getsource(STO._mass_above)
+    assert old in src
+    ns = dict(STO.__dict__)
+    exec(src.replace(old, new), ns)
+    return ns["_mass_above"]
+
+
+@pytest.mark.parametrize("old,new", [
+    ("keep &= _count_above(l) < top_k", "keep &= _count_above(l) <= top_k"),  # k+1 kept
+    ("keep &= mass_above < top_p", "keep &= mass_above <= top_p"),           # boundary kept
+    ("q = q / q.sum()", "pass"),                        # top-p on the unrenormalised mass
+    ("return f / f.sum()", "return f"),                 # kept mass not renormalised
+    ("mass_above = _mass_above(l, q)", "mass_above = _mass_above(l, p)"),  # top-p before top-k
+])
+def test_wrong_filter_is_caught(monkeypatch, old, new):
+    monkeypatch.setattr(STO, "target_probs", _filter_with(old, new))
+    caught = _fails(spins2.test_filters_hand_worked) or any(
+        _fails(spins2.test_filters_match_brute_force, s) for s in range(30))
+    assert caught
+
+
+@pytest.mark.parametrize("old,new", [
+    ("out[order[i:j]] = run          # mass strictly above this value",
+     "out[order[i:j]] = run + qs[i:j].sum()"),          # ties counted as above
+    ("while j < ls.size and ls[j] == ls[i]:", "while j < ls.size and j == i:"),  # ties split
+])
+def test_wrong_mass_above_is_caught(monkeypatch, old, new):
+    monkeypatch.setattr(STO, "_mass_above", _mass_above_with(old, new))
+    caught = _fails(spins2.test_filters_hand_worked) or any(
+        _fails(spins2.test_filters_match_brute_force, s) for s in range(30))
+    assert caught
