@@ -237,6 +237,20 @@ class StepRunner:
                                        workspace=self.ws_sto, dev_err=self.err,
                                        outputs=self.sto_out)
 
+    def k_accept_stochastic_filtered(self, s):
+        # SpecPV App. D's sampling settings: T = 0.6, top-k 20, top-p 0.95
+        self.binding.stochastic_accept_filtered(s.logits, s.parents, s.draft, 0.6, top_k=20,
+                                                top_p=0.95, seed=(1, 2), step=0,
+                                                workspace=self.ws_sto, dev_err=self.err,
+                                                outputs=self.sto_out)
+
+    def k_accept_stochastic_top_p(self, s):
+        # SpecPV App. E's: T = 0.7, top-k off, top-p 0.9
+        self.binding.stochastic_accept_filtered(s.logits, s.parents, s.draft, 0.7, top_k=0,
+                                                top_p=0.9, seed=(1, 2), step=0,
+                                                workspace=self.ws_sto, dev_err=self.err,
+                                                outputs=self.sto_out)
+
     def k_accept_commit(self, s):
         # acceptance, and the commit of its path by the same walk workgroups
         self.binding.greedy_accept_commit(s.logits, s.parents, s.draft, s.k_tree, s.v_tree,
@@ -384,6 +398,8 @@ def measure(wl, partial, steps, warmup, warm, num_splits, dev, graph=True, specp
              "commit": tm(r.k_commit), "accept_commit": tm(r.k_accept_commit)}
     if not specpv and not partial:
         calls["accept_stochastic"] = tm(r.k_accept_stochastic)
+        calls["accept_stochastic_filtered"] = tm(r.k_accept_stochastic_filtered)
+        calls["accept_stochastic_top_p"] = tm(r.k_accept_stochastic_top_p)
     if specpv:
         calls["select"] = tm(r.k_select)
         calls["summaries_update"] = tm(r.k_summ_update)
@@ -695,7 +711,8 @@ def main():
         "kv_hbm_frac": round(kv_bytes / (calls["attention"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "call_us": {k: round(v, 3) for k, v in calls.items()},
         "accept_gbps": {k: round(logit_bytes / (calls[k] * 1e-6) / 1e9, 1)
-                        for k in ("accept", "accept_stochastic") if k in calls},
+                        for k in ("accept", "accept_stochastic", "accept_stochastic_filtered",
+                                  "accept_stochastic_top_p") if k in calls},
         "roofline": {
             "kernel": ("tv_tree_attention (attn_split_kernel + attn_combine_kernel)"
                        if dominant == "attention" else

@@ -292,6 +292,41 @@ tv_status tv_stochastic_accept(const void* logits, tv_dtype dtype, int64_t vocab
                                hipStream_t stream);
 
 /*
+ * tv_stochastic_accept_filtered -- tv_stochastic_accept with every node's
+ * distribution filtered by top-k and top-p first.
+ *
+ * Source: SpecPV App. D "Generation Settings" (Qwen3 thinking mode samples at
+ * temperature 0.6 with top-p 0.95 and top-k 20) and App. E (temperatures 0.7
+ * and 1.0 with top-k off and top-p 0.9).
+ *
+ * Filters, in this order, on p_u = softmax(l_u / T):
+ *   top-k (top_k > 0): token x is kept iff fewer than top_k tokens have a
+ *     strictly larger logit (ties with the top_k-th largest are all kept);
+ *   top-p (top_p < 1): of the tokens top-k kept, with their probabilities
+ *     renormalised, x is kept iff the tokens with a strictly larger logit
+ *     hold less than top_p of that mass (the most likely token always stays);
+ * and the kept probabilities are renormalised.  Every kept set is "logit >=
+ * tau_u" for one threshold per row, which a radix selection finds (the
+ * top-p masses are fp32 exponentials summed in 2^-40 fixed point, so a
+ * token whose larger tokens hold within about 1e-6 of top_p may fall either
+ * way).  The walk, the bonus draw,
+ * the uniforms, outputs and fallbacks are then exactly those of
+ * tv_stochastic_accept with p_u replaced by the filtered distribution;
+ * top_k = 0 and top_p = 1 give tv_stochastic_accept itself.
+ * Errors: top_k < 0 or top_p outside (0, 1] (TV_ERR_SHAPE).  Workspace:
+ * tv_stochastic_accept_workspace_size(...) bytes, as for tv_stochastic_accept.
+ */
+tv_status tv_stochastic_accept_filtered(const void* logits, tv_dtype dtype, int64_t vocab,
+                                        int64_t row_stride, const int32_t* parents,
+                                        const int32_t* draft_tokens, int32_t batch,
+                                        int32_t n_nodes, float temperature, int32_t top_k,
+                                        float top_p, uint64_t seed0, uint64_t seed1,
+                                        uint64_t step, int32_t* accept_len, int32_t* accept_path,
+                                        int32_t* bonus_token, void* workspace,
+                                        size_t workspace_bytes, int32_t* dev_err,
+                                        hipStream_t stream);
+
+/*
  * tv_commit_kv -- append the accepted path's K/V to the cache.
  *
  * Source: SpecBlock App. A.5 (commit the longest accepted prefix before the

@@ -186,3 +186,18 @@ def test_multi_layer_commit_host_checks():
     assert accept_commit(0, 1024, 8192) == 2
     assert accept_commit(3, 1024, 8188) == 2
     assert accept_commit(3, 1024, 8192, a) == 3
+
+
+def test_filtered_stochastic_accept_host_checks():
+    L = binding.lib()
+    assert "tv_stochastic_accept_filtered" in declared_functions()
+    p = ctypes.c_void_p(256)
+
+    def call(k, top_p, temp=1.0):
+        return L.tv_stochastic_accept_filtered(p, 0, 100, 100, p, p, 1, 8, temp, k, top_p, 1, 2,
+                                               3, p, p, p, p, 1 << 20, None, None)
+    assert call(-1, 1.0) == 2
+    assert call(0, 0.0) == 2
+    assert call(0, 1.5) == 2
+    assert call(0, float("nan")) == 2
+    assert call(20, 0.95, temp=0.0) == 2

@@ -17,6 +17,11 @@ a few 1e-6 in these inputs.
 A Monte Carlo check over 3000 keys also compares the GPU's first emitted
 token with the target distribution directly (chi-square), independent of the
 oracle.
+
+The filtered call (top-k / top-p, SpecPV App. D and E settings) is compared
+the same way against the oracle's filtered distributions, with the filters
+off it must equal the plain call bit for bit, and a Monte Carlo check
+confirms that no filtered-out token is ever emitted.
 """
 
 import sys
@@ -49,7 +54,8 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-def gpu_run(parents, draft, logits, temperature, seed, step, dtype="bf16", stride_pad=0):
+def gpu_run(parents, draft, logits, temperature, seed, step, dtype="bf16", stride_pad=0,
+            filt=None):
     if dtype == "bf16":
         lg = dev_bf16(logits)
     else:
@@ -60,13 +66,19 @@ def gpu_run(parents, draft, logits, temperature, seed, step, dtype="bf16", strid
         big[:, :, :v] = lg
         lg = big[:, :, :v]
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
-    alen, path, bonus = binding.stochastic_accept(lg, dev_i32(parents), dev_i32(draft),
-                                                  temperature, seed=seed, step=step, dev_err=err)
+    if filt is None:
+        alen, path, bonus = binding.stochastic_accept(lg, dev_i32(parents), dev_i32(draft),
+                                                      temperature, seed=seed, step=step,
+                                                      dev_err=err)
+    else:
+        alen, path, bonus = binding.stochastic_accept_filtered(
+            lg, dev_i32(parents), dev_i32(draft), temperature, top_k=filt[0], top_p=filt[1],
+            seed=seed, step=step, dev_err=err)
     torch.cuda.synchronize()
     return alen.cpu().numpy(), path.cpu().numpy(), bonus.cpu().numpy(), int(err.item())
 
 
-def check_against_oracle(parents, draft, logits, temperature, seed, step, got):
+def check_against_oracle(parents, draft, logits, temperature, seed, step, got, filt=(0, 1.0)):
     alen, path, bonus = got[:3]
     bsz = parents.shape[0]
 
@@ -79,7 +91,8 @@ def check_against_oracle(parents, draft, logits, temperature, seed, step, got):
         return u in gp and gp.index(u) + 1 < len(gp) and gp[gp.index(u) + 1] == c
 
     a, p, y, events = ST.stochastic_accept(logits, parents, draft, temperature, seed, step,
-                                           return_events=True, decide=decide)
+                                           return_events=True, decide=decide, top_k=filt[0],
+                                           top_p=filt[1])
     assert np.array_equal(alen, a), f"accept_len {alen} vs oracle {a}"
     assert np.array_equal(path, p)
     for b in range(bsz):
@@ -87,7 +100,7 @@ def check_against_oracle(parents, draft, logits, temperature, seed, step, got):
             continue
         # only a draw within TOL of the boundary between the two tokens may differ
         _, u, _, unif, rest, target = events[b][-1]
-        probs = ST.target_probs(logits[b, u], temperature)
+        probs = ST.target_probs(logits[b, u], temperature, filt[0], filt[1])
         removed = {int(draft[b, c]) for (kind, uu, c, *_r) in events[b][:-1]
                    if kind == "child" and uu == u and 0 <= int(draft[b, c]) < probs.shape[0]}
         resid = probs.copy()
@@ -200,3 +213,85 @@ def test_first_token_is_distributed_as_the_target():
     assert stats.chisquare(counts, p * trials).pvalue > 1e-4
     # the repeated sibling (node 3) is never accepted
     assert not np.any((r[:, 0] >= 1) & (r[:, 1] == 3))
+
+
+# top-k / top-p: the pages' settings (SpecPV App. D: T 0.6, top-k 20, top-p
+# 0.95; App. E: T 0.7 / 1.0, top-p 0.9) and edge values
+FILTER_CASES = [
+    # seed, batch, n_nodes, vocab, dtype, temperature, tree, top_k, top_p, logit lean
+    # (lean (3, 7): top-k 20 keeps 10-21 tokens, top-p 0.9 about 55000 of 128256;
+    # lean (9, 16): rows peaked on one token)
+    (21, 4, 60, 128256, "bf16", 0.6, "eagle", 20, 0.95, (3.0, 7.0)),
+    (22, 4, 60, 128256, "bf16", 0.7, "eagle", 0, 0.9, (3.0, 7.0)),
+    (23, 2, 60, 128256, "bf16", 1.0, "eagle", 0, 0.9, (9.0, 16.0)),
+    (24, 3, 96, 32000, "bf16", 0.7, "random", 50, 1.0, (3.0, 7.0)),
+    (25, 2, 17, 1000, "f32", 0.7, "chain", 5, 0.8, (1.0, 3.0)),
+    (26, 2, 64, 4099, "f32", 0.6, "random", 1, 1.0, (9.0, 16.0)),
+    (27, 2, 33, 5003, "bf16", 1.0, "random", 3000, 0.5, (1.0, 3.0)),
+    (28, 1, 1, 128256, "bf16", 0.6, "eagle", 20, 0.95, (3.0, 7.0)),
+]
+
+
+@pytest.mark.parametrize("case", FILTER_CASES, ids=lambda c: f"seed{c[0]}")
+def test_filtered_sampling_matches_oracle(case):
+    # The GPU's top-p masses are fp32 exponentials in 2^-40 fixed point: a
+    # tail token whose larger tokens hold within ~1e-6 of top_p may be kept
+    # on one side only.  Such tokens carry ~1e-6 of probability, so they
+    # change the renormalised probabilities by far less than TOL and are
+    # drawn with probability ~1e-6; the comparison below is unaffected.
+    seed, batch, n, vocab, dtype, temp, tree, top_k, top_p, lean = case
+    _say(f"[stochastic filtered] seed {seed} batch {batch} N {n} V {vocab} {dtype} T {temp} "
+         f"top-k {top_k} top-p {top_p}")
+    parents, draft, logits = W.make_sampling_case(seed, batch=batch, n_nodes=n, vocab=vocab,
+                                                  dtype=dtype, tree=tree, lean=lean)
+    for step in (0, 3):
+        got = gpu_run(parents, draft, logits, temp, (seed, 5), step, dtype, filt=(top_k, top_p))
+        assert got[3] == 0
+        check_against_oracle(parents, draft, logits, temp, (seed, 5), step, got,
+                             filt=(top_k, top_p))
+
+
+def test_filters_off_equal_the_unfiltered_call():
+    _say("[stochastic filtered] top-k 0 / >= V and top-p 1 equal tv_stochastic_accept")
+    parents, draft, logits = W.make_sampling_case(3, batch=3, n_nodes=40, vocab=5000,
+                                                  dtype="bf16", tree="random")
+    base = gpu_run(parents, draft, logits, 0.8, (9, 9), 2, "bf16")
+    for filt in ((0, 1.0), (5000, 1.0), (9999, 1.0)):
+        got = gpu_run(parents, draft, logits, 0.8, (9, 9), 2, "bf16", filt=filt)
+        for x, y in zip(got[:3], base[:3]):
+            assert np.array_equal(x, y), filt
+
+
+def test_filtered_first_token_is_distributed_as_the_filtered_target():
+    # independent of the walk oracle: chi-square of the first emitted token
+    _say("[stochastic filtered] Monte Carlo of the first emitted token")
+    vocab, temp, top_k, top_p = 12, 0.8, 6, 0.8
+    rng = np.random.default_rng(31)
+    rows = rng.normal(0, 1.5, size=(4, vocab)).astype(np.float32)
+    parents = np.array([[-1, 0, 0, 0]], dtype=np.int32)
+    # drafts: a kept token, a filtered-out token, a repeated one
+    target = ST.target_probs(rows[0], temp, top_k, top_p)
+    kept, dropped = np.nonzero(target > 0)[0], np.nonzero(target == 0)[0]
+    draft = np.array([[0, kept[0], dropped[0], kept[0]]], dtype=np.int32)
+    lg = torch.from_numpy(rows.copy()).cuda().view(1, 4, vocab)
+    par_d, dr_d = dev_i32(parents), dev_i32(draft)
+    ws = torch.empty(binding.stochastic_accept_workspace_size(1, 4, vocab), dtype=torch.uint8,
+                     device="cuda")
+    outs = (torch.empty(1, dtype=torch.int32, device="cuda"),
+            torch.empty((1, 4), dtype=torch.int32, device="cuda"),
+            torch.empty(1, dtype=torch.int32, device="cuda"))
+    trials = 3000
+    res = torch.empty((trials, 3), dtype=torch.int32, device="cuda")
+    for k in range(trials):
+        binding.stochastic_accept_filtered(lg, par_d, dr_d, temp, top_k=top_k, top_p=top_p,
+                                           seed=(k, 777), step=0, workspace=ws, outputs=outs)
+        res[k, 0] = outs[0][0]
+        res[k, 1] = outs[1][0, 1]
+        res[k, 2] = outs[2][0]
+    r = res.cpu().numpy()
+    firsts = np.array([int(draft[0, node1]) if alen >= 1 else int(bonus) for alen, node1, bonus in r])
+    # never a filtered-out token, never the filtered-out or repeated child
+    assert np.all(target[firsts] > 0)
+    assert not np.any((r[:, 0] >= 1) & ((r[:, 1] == 2) | (r[:, 1] == 3)))
+    counts = np.bincount(firsts, minlength=vocab)[kept]
+    assert stats.chisquare(counts, target[kept] * trials).pvalue > 1e-4

@@ -135,6 +135,10 @@ def lib() -> ctypes.CDLL:
                                                ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64,
                                                ctypes.c_uint64, vp, vp, vp, vp, sz, vp, vp]
             L.tv_stochastic_accept.restype = i32
+            L.tv_stochastic_accept_filtered.argtypes = [
+                vp, i32, i64, i64, vp, vp, i32, i32, ctypes.c_float, i32, ctypes.c_float,
+                ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, vp, vp, vp, vp, sz, vp, vp]
+            L.tv_stochastic_accept_filtered.restype = i32
             L.tv_status_string.argtypes = [i32]
             L.tv_status_string.restype = ctypes.c_char_p
             L.tv_version.argtypes = []
@@ -465,6 +469,22 @@ def stochastic_accept(logits, parents, draft_tokens, temperature, *, seed=(0, 0)
                       vocab=None, workspace=None, dev_err=None, outputs=None):
     """Speculative sampling along the tree at temperature > 0 ->
     (accept_len [B], accept_path [B][N], bonus [B]), int32."""
+    return _stochastic(logits, parents, draft_tokens, temperature, None, seed, step, vocab,
+                       workspace, dev_err, outputs)
+
+
+def stochastic_accept_filtered(logits, parents, draft_tokens, temperature, *, top_k=0,
+                               top_p=1.0, seed=(0, 0), step=0, vocab=None, workspace=None,
+                               dev_err=None, outputs=None):
+    """tv_stochastic_accept_filtered: speculative sampling along the tree
+    from the top-k / top-p filtered distributions (top_k = 0: off; top_p =
+    1: off) -> (accept_len, accept_path, bonus)."""
+    return _stochastic(logits, parents, draft_tokens, temperature, (int(top_k), float(top_p)),
+                       seed, step, vocab, workspace, dev_err, outputs)
+
+
+def _stochastic(logits, parents, draft_tokens, temperature, filt, seed, step, vocab, workspace,
+                dev_err, outputs):
     _on_gpu("logits", logits, (torch.bfloat16, torch.float32), contiguous=False)
     _on_gpu("parents", parents, torch.int32)
     _on_gpu("draft_tokens", draft_tokens, torch.int32)
@@ -486,11 +506,17 @@ def stochastic_accept(logits, parents, draft_tokens, temperature, *, seed=(0, 0)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     mask64 = (1 << 64) - 1
-    _check("tv_stochastic_accept", lib().tv_stochastic_accept(
-        _ptr(logits), dt, v, int(logits.stride(1)), _ptr(parents), _ptr(draft_tokens), bsz, n,
-        float(temperature), int(seed[0]) & mask64, int(seed[1]) & mask64, int(step) & mask64,
-        _ptr(alen), _ptr(path), _ptr(bonus), _ptr(workspace), workspace.numel(),
-        _err_ptr(dev_err), _stream(dev)))
+    seeds = (int(seed[0]) & mask64, int(seed[1]) & mask64, int(step) & mask64)
+    if filt is None:
+        _check("tv_stochastic_accept", lib().tv_stochastic_accept(
+            _ptr(logits), dt, v, int(logits.stride(1)), _ptr(parents), _ptr(draft_tokens), bsz, n,
+            float(temperature), *seeds, _ptr(alen), _ptr(path), _ptr(bonus), _ptr(workspace),
+            workspace.numel(), _err_ptr(dev_err), _stream(dev)))
+    else:
+        _check("tv_stochastic_accept_filtered", lib().tv_stochastic_accept_filtered(
+            _ptr(logits), dt, v, int(logits.stride(1)), _ptr(parents), _ptr(draft_tokens), bsz, n,
+            float(temperature), filt[0], filt[1], *seeds, _ptr(alen), _ptr(path), _ptr(bonus),
+            _ptr(workspace), workspace.numel(), _err_ptr(dev_err), _stream(dev)))
     return alen, path, bonus
 
 

@@ -244,6 +244,21 @@ tv_status tv_stochastic_accept(const void* logits, tv_dtype dtype, int64_t vocab
                                int32_t* accept_len, int32_t* accept_path, int32_t* bonus_token,
                                void* workspace, size_t workspace_bytes, int32_t* dev_err,
                                hipStream_t stream) {
+  return tv_stochastic_accept_filtered(logits, dtype, vocab, row_stride, parents, draft_tokens,
+                                       batch, n_nodes, temperature, 0, 1.f, seed0, seed1, step,
+                                       accept_len, accept_path, bonus_token, workspace,
+                                       workspace_bytes, dev_err, stream);
+}
+
+tv_status tv_stochastic_accept_filtered(const void* logits, tv_dtype dtype, int64_t vocab,
+                                        int64_t row_stride, const int32_t* parents,
+                                        const int32_t* draft_tokens, int32_t batch,
+                                        int32_t n_nodes, float temperature, int32_t top_k,
+                                        float top_p, uint64_t seed0, uint64_t seed1,
+                                        uint64_t step, int32_t* accept_len, int32_t* accept_path,
+                                        int32_t* bonus_token, void* workspace,
+                                        size_t workspace_bytes, int32_t* dev_err,
+                                        hipStream_t stream) {
   if (!logits || !parents || !draft_tokens || !accept_len || !accept_path || !bonus_token ||
       !workspace)
     return TV_ERR_NULL;
@@ -251,13 +266,14 @@ tv_status tv_stochastic_accept(const void* logits, tv_dtype dtype, int64_t vocab
   if (batch < 0 || n_nodes < 1 || n_nodes > TV_MAX_NODES) return TV_ERR_SHAPE;
   if (vocab < 1 || vocab >= INT_MAX || row_stride < vocab) return TV_ERR_SHAPE;
   if (!(temperature > 0.f) || std::isinf(temperature)) return TV_ERR_SHAPE;
+  if (top_k < 0 || !(top_p > 0.f && top_p <= 1.f)) return TV_ERR_SHAPE;
   if (batch == 0) return TV_OK;
   const tv::AcceptPlan plan = tv::plan_stochastic(batch, n_nodes, vocab);
   if (!aligned(workspace, 16) || workspace_bytes < plan.ws_bytes) return TV_ERR_WORKSPACE;
   return launch_status(tv::launch_stochastic(logits, dtype, vocab, row_stride, parents,
-                                             draft_tokens, batch, n_nodes, temperature, seed0,
-                                             seed1, step, accept_len, accept_path, bonus_token,
-                                             workspace, plan, dev_err, stream));
+                                             draft_tokens, batch, n_nodes, temperature, top_k,
+                                             top_p, seed0, seed1, step, accept_len, accept_path,
+                                             bonus_token, workspace, plan, dev_err, stream));
 }
 
 tv_status tv_commit_kv(const void* k_tree, const void* v_tree, const int32_t* accept_path,

@@ -80,10 +80,10 @@ AcceptPlan plan_stochastic(int batch, int n, int64_t vocab);
 
 hipError_t launch_stochastic(const void* logits, tv_dtype dt, int64_t vocab, int64_t row_stride,
                              const int32_t* parents, const int32_t* draft, int batch, int n,
-                             float temperature, uint64_t seed0, uint64_t seed1, uint64_t step,
-                             int32_t* accept_len, int32_t* accept_path, int32_t* bonus,
-                             void* workspace, const AcceptPlan& plan, int32_t* dev_err,
-                             hipStream_t stream);
+                             float temperature, int top_k, float top_p, uint64_t seed0,
+                             uint64_t seed1, uint64_t step, int32_t* accept_len,
+                             int32_t* accept_path, int32_t* bonus, void* workspace,
+                             const AcceptPlan& plan, int32_t* dev_err, hipStream_t stream);
 
 struct SelectPlan {
   int nb_cap;        // summary records per (sequence, kv head): ceil(capacity / block_size)

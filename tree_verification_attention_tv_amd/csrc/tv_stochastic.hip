@@ -6,20 +6,31 @@
 // numbers: Philox-4x64-10 (Salmon et al., SC 2011) on counters, so every
 // decision has a fixed uniform.
 //
-// Node u's target distribution is p_u = softmax(l_u / T).  Drafts are point
-// masses: at an accepted node the children are tried in ascending node
+// Node u's target distribution is p_u = softmax(l_u / T), optionally
+// filtered (SpecPV App. D: T 0.6, top-p 0.95, top-k 20; App. E: T 0.7 and
+// 1.0, top-p 0.9): top-k keeps the tokens with fewer than k strictly larger
+// logits, then top-p keeps, of those, the tokens whose strictly larger ones
+// hold less than p of their mass, and the kept probabilities are
+// renormalised.  Both keep every token at or above a logit threshold tau, so
+// the filter is one value per row.  Drafts are point masses: at an accepted node the children are tried in ascending node
 // index, child c (token x) is accepted with probability p_u(x) / R, R the
 // mass not yet rejected at u (a token already rejected at u has probability
 // 0).  When every child is rejected the bonus token is drawn from the
 // residual by inverse CDF in vocabulary order.
 //
-// Two kernels:
+// Kernels:
+//  0. filter_threshold_kernel (only with a filter): one 1024-thread
+//     workgroup per row finds tau by radix selection over order-preserving
+//     32-bit keys of the logits (11-bit digits, histograms in LDS): top-k by
+//     counts, then top-p by masses 2^((l - M) c) in 2^-40 fixed point (integer
+//     sums, so the result does not depend on the order of the atomics).
 //  1. softmax_stats_kernel: one workgroup per (row chunk, logits row), the
 //     same streaming layout as the greedy argmax: each thread's 16-byte loads
 //     are all in flight at once.  Per chunk it writes (m, s): the chunk's max
 //     logit and sum_v 2^((l_v - m) c), c = log2(e) / T, summed in a fixed
-//     order (thread, then DPP/lane tree, then waves in order).  HBM-bound:
-//     the B*N*V logits are read once.
+//     order (thread, then DPP/lane tree, then waves in order), over the
+//     tokens at or above the row's tau.  HBM-bound: the B*N*V logits are read
+//     once.
 //  2. stochastic_walk_kernel: one workgroup per sequence.  Every input of
 //     the walk is fetched in parallel first: each node's row statistics
 //     (M, Z), the probability of its draft token at its parent and its
@@ -140,6 +151,7 @@ __global__ __launch_bounds__(kThreads) void softmax_stats_kernel(const T* __rest
                                                                  int64_t vocab, int64_t row_stride,
                                                                  int64_t chunk_len, int chunks,
                                                                  float c2,
+                                                                 const float* __restrict__ tau,
                                                                  float2* __restrict__ stats) {
   constexpr int VEC = 16 / sizeof(T);
   constexpr int U = kUnroll * 8 / VEC;
@@ -192,10 +204,11 @@ __global__ __launch_bounds__(kThreads) void softmax_stats_kernel(const T* __rest
   for (int w = 1; w < kWaves; ++w) m = fmaxf(m, s_red[w]);
   __syncthreads();
   float s = 0.f;
+  const float lo = tau ? tau[row] : -INFINITY;  // kept: l >= lo
 #pragma unroll
   for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) s += exp2f((v[u][e] - m) * c2);  // -inf -> 0
+    for (int e = 0; e < VEC; ++e) s += v[u][e] >= lo ? exp2f((v[u][e] - m) * c2) : 0.f;  // -inf -> 0
   s = wave_sum(s);
   if (lane == 0) s_red[wave] = s;
   __syncthreads();
@@ -207,6 +220,258 @@ __global__ __launch_bounds__(kThreads) void softmax_stats_kernel(const T* __rest
   }
 }
 
+// ---- kernel 0: the filter's threshold -------------------------------------------------
+constexpr int kFiltThreads = 1024;
+constexpr int kFiltWaves = kFiltThreads / kWave;
+constexpr int kBinBits = 11;
+constexpr int kBins = 1 << kBinBits;
+constexpr float kFix = 1099511627776.0f;  // 2^40: masses in fixed point
+constexpr int kCand = 4096;                // top-k candidate list in LDS
+
+// Order-preserving key of a logit: larger value, larger key; -0 and +0 share
+// the key of +0 (they compare equal).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f == 0.f ? 0.f : f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Wave 0 over a descending scan of the 2^bits bins: the largest bin d with
+// above + sum(hist[d..]) >= target (target = frac * total when frac > 0),
+// and the mass strictly above it (*s_sel = -1 when even the whole range
+// falls short); *s_total gets the histogram's total.
+__device__ void select_bin(const unsigned long long* hist, int nbins, unsigned long long above,
+                           double target, double frac, int* s_sel,
+                           unsigned long long* s_above, unsigned long long* s_total) {
+  const int lane = threadIdx.x;  // wave 0 only
+  // bins per lane (lane 0 the top ones); with fewer bins than lanes, one
+  // bin per lane and the lanes past them empty
+  const int per = nbins >= kWave ? nbins / kWave : 1;
+  const int hi = nbins - 1 - lane * per;
+  unsigned long long mine = 0;
+  for (int j = 0; j < per && hi - j >= 0; ++j) mine += hist[hi - j];
+  // inclusive scan in lane order (descending bins)
+  unsigned long long incl = mine;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const unsigned long long o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  const unsigned long long total = __shfl(incl, kWave - 1);
+  if (lane == 0) *s_total = total;
+  if (frac > 0.0) target = frac * (double)total;
+  const bool cross = (double)(above + incl) >= target;
+  const uint64_t ball = __ballot(cross);
+  if (ball == 0) {
+    if (lane == 0) {
+      *s_sel = -1;
+      *s_above = above + total;
+    }
+    return;
+  }
+  const int l = __builtin_ctzll(ball);
+  if (lane == l) {
+    unsigned long long run = above + incl - mine;
+    int d = hi;
+    for (int j = 0; j < per && hi - j >= 0; ++j) {
+      d = hi - j;
+      if ((double)(run + hist[d]) >= target) break;
+      run += hist[d];
+    }
+    *s_sel = d;
+    *s_above = run;
+  }
+}
+
+template <typename T, bool kVector>
+__global__ __launch_bounds__(kFiltThreads) void filter_threshold_kernel(
+    const T* __restrict__ logits, int64_t vocab, int64_t row_stride, int top_k, float top_p,
+    float c2, float* __restrict__ tau) {
+  constexpr int VEC = 16 / sizeof(T);
+  __shared__ unsigned long long hist[kBins];
+  __shared__ uint32_t c_key[kCand];  // candidates: the elements at or above a lower bound
+  __shared__ float c_val[kCand];
+  __shared__ int s_ncand;
+  __shared__ float s_red[kFiltWaves];
+  __shared__ int s_sel;
+  __shared__ unsigned long long s_above, s_total;
+  const int64_t row = blockIdx.x;
+  const T* src = logits + row * row_stride;
+  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
+  // Every value of the row this thread owns: elements k0 .. k0 + VEC - 1 for
+  // k0 = (t + i * kFiltThreads) * VEC, read with 8 loads in flight per
+  // thread (the row stays in L2 between passes).
+  typedef T vec_t __attribute__((ext_vector_type(VEC)));
+  constexpr int kBatch = 8;
+  auto visit = [&](auto&& f) {
+    for (int b0 = t * VEC; b0 < (int)vocab; b0 += kBatch * kFiltThreads * VEC) {
+      vec_t x[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int k0 = b0 + i * kFiltThreads * VEC;
+        if (kVector && k0 + VEC <= (int)vocab) {
+          x[i] = *reinterpret_cast<const vec_t*>(src + k0);
+        } else {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) x[i][e] = k0 + e < (int)vocab ? src[k0 + e] : (T)0.f;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int k0 = b0 + i * kFiltThreads * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          if (k0 + e < (int)vocab) f(to_f32<T>(x[i][e]));
+      }
+    }
+  };
+  // digits of the key, high first: bf16 values fill the top 16 bits
+  constexpr int kDigits = sizeof(T) == 2 ? 2 : 3;
+  const int shifts[3] = {21, sizeof(T) == 2 ? 16 : 10, 0};
+  const int widths[3] = {11, sizeof(T) == 2 ? 5 : 11, 10};
+
+  auto clear = [&]() {
+    for (int i = t; i < kBins; i += kFiltThreads) hist[i] = 0ull;
+    __syncthreads();
+  };
+  // Element sources: f(key, value) for every element of the row, or of the
+  // candidate list collected in LDS (below).
+  auto row_src = [&](auto&& f) { visit([&](float v) { f(order_key(v), v); }); };
+  auto cand_src = [&](auto&& f) {
+    const int nc = s_ncand;
+    for (int i = t; i < nc; i += kFiltThreads) f(c_key[i], c_val[i]);
+  };
+
+  // ---- the row's maximum, and each thread's own maximum ----
+  float m_t = -INFINITY;  // a thread without elements offers -inf
+  visit([&](float v) { m_t = fmaxf(m_t, v); });
+  {
+    const float wm = wave_max(m_t);
+    if (lane == 0) s_red[wave] = wm;
+    __syncthreads();
+  }
+  float M = s_red[0];
+  for (int w = 1; w < kFiltWaves; ++w) M = fmaxf(M, s_red[w]);
+
+  // ---- top-k: the k-th largest key (ties at it are kept) ----
+  // kth(src): the top_k-th largest of the keys src hands over (radix
+  // selection, counts in LDS)
+  auto kth = [&](auto&& src) -> uint32_t {
+    uint32_t prefix = 0u, fixed = 0u;
+    unsigned long long above = 0ull;
+    for (int g = 0; g < kDigits; ++g) {
+      const int sh = shifts[g], mask = (1 << widths[g]) - 1;
+      clear();
+      src([&](uint32_t key, float) {
+        if ((key & fixed) == prefix) atomicAdd(&hist[(key >> sh) & mask], 1ull);
+      });
+      __syncthreads();
+      if (wave == 0)
+        select_bin(hist, mask + 1, above, (double)top_k, 0.0, &s_sel, &s_above, &s_total);
+      __syncthreads();
+      prefix |= (uint32_t)s_sel << sh;  // a count of >= top_k always exists
+      fixed |= (uint32_t)mask << sh;
+      above = s_above;
+      __syncthreads();
+    }
+    return prefix;
+  };
+  uint32_t tau_k = 0u;
+  bool use_cand = false;  // every key >= tau_k is in the candidate list
+  if (top_k > 0 && (int64_t)top_k < vocab) {
+    // A lower bound first: the top_k-th largest of the threads' maxima (top_k
+    // threads hold an element at or above it, so the answer is at or above
+    // it too).  The elements at or above it are few: they are collected
+    // once into LDS, and the selections run on them instead of the row.
+    uint32_t lower = 0u;
+    if (top_k <= kFiltThreads) {
+      const uint32_t mk = order_key(m_t);
+      lower = kth([&](auto&& f) { f(mk, m_t); });
+      if (t == 0) s_ncand = 0;
+      __syncthreads();
+      visit([&](float v) {
+        const uint32_t key = order_key(v);
+        const bool c = key >= lower;
+        const uint64_t bal = __ballot(c);
+        if (bal) {  // one atomic per wave and element slot
+          const int leader = __builtin_ctzll(bal);
+          int base = 0;
+          if (lane == leader) base = atomicAdd(&s_ncand, __builtin_popcountll(bal));
+          base = __shfl(base, leader);
+          if (c) {
+            const int i = base + __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+            if (i < kCand) {
+              c_key[i] = key;
+              c_val[i] = v;
+            }
+          }
+        }
+      });
+      __syncthreads();
+      use_cand = s_ncand <= kCand;  // else (many ties) the row is used
+      __syncthreads();
+    }
+    if (use_cand) {
+      tau_k = kth(cand_src);
+    } else {
+      tau_k = kth([&](auto&& f) {
+        row_src([&](uint32_t key, float v) {
+          if (key >= lower) f(key, v);
+        });
+      });
+    }
+  }
+
+  // ---- top-p: the last key (descending) whose strictly larger keys hold
+  // less than top_p of the mass kept by top-k ----
+  uint32_t tau_p = 0u;
+  if (top_p < 1.f) {
+    uint32_t prefix = 0u, fixed = 0u;
+    unsigned long long above = 0ull;
+    double target = 0.0;
+    bool whole = false;  // every remaining key is kept
+    auto pass = [&](auto&& src, int sh, int mask) {
+      src([&](uint32_t key, float v) {
+        if (key >= tau_k && (key & fixed) == prefix) {
+          const unsigned long long w = (unsigned long long)(exp2f((v - M) * c2) * kFix);
+          atomicAdd(&hist[(key >> sh) & mask], w);
+        }
+      });
+    };
+    for (int g = 0; g < kDigits && !whole; ++g) {
+      const int sh = shifts[g], mask = (1 << widths[g]) - 1;
+      clear();
+      if (use_cand)
+        pass(cand_src, sh, mask);
+      else
+        pass(row_src, sh, mask);
+      __syncthreads();
+      // the first digit's histogram holds the whole kept mass: target = top_p * it
+      if (wave == 0)
+        select_bin(hist, mask + 1, above, target, g == 0 ? (double)top_p : 0.0, &s_sel, &s_above,
+                   &s_total);
+      __syncthreads();
+      if (g == 0) target = (double)top_p * (double)s_total;
+      if (s_sel < 0) {
+        whole = true;  // rounding: the range holds less than the target, keep it all
+      } else {
+        prefix |= (uint32_t)s_sel << sh;
+        fixed |= (uint32_t)mask << sh;
+        above = s_above;
+      }
+      __syncthreads();
+    }
+    tau_p = prefix;
+  }
+  if (t == 0) {
+    const bool any = (top_k > 0 && (int64_t)top_k < vocab) || top_p < 1.f;
+    tau[row] = any ? key_value(tau_k > tau_p ? tau_k : tau_p) : -INFINITY;
+  }
+}
+
 // ---- kernel 2: the walk ------------------------------------------------------------------
 struct WalkArgs {
   const void* logits;
@@ -214,6 +479,7 @@ struct WalkArgs {
   int chunks;
   float c2;
   const float2* stats;
+  const float* tau;  // per row: the filter's threshold, or null (no filter)
   const int32_t* parents;
   const int32_t* draft;
   int n;
@@ -340,7 +606,8 @@ __global__ __launch_bounds__(kWalkThreads) void stochastic_walk_kernel(WalkArgs 
     s_next[t] = nx;
     const bool valid = tok >= 0 && (int64_t)tok < a.vocab && !repeated;
     const float l = valid ? to_f32<T>(logits[(row0 + par) * a.row_stride + tok]) : 0.f;
-    s_p[t] = valid ? exp2f((l - s_M[par]) * a.c2) / s_Z[par] : 0.f;
+    const float lo = a.tau ? a.tau[row0 + par] : -INFINITY;  // filtered out below lo
+    s_p[t] = valid && l >= lo ? exp2f((l - s_M[par]) * a.c2) / s_Z[par] : 0.f;
     s_u[t] = philox_uniform(a.step, (uint64_t)b, (uint64_t)par, (uint64_t)rank, a.k0, a.k1);
   }
   // the bonus uniforms on other waves (other SIMDs) than the acceptance ones:
@@ -429,8 +696,10 @@ __global__ __launch_bounds__(kWalkThreads) void stochastic_walk_kernel(WalkArgs 
   float q[kPer];
   load_span<T, kVector>(logits + row * a.row_stride, my0, hi, q);
   const float c2 = a.c2;
+  const float lo_u = a.tau ? a.tau[row] : -INFINITY;
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) q[e] = my0 + e < hi ? exp2f((q[e] - M) * c2) * inv_z : 0.f;
+  for (int e = 0; e < kPer; ++e)
+    q[e] = my0 + e < hi && q[e] >= lo_u ? exp2f((q[e] - M) * c2) * inv_z : 0.f;
   // rejected children's tokens leave the residual
   if (!bad)
     for (int k = s_first[u]; k != INT_MAX; k = s_next[k]) {
@@ -492,41 +761,45 @@ AcceptPlan plan_stochastic(int batch, int n, int64_t vocab) {
   static_assert((int64_t)kThreads * 8 * kUnroll <= (int64_t)kWalkThreads * kPer, "bonus scan size");
   p.chunk_len = chunk;
   p.chunks = (int)((vocab + chunk - 1) / chunk);
-  p.ws_bytes = (size_t)batch * n * p.chunks * sizeof(float2) + 256;
+  // chunk statistics, then one threshold per row
+  const size_t rows = (size_t)batch * n;
+  p.ws_bytes = ((rows * p.chunks * sizeof(float2) + 255) / 256) * 256 + rows * sizeof(float) + 256;
   return p;
 }
 
+namespace {
+
+template <typename T, bool kVector>
+void launch_typed(const void* logits, int64_t vocab, int64_t row_stride, int batch, int n,
+                  float c2, int top_k, float top_p, const AcceptPlan& plan, float2* stats,
+                  float* tau, const WalkArgs& w, hipStream_t stream) {
+  const unsigned rows = (unsigned)((size_t)batch * n);
+  if (tau)
+    hipLaunchKernelGGL((filter_threshold_kernel<T, kVector>), dim3(rows), dim3(kFiltThreads), 0,
+                       stream, (const T*)logits, vocab, row_stride, top_k, top_p, c2, tau);
+  hipLaunchKernelGGL((softmax_stats_kernel<T, kVector>), dim3(plan.chunks, rows), dim3(kThreads),
+                     0, stream, (const T*)logits, vocab, row_stride, plan.chunk_len, plan.chunks,
+                     c2, (const float*)tau, stats);
+  hipLaunchKernelGGL((stochastic_walk_kernel<T, kVector>), dim3(batch), dim3(kWalkThreads), 0,
+                     stream, w);
+}
+
+}  // namespace
+
 hipError_t launch_stochastic(const void* logits, tv_dtype dt, int64_t vocab, int64_t row_stride,
                              const int32_t* parents, const int32_t* draft, int batch, int n,
-                             float temperature, uint64_t seed0, uint64_t seed1, uint64_t step,
-                             int32_t* accept_len, int32_t* accept_path, int32_t* bonus,
-                             void* workspace, const AcceptPlan& plan, int32_t* dev_err,
-                             hipStream_t stream) {
+                             float temperature, int top_k, float top_p, uint64_t seed0,
+                             uint64_t seed1, uint64_t step, int32_t* accept_len,
+                             int32_t* accept_path, int32_t* bonus, void* workspace,
+                             const AcceptPlan& plan, int32_t* dev_err, hipStream_t stream) {
+  const size_t rows = (size_t)batch * n;
   float2* stats = reinterpret_cast<float2*>(workspace);
+  const bool filtered = (top_k > 0 && (int64_t)top_k < vocab) || top_p < 1.f;
+  float* tau = filtered ? reinterpret_cast<float*>(
+                              reinterpret_cast<char*>(workspace) +
+                              ((rows * plan.chunks * sizeof(float2) + 255) / 256) * 256)
+                        : nullptr;
   const float c2 = kLog2e / temperature;
-  const dim3 grid(plan.chunks, (unsigned)((size_t)batch * n));
-  const uintptr_t addr = reinterpret_cast<uintptr_t>(logits);
-  if (dt == TV_BF16) {
-    if ((addr % 16 == 0) && (row_stride % 8 == 0))
-      hipLaunchKernelGGL((softmax_stats_kernel<bf16, true>), grid, dim3(kThreads), 0, stream,
-                         (const bf16*)logits, vocab, row_stride, plan.chunk_len, plan.chunks, c2,
-                         stats);
-    else
-      hipLaunchKernelGGL((softmax_stats_kernel<bf16, false>), grid, dim3(kThreads), 0, stream,
-                         (const bf16*)logits, vocab, row_stride, plan.chunk_len, plan.chunks, c2,
-                         stats);
-  } else {
-    if ((addr % 16 == 0) && (row_stride % 4 == 0))
-      hipLaunchKernelGGL((softmax_stats_kernel<float, true>), grid, dim3(kThreads), 0, stream,
-                         (const float*)logits, vocab, row_stride, plan.chunk_len, plan.chunks, c2,
-                         stats);
-    else
-      hipLaunchKernelGGL((softmax_stats_kernel<float, false>), grid, dim3(kThreads), 0, stream,
-                         (const float*)logits, vocab, row_stride, plan.chunk_len, plan.chunks, c2,
-                         stats);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   WalkArgs w{};
   w.logits = logits;
   w.vocab = vocab;
@@ -535,6 +808,7 @@ hipError_t launch_stochastic(const void* logits, tv_dtype dt, int64_t vocab, int
   w.chunks = plan.chunks;
   w.c2 = c2;
   w.stats = stats;
+  w.tau = tau;
   w.parents = parents;
   w.draft = draft;
   w.n = n;
@@ -545,20 +819,21 @@ hipError_t launch_stochastic(const void* logits, tv_dtype dt, int64_t vocab, int
   w.accept_path = accept_path;
   w.bonus = bonus;
   w.dev_err = dev_err;
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(logits);
   if (dt == TV_BF16) {
     if ((addr % 16 == 0) && (row_stride % 8 == 0))
-      hipLaunchKernelGGL((stochastic_walk_kernel<bf16, true>), dim3(batch), dim3(kWalkThreads), 0,
-                         stream, w);
+      launch_typed<bf16, true>(logits, vocab, row_stride, batch, n, c2, top_k, top_p, plan, stats,
+                               tau, w, stream);
     else
-      hipLaunchKernelGGL((stochastic_walk_kernel<bf16, false>), dim3(batch), dim3(kWalkThreads),
-                         0, stream, w);
+      launch_typed<bf16, false>(logits, vocab, row_stride, batch, n, c2, top_k, top_p, plan,
+                                stats, tau, w, stream);
   } else {
     if ((addr % 16 == 0) && (row_stride % 4 == 0))
-      hipLaunchKernelGGL((stochastic_walk_kernel<float, true>), dim3(batch), dim3(kWalkThreads),
-                         0, stream, w);
+      launch_typed<float, true>(logits, vocab, row_stride, batch, n, c2, top_k, top_p, plan,
+                                stats, tau, w, stream);
     else
-      hipLaunchKernelGGL((stochastic_walk_kernel<float, false>), dim3(batch), dim3(kWalkThreads),
-                         0, stream, w);
+      launch_typed<float, false>(logits, vocab, row_stride, batch, n, c2, top_k, top_p, plan,
+                                 stats, tau, w, stream);
   }
   return hipGetLastError();
 }
