@@ -185,3 +185,90 @@ def test_specpv_step_graph_replays_match_eager():
         torch.cuda.synchronize()
         for k, (got, want) in enumerate(zip(graphed.results(), ref)):
             assert torch.equal(got, want), f"replay {rep}: output {k} differs from the eager step"
+
+
+def test_multi_layer_and_filtered_calls_replay_to_eager():
+    """Three layers' attention, the layer-batched acceptance and commit, and
+    a filtered sampling call, captured once and replayed."""
+    print("[graph] multi-layer step and filtered sampling, capture and replay", flush=True)
+    import numpy as np
+    layers = 3
+    wl = W.make_random_case(91, batch=2, n_nodes=30, hq=8, hkv=2, d=128, prefix_lens=[700, 333],
+                            vocab=3000, p_match=0.7)
+    rng = np.random.default_rng(91)
+
+    def bf(a):
+        return torch.from_numpy(W.f32_to_bf16_bits(a.astype(np.float32)).view(np.int16)).cuda() \
+            .view(torch.bfloat16)
+
+    class Layered:
+        def __init__(self):
+            self.dw = DevWorkload(wl)
+            b, n = wl.parents.shape
+            cap = wl.capacity
+            self.q = bf(rng.standard_normal((layers,) + wl.q.shape) * 0.1)
+            self.kt = bf(rng.standard_normal((layers, b, n, 2, 128)))
+            self.vt = bf(rng.standard_normal((layers, b, n, 2, 128)))
+            self.kc = bf(rng.standard_normal((layers, b, 2, cap, 128)))
+            self.vc = bf(rng.standard_normal((layers, b, 2, cap, 128)))
+            self.out = torch.empty_like(self.q)
+            self.mask = torch.empty((b, n, 1), dtype=torch.int32, device="cuda")
+            self.err = torch.zeros(1, dtype=torch.int32, device="cuda")
+            self.acc = tuple(torch.empty(s, dtype=torch.int32, device="cuda")
+                             for s in ((b, n), (b,), (b, n), (b,)))
+            self.sto = tuple(torch.empty(s, dtype=torch.int32, device="cuda")
+                             for s in ((b,), (b, n), (b,)))
+            self.new_prefix = torch.empty_like(self.dw.prefix_len)
+            desc = binding.attn_desc(self.q[0], self.kc[0], max_prefix_len=wl.max_prefix_len)
+            self.ws_attn = torch.empty(binding.attention_workspace_size(desc), dtype=torch.uint8,
+                                       device="cuda")
+            self.ws_acc = torch.empty(binding.accept_workspace_size(b, n, wl.vocab),
+                                      dtype=torch.uint8, device="cuda")
+            self.ws_sto = torch.empty(binding.stochastic_accept_workspace_size(b, n, wl.vocab),
+                                      dtype=torch.uint8, device="cuda")
+
+        def run(self):
+            dw = self.dw
+            for l in range(layers):
+                binding.tree_attention(self.q[l], self.kc[l], self.vc[l], self.kt[l], self.vt[l],
+                                       dw.prefix_len, None, max_prefix_len=wl.max_prefix_len,
+                                       out=self.out[l], workspace=self.ws_attn, dev_err=self.err,
+                                       parents=dw.parents, mask_out=self.mask if l == 0 else None)
+            binding.greedy_accept_commit_layers(dw.logits, dw.parents, dw.draft, self.kt, self.vt,
+                                                dw.prefix_len, self.kc, self.vc,
+                                                new_prefix_len=self.new_prefix,
+                                                workspace=self.ws_acc, dev_err=self.err,
+                                                outputs=self.acc)
+            binding.stochastic_accept_filtered(dw.logits, dw.parents, dw.draft, 0.6, top_k=20,
+                                               top_p=0.95, seed=(4, 5), step=1,
+                                               workspace=self.ws_sto, dev_err=self.err,
+                                               outputs=self.sto)
+
+        def results(self):
+            return [self.mask, self.out.view(torch.int16), *self.acc, *self.sto, self.new_prefix,
+                    self.kc.view(torch.int16), self.vc.view(torch.int16), self.err]
+
+        def scramble(self):
+            for t in (self.mask, self.out.view(torch.int16), *self.acc, *self.sto,
+                      self.new_prefix):
+                t.fill_(-7)
+
+    eager = Layered()
+    rng = np.random.default_rng(91)   # identical inputs for the graphed copy
+    graphed = Layered()
+    eager.run()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in eager.results()]
+    assert int(eager.err.item()) == 0
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        graphed.run()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        graphed.scramble()
+        eager.run()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, (got, want) in enumerate(zip(graphed.results(), ref)):
+            assert torch.equal(got, want), f"replay {rep}: output {k} differs from the eager step"
