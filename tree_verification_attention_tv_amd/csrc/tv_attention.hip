@@ -310,6 +310,22 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
   } else if (tid < a.n) {
     par_t = a.parents[(int64_t)b * a.n + tid];
   }
+  // partial mode: the block ids this split can touch (the blocks of slots
+  // begin .. begin + chunk - 1, within the list), in the same round trip;
+  // which of them count is decided once the list length and the prefix
+  // length are known
+  constexpr int kBlkPer = kBlkCache / kSplitThreads;
+  int pre_blk[kBlkPer];
+  if (PARTIAL) {
+    const int pbi0 = begin / a.block_size;
+    const int pcount = min((begin + a.chunk - 1) / a.block_size - pbi0 + 1, a.max_blocks - pbi0);
+    const int32_t* blist = a.block_idx + (int64_t)b * a.max_blocks;
+#pragma unroll
+    for (int u = 0; u < kBlkPer; ++u) {
+      const int k = tid + u * kSplitThreads;
+      pre_blk[u] = k < pcount ? blist[pbi0 + k] : -1;
+    }
+  }
 
   int err = 0;
   const int p_len = clamped_prefix(a, b, &err);
@@ -383,17 +399,20 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
     if (bad && g == 0 && rg == 0 && tid == 0) raise_err(a.dev_err, TV_DERR_BAD_PARENT);
   }
   if (PARTIAL && np > 0) {
-    const int32_t* blist = a.block_idx + (int64_t)b * a.max_blocks;
     bi0 = begin / a.block_size;
     const int bi1 = (end - 1) / a.block_size;
-    // the plan keeps a split within kBlkCache blocks
+    // the plan keeps a split within kBlkCache blocks, all of them loaded above
     if (tid == 0) s_first = INT32_MAX;
     __syncthreads();
-    for (int k = tid; k < bi1 - bi0 + 1; k += kSplitThreads) {
-      const int blk = blist[bi0 + k];
-      sblk[k] = blk;
-      if (blk >= 0 && (int64_t)blk * a.block_size < p_len) atomicMin(&s_first, k);
-      else err |= TV_DERR_BAD_BLOCK;
+#pragma unroll
+    for (int u = 0; u < kBlkPer; ++u) {
+      const int k = tid + u * kSplitThreads;
+      if (k < bi1 - bi0 + 1) {
+        const int blk = pre_blk[u];
+        sblk[k] = blk;
+        if (blk >= 0 && (int64_t)blk * a.block_size < p_len) atomicMin(&s_first, k);
+        else err |= TV_DERR_BAD_BLOCK;
+      }
     }
     __syncthreads();
     const int first = s_first;
@@ -410,7 +429,7 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
       }
       np = 0;
     } else {
-      fb_row = blist[bi0 + first] * a.block_size;
+      fb_row = sblk[first] * a.block_size;
     }
   }
   const int ntiles = np + nt;
