@@ -227,6 +227,8 @@ constexpr int kBinBits = 11;
 constexpr int kBins = 1 << kBinBits;
 constexpr float kFix = 1099511627776.0f;  // 2^40: masses in fixed point
 constexpr int kCand = 4096;                // top-k candidate list in LDS
+constexpr int kSlices = 4;                 // workgroups per row collecting top-k candidates
+constexpr int kSliceCand = 256;            // candidates kept per (row, slice)
 
 // Order-preserving key of a logit: larger value, larger key; -0 and +0 share
 // the key of +0 (they compare equal).
@@ -289,7 +291,15 @@ __device__ void select_bin(const unsigned long long* hist, int nbins, unsigned l
 template <typename T, bool kVector>
 __global__ __launch_bounds__(kFiltThreads) void filter_threshold_kernel(
     const T* __restrict__ logits, int64_t vocab, int64_t row_stride, int top_k, float top_p,
-    float c2, float* __restrict__ tau) {
+    float c2, float* __restrict__ tau, int phase, uint32_t* __restrict__ cand_keys,
+    int* __restrict__ cand_count, float* __restrict__ slice_max) {
+  // phase 0: the whole search in this workgroup.
+  // phase 1 (grid rows x kSlices, top_k <= kFiltThreads): each workgroup
+  //   collects its slice's top-k candidates (the elements at or above the
+  //   top_k-th largest of its threads' maxima: the row's top-k elements are
+  //   among them, since each is in its slice's top-k) and the slice maximum.
+  // phase 2: the search from those candidates (the row itself if a slice
+  //   had more than kSliceCand).
   constexpr int VEC = 16 / sizeof(T);
   __shared__ unsigned long long hist[kBins];
   __shared__ uint32_t c_key[kCand];  // candidates: the elements at or above a lower bound
@@ -301,22 +311,29 @@ __global__ __launch_bounds__(kFiltThreads) void filter_threshold_kernel(
   const int64_t row = blockIdx.x;
   const T* src = logits + row * row_stride;
   const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
+  // elements [lo, hi) of the row (a slice of VEC-multiple length in phase 1)
+  int lo = 0, hi = (int)vocab;
+  if (phase == 1) {
+    const int sl = (((int)vocab + kSlices - 1) / kSlices + VEC - 1) / VEC * VEC;
+    lo = min((int)blockIdx.y * sl, (int)vocab);
+    hi = min(lo + sl, (int)vocab);
+  }
   // Every value of the row this thread owns: elements k0 .. k0 + VEC - 1 for
   // k0 = (t + i * kFiltThreads) * VEC, read with 8 loads in flight per
   // thread (the row stays in L2 between passes).
   typedef T vec_t __attribute__((ext_vector_type(VEC)));
   constexpr int kBatch = 8;
   auto visit = [&](auto&& f) {
-    for (int b0 = t * VEC; b0 < (int)vocab; b0 += kBatch * kFiltThreads * VEC) {
+    for (int b0 = lo + t * VEC; b0 < hi; b0 += kBatch * kFiltThreads * VEC) {
       vec_t x[kBatch];
 #pragma unroll
       for (int i = 0; i < kBatch; ++i) {
         const int k0 = b0 + i * kFiltThreads * VEC;
-        if (kVector && k0 + VEC <= (int)vocab) {
+        if (kVector && k0 + VEC <= hi) {
           x[i] = *reinterpret_cast<const vec_t*>(src + k0);
         } else {
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) x[i][e] = k0 + e < (int)vocab ? src[k0 + e] : (T)0.f;
+          for (int e = 0; e < VEC; ++e) x[i][e] = k0 + e < hi ? src[k0 + e] : (T)0.f;
         }
       }
 #pragma unroll
@@ -324,7 +341,7 @@ __global__ __launch_bounds__(kFiltThreads) void filter_threshold_kernel(
         const int k0 = b0 + i * kFiltThreads * VEC;
 #pragma unroll
         for (int e = 0; e < VEC; ++e)
-          if (k0 + e < (int)vocab) f(to_f32<T>(x[i][e]));
+          if (k0 + e < hi) f(to_f32<T>(x[i][e]));
       }
     }
   };
@@ -345,16 +362,47 @@ __global__ __launch_bounds__(kFiltThreads) void filter_threshold_kernel(
     for (int i = t; i < nc; i += kFiltThreads) f(c_key[i], c_val[i]);
   };
 
-  // ---- the row's maximum, and each thread's own maximum ----
-  float m_t = -INFINITY;  // a thread without elements offers -inf
-  visit([&](float v) { m_t = fmaxf(m_t, v); });
-  {
+  // ---- phase 2: the candidates the slices collected, when none overflowed ----
+  bool pre = false;
+  float M = -INFINITY, m_t = -INFINITY;
+  if (phase == 2) {
+    const int64_t r0 = row * kSlices;
+    if (t == 0) {
+      int total = 0;
+      bool ok = true;
+      for (int q = 0; q < kSlices; ++q) {
+        const int c = cand_count[r0 + q];
+        ok = ok && c <= kSliceCand;
+        total += c;
+      }
+      s_ncand = ok ? total : -1;
+    }
+    __syncthreads();
+    pre = s_ncand >= 0;
+    if (pre) {
+      // slice q's candidates go to c_key[off_q ..] with off_q the counts before it
+      for (int q = 0, off = 0; q < kSlices; ++q) {
+        const int c = cand_count[r0 + q];
+        for (int i = t; i < c; i += kFiltThreads) {
+          const uint32_t key = cand_keys[(r0 + q) * kSliceCand + i];
+          c_key[off + i] = key;
+          c_val[off + i] = key_value(key);
+        }
+        off += c;
+        M = fmaxf(M, slice_max[r0 + q]);
+      }
+      __syncthreads();
+    }
+  }
+  if (!pre) {
+    // ---- the row's (or slice's) maximum, and each thread's own maximum ----
+    visit([&](float v) { m_t = fmaxf(m_t, v); });
     const float wm = wave_max(m_t);
     if (lane == 0) s_red[wave] = wm;
     __syncthreads();
+    M = s_red[0];
+    for (int w = 1; w < kFiltWaves; ++w) M = fmaxf(M, s_red[w]);
   }
-  float M = s_red[0];
-  for (int w = 1; w < kFiltWaves; ++w) M = fmaxf(M, s_red[w]);
 
   // ---- top-k: the k-th largest key (ties at it are kept) ----
   // kth(src): the top_k-th largest of the keys src hands over (radix
@@ -380,8 +428,10 @@ __global__ __launch_bounds__(kFiltThreads) void filter_threshold_kernel(
     return prefix;
   };
   uint32_t tau_k = 0u;
-  bool use_cand = false;  // every key >= tau_k is in the candidate list
-  if (top_k > 0 && (int64_t)top_k < vocab) {
+  bool use_cand = pre;  // every key >= tau_k is in the candidate list
+  if (pre) {
+    tau_k = kth(cand_src);
+  } else if (top_k > 0 && (int64_t)top_k < vocab) {
     // A lower bound first: the top_k-th largest of the threads' maxima (top_k
     // threads hold an element at or above it, so the answer is at or above
     // it too).  The elements at or above it are few: they are collected
@@ -411,6 +461,18 @@ __global__ __launch_bounds__(kFiltThreads) void filter_threshold_kernel(
         }
       });
       __syncthreads();
+      if (phase == 1) {
+        // this slice's candidates and maximum for phase 2
+        const int64_t q = row * kSlices + blockIdx.y;
+        const int c = s_ncand;
+        for (int i = t; i < min(c, kSliceCand); i += kFiltThreads)
+          cand_keys[q * kSliceCand + i] = c_key[i];
+        if (t == 0) {
+          cand_count[q] = c;
+          slice_max[q] = M;
+        }
+        return;  // uniform over the workgroup
+      }
       use_cand = s_ncand <= kCand;  // else (many ties) the row is used
       __syncthreads();
     }
@@ -761,9 +823,11 @@ AcceptPlan plan_stochastic(int batch, int n, int64_t vocab) {
   static_assert((int64_t)kThreads * 8 * kUnroll <= (int64_t)kWalkThreads * kPer, "bonus scan size");
   p.chunk_len = chunk;
   p.chunks = (int)((vocab + chunk - 1) / chunk);
-  // chunk statistics, then one threshold per row
+  // chunk statistics, one threshold per row, then the slices' top-k candidates
   const size_t rows = (size_t)batch * n;
-  p.ws_bytes = ((rows * p.chunks * sizeof(float2) + 255) / 256) * 256 + rows * sizeof(float) + 256;
+  p.ws_bytes = ((rows * p.chunks * sizeof(float2) + 255) / 256) * 256 +
+               ((rows * sizeof(float) + 255) / 256) * 256 +
+               rows * kSlices * (kSliceCand * sizeof(uint32_t) + sizeof(int) + sizeof(float)) + 256;
   return p;
 }
 
@@ -774,9 +838,25 @@ void launch_typed(const void* logits, int64_t vocab, int64_t row_stride, int bat
                   float c2, int top_k, float top_p, const AcceptPlan& plan, float2* stats,
                   float* tau, const WalkArgs& w, hipStream_t stream) {
   const unsigned rows = (unsigned)((size_t)batch * n);
-  if (tau)
-    hipLaunchKernelGGL((filter_threshold_kernel<T, kVector>), dim3(rows), dim3(kFiltThreads), 0,
-                       stream, (const T*)logits, vocab, row_stride, top_k, top_p, c2, tau);
+  if (tau) {
+    // the slices' candidate buffers follow the thresholds in the workspace
+    char* base = reinterpret_cast<char*>(tau) + (((size_t)rows * sizeof(float) + 255) / 256) * 256;
+    uint32_t* cand_keys = reinterpret_cast<uint32_t*>(base);
+    int* cand_count = reinterpret_cast<int*>(cand_keys + (size_t)rows * kSlices * kSliceCand);
+    float* slice_max = reinterpret_cast<float*>(cand_count + (size_t)rows * kSlices);
+    if (top_k > 0 && top_k <= kFiltThreads && (int64_t)top_k < vocab) {
+      hipLaunchKernelGGL((filter_threshold_kernel<T, kVector>), dim3(rows, kSlices),
+                         dim3(kFiltThreads), 0, stream, (const T*)logits, vocab, row_stride,
+                         top_k, top_p, c2, tau, 1, cand_keys, cand_count, slice_max);
+      hipLaunchKernelGGL((filter_threshold_kernel<T, kVector>), dim3(rows), dim3(kFiltThreads), 0,
+                         stream, (const T*)logits, vocab, row_stride, top_k, top_p, c2, tau, 2,
+                         cand_keys, cand_count, slice_max);
+    } else {
+      hipLaunchKernelGGL((filter_threshold_kernel<T, kVector>), dim3(rows), dim3(kFiltThreads), 0,
+                         stream, (const T*)logits, vocab, row_stride, top_k, top_p, c2, tau, 0,
+                         cand_keys, cand_count, slice_max);
+    }
+  }
   hipLaunchKernelGGL((softmax_stats_kernel<T, kVector>), dim3(plan.chunks, rows), dim3(kThreads),
                      0, stream, (const T*)logits, vocab, row_stride, plan.chunk_len, plan.chunks,
                      c2, (const float*)tau, stats);
