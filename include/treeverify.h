@@ -13,8 +13,12 @@
  *   tv_greedy_accept     per-node vocabulary argmax, longest accepted path,
  *                        accepted length and bonus token
  *   tv_stochastic_accept the same at temperature > 0 (speculative sampling
- *                        along the tree, counter-based random numbers)
- *   tv_commit_kv         copy the accepted nodes' K/V rows into the cache
+ *                        along the tree, counter-based random numbers);
+ *                        tv_stochastic_accept_filtered adds top-k / top-p
+ *   tv_commit_kv         copy the accepted nodes' K/V rows into the cache;
+ *                        tv_greedy_accept_commit does acceptance and commit
+ *                        in one call, the *_layers forms commit every layer's
+ *                        cache in one launch
  *   tv_block_summaries   per-block element-wise max/min keys (SpecPV retrieval)
  *   tv_select_blocks     score blocks against the tree's queries and pick the
  *                        sink + top-k + window list for partial attention
