@@ -295,3 +295,15 @@ def test_filtered_first_token_is_distributed_as_the_filtered_target():
     assert not np.any((r[:, 0] >= 1) & ((r[:, 1] == 2) | (r[:, 1] == 3)))
     counts = np.bincount(firsts, minlength=vocab)[kept]
     assert stats.chisquare(counts, target[kept] * trials).pvalue > 1e-4
+
+
+def test_filtered_sampling_unaligned_rows():
+    # a row stride that is not a whole number of 16-byte vectors: the
+    # element-wise load paths of every kernel, top-k through the slices
+    _say("[stochastic filtered] strided rows (element-wise loads)")
+    parents, draft, logits = W.make_sampling_case(41, batch=2, n_nodes=24, vocab=9001,
+                                                  dtype="bf16", tree="random", lean=(3.0, 7.0))
+    for filt in ((20, 0.95), (0, 0.9), (1, 1.0)):
+        got = gpu_run(parents, draft, logits, 0.7, (41, 8), 1, "bf16", stride_pad=13, filt=filt)
+        assert got[3] == 0
+        check_against_oracle(parents, draft, logits, 0.7, (41, 8), 1, got, filt=filt)
