@@ -81,8 +81,11 @@ def test_attention_descriptor_tree_placement_is_validated():
         assert L.tv_tree_attention(ctypes.byref(d), None, None, 0, None, None) == 1
     d.tree_placement = 3
     assert L.tv_tree_attention(ctypes.byref(d), None, None, 0, None, None) == 2
-    d.tree_placement, d.reserved = 0, 1
+    d.tree_placement, d.kernel = 0, 3
     assert L.tv_tree_attention(ctypes.byref(d), None, None, 0, None, None) == 2
+    for k in (binding.KERNEL_AUTO, binding.KERNEL_SPLIT16, binding.KERNEL_WIDE):
+        d.kernel = k
+        assert L.tv_tree_attention(ctypes.byref(d), None, None, 0, None, None) == 1
 
 
 def test_header_declares_the_selection_calls():
@@ -201,3 +204,14 @@ def test_filtered_stochastic_accept_host_checks():
     assert call(0, 1.5) == 2
     assert call(0, float("nan")) == 2
     assert call(20, 0.95, temp=0.0) == 2
+
+
+def test_binding_constants_match_the_header():
+    text = open(os.path.join(ROOT, "include", "treeverify.h")).read()
+    defs = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define\s+(TV_\w+)\s+(\d+)", text)}
+    assert defs["TV_ATTN_WS_COUNTER_BYTES"] == binding.ATTN_WS_COUNTER_BYTES
+    assert defs["TV_DERR_SYNC"] == binding.DERR_SYNC
+    enums = dict(re.findall(r"(TV_ATTN_KERNEL_\w+)\s*=\s*(\d+)", text))
+    assert [int(enums[k]) for k in ("TV_ATTN_KERNEL_AUTO", "TV_ATTN_KERNEL_SPLIT16", "TV_ATTN_KERNEL_WIDE")] == \
+        [binding.KERNEL_AUTO, binding.KERNEL_SPLIT16, binding.KERNEL_WIDE]
+

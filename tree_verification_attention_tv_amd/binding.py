@@ -20,6 +20,7 @@ _lib = None
 
 TV_BF16, TV_F32 = 0, 1
 DERR_BAD_PARENT, DERR_BAD_BLOCK, DERR_CAPACITY, DERR_BAD_PREFIX, DERR_BAD_PATH = 1, 2, 4, 8, 16
+DERR_SYNC = 32  # a merge of split partials waited past its bound
 MAX_NODES = 256
 MAX_LAYERS = 4096
 
@@ -38,7 +39,7 @@ class AttnDesc(ctypes.Structure):
         ("block_size", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float), ("num_splits", ctypes.c_int32),
         ("cache_seq_stride", ctypes.c_int64),
-        ("tree_placement", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("tree_placement", ctypes.c_int32), ("kernel", ctypes.c_int32),
     ]
 
 
@@ -179,6 +180,162 @@ def _on_gpu(name, t, dtype=None, contiguous=True):
     return t
 
 
+def _shape(name, t, shape):
+    """Raise ValueError unless tensor ``t`` has exactly ``shape``."""
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(x) for x in shape)}, "
+                         f"got {tuple(t.shape)}")
+
+
+def _same_device(ref, **tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, the other operands on {ref.device}")
+
+
+def _int_vec(name, t, n, dtype=torch.int32):
+    """A contiguous int32 vector of n elements (None passes)."""
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    _shape(name, t, (n,))
+
+
+def _workspace_ok(workspace, ref):
+    if workspace is None:
+        return
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous 1-D uint8 tensor")
+    _same_device(ref, workspace=workspace)
+
+
+def _dev_err_ok(dev_err, ref):
+    if dev_err is None:
+        return
+    if dev_err.dtype != torch.int32 or dev_err.numel() < 1:
+        raise ValueError("dev_err must be an int32 tensor with at least one element")
+    _same_device(ref, dev_err=dev_err)
+
+
+def _cache_rows(name, t, ref_shape):
+    """A [B][Hkv][cap][D] cache with contiguous rows within a sequence."""
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B][Hkv][cap][D]")
+    if tuple(t.shape) != tuple(ref_shape):
+        raise ValueError(f"{name} must have shape {tuple(ref_shape)}, got {tuple(t.shape)}")
+    _, hkv, cap, d = t.shape
+    if t.stride()[1:] != (cap * d, d, 1):
+        raise ValueError(f"{name} must have contiguous rows per sequence ([B][Hkv][cap][D])")
+
+
+def validate_attention(q, k_cache, v_cache, k_tree, v_tree, prefix_len, mask, *, block_idx=None,
+                       n_blocks=None, out=None, lse=None, parents=None, mask_out=None,
+                       depth_out=None, workspace=None, dev_err=None):
+    """Shape, dtype, layout and device checks of tv_tree_attention's operands
+    against q [B][N][Hq][D] and k_cache [B][Hkv][cap][D]; raises before any
+    launch.  (Pure: needs no GPU.)"""
+    if q.dim() != 4:
+        raise ValueError("q must be [B][N][Hq][D]")
+    bsz, n, hq, d = q.shape
+    if k_cache.dim() != 4 or k_cache.shape[0] != bsz or k_cache.shape[3] != d:
+        raise ValueError(f"k_cache must be [B={bsz}][Hkv][cap][D={d}], got {tuple(k_cache.shape)}")
+    hkv = k_cache.shape[1]
+    if hkv < 1 or hq % hkv:
+        raise ValueError(f"n_q_heads {hq} is not a multiple of n_kv_heads {hkv}")
+    _cache_rows("k_cache", k_cache, k_cache.shape)
+    _cache_rows("v_cache", v_cache, k_cache.shape)
+    if v_cache.stride() != k_cache.stride():
+        raise ValueError("k_cache and v_cache must have the same strides")
+    for name, t in (("k_tree", k_tree), ("v_tree", v_tree)):
+        _shape(name, t, (bsz, n, hkv, d))
+    _int_vec("prefix_len", prefix_len, bsz)
+    w = (n + 31) // 32
+    if mask is not None:
+        _shape("mask", mask, (bsz, n, w))
+    if parents is not None:
+        _shape("parents", parents, (bsz, n))
+    if mask_out is not None:
+        _shape("mask_out", mask_out, (bsz, n, w))
+    if depth_out is not None:
+        _shape("depth_out", depth_out, (bsz, n))
+    if (block_idx is None) != (n_blocks is None):
+        raise ValueError("give both block_idx and n_blocks, or neither")
+    if block_idx is not None:
+        if block_idx.dim() != 2 or block_idx.shape[0] != bsz or block_idx.shape[1] < 1:
+            raise ValueError(f"block_idx must be [B={bsz}][max_blocks >= 1]")
+        _int_vec("n_blocks", n_blocks, bsz)
+    if out is not None:
+        if out.dtype != q.dtype or not out.is_contiguous():
+            raise ValueError("out must be a contiguous bf16 tensor")
+        _shape("out", out, q.shape)
+    if lse is not None:
+        if lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 tensor")
+        _shape("lse", lse, (bsz, n, hq))
+    _workspace_ok(workspace, q)
+    _dev_err_ok(dev_err, q)
+    _same_device(q, k_cache=k_cache, v_cache=v_cache, k_tree=k_tree, v_tree=v_tree,
+                 prefix_len=prefix_len, mask=mask, block_idx=block_idx, n_blocks=n_blocks,
+                 out=out, lse=lse, parents=parents, mask_out=mask_out, depth_out=depth_out)
+
+
+def validate_accept(logits, parents, draft_tokens, vocab=None, outputs=None, n_outputs=4):
+    """Checks of the acceptance calls' operands: logits [B][N][V] with unit
+    vocab stride and one row stride, parents and draft_tokens [B][N], the
+    vocab override within the row, and the output tensors' shapes."""
+    if parents.dim() != 2:
+        raise ValueError("parents must be [B][N]")
+    bsz, n = parents.shape
+    _shape("draft_tokens", draft_tokens, (bsz, n))
+    if logits.dim() != 3 or tuple(logits.shape[:2]) != (bsz, n) or logits.stride(2) != 1 or \
+            (bsz > 1 and logits.stride(0) != n * logits.stride(1)):
+        raise ValueError("logits must be [B][N][V] with unit vocab stride and uniform row stride")
+    if vocab is not None and not (1 <= int(vocab) <= logits.shape[2]):
+        raise ValueError(f"vocab {vocab} must be in [1, {logits.shape[2]}] (the logits row)")
+    if outputs is not None:
+        if len(outputs) != n_outputs:
+            raise ValueError(f"outputs must hold {n_outputs} tensors")
+        shapes = ([(bsz, n), (bsz,), (bsz, n), (bsz,)] if n_outputs == 4
+                  else [(bsz,), (bsz, n), (bsz,)])
+        names = (["target_argmax", "accept_len", "accept_path", "bonus_token"] if n_outputs == 4
+                 else ["accept_len", "accept_path", "bonus_token"])
+        for name, t, shp in zip(names, outputs, shapes):
+            if t.dtype != torch.int32 or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous int32 tensor")
+            _shape(name, t, shp)
+            _same_device(parents, **{name: t})
+    _same_device(parents, logits=logits, draft_tokens=draft_tokens)
+
+
+def validate_commit(k_tree, v_tree, k_cache, v_cache, prefix_len, *, accept_path=None,
+                    accept_len=None, new_prefix_len=None, n_nodes=None):
+    """Checks of the commit operands: tree K/V [B][N][Hkv][D] contiguous,
+    caches [B][Hkv][cap][D] with contiguous rows, and [B] / [B][N] int32
+    vectors."""
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be [B][Hkv][cap][D]")
+    bsz, hkv, cap, d = k_cache.shape
+    _cache_rows("k_cache", k_cache, k_cache.shape)
+    _cache_rows("v_cache", v_cache, k_cache.shape)
+    if v_cache.stride() != k_cache.stride():
+        raise ValueError("k_cache and v_cache must have the same strides")
+    if k_tree.dim() != 4:
+        raise ValueError("k_tree must be [B][N][Hkv][D]")
+    n = k_tree.shape[1] if n_nodes is None else n_nodes
+    for name, t in (("k_tree", k_tree), ("v_tree", v_tree)):
+        _shape(name, t, (bsz, n, hkv, d))
+    _int_vec("prefix_len", prefix_len, bsz)
+    _int_vec("accept_len", accept_len, bsz)
+    _int_vec("new_prefix_len", new_prefix_len, bsz)
+    if accept_path is not None:
+        _shape("accept_path", accept_path, (bsz, n))
+    _same_device(k_cache, k_tree=k_tree, v_tree=v_tree, v_cache=v_cache, prefix_len=prefix_len,
+                 accept_path=accept_path, accept_len=accept_len, new_prefix_len=new_prefix_len)
+
+
 def _check(fn, status):
     if status != 0:
         raise TVError(fn, status)
@@ -199,6 +356,9 @@ def build_tree_mask(parents: torch.Tensor, *, dev_err=None, with_depth=True):
     """parents int32 [B][N] -> (mask int32 [B][N][W] holding uint32 bit
     patterns, depth int32 [B][N] or None)."""
     _on_gpu("parents", parents, torch.int32)
+    if parents.dim() != 2:
+        raise ValueError("parents must be [B][N]")
+    _dev_err_ok(dev_err, parents)
     bsz, n = parents.shape
     w = (n + 31) // 32
     mask = torch.empty((bsz, n, w), dtype=torch.int32, device=parents.device)
@@ -209,10 +369,12 @@ def build_tree_mask(parents: torch.Tensor, *, dev_err=None, with_depth=True):
 
 
 TREE_AUTO, TREE_OWN_WORKGROUP, TREE_IN_LAST_SPLIT = 0, 1, 2
+KERNEL_AUTO, KERNEL_SPLIT16, KERNEL_WIDE = 0, 1, 2
+ATTN_WS_COUNTER_BYTES = 32768  # merge counters at the start of an attention workspace
 
 
 def attn_desc(q, k_cache, *, max_prefix_len, block_size=0, max_blocks=0, scale=0.0,
-              num_splits=0, tree_placement=TREE_AUTO) -> AttnDesc:
+              num_splits=0, tree_placement=TREE_AUTO, kernel=KERNEL_AUTO) -> AttnDesc:
     bsz, n, hq, d = q.shape
     _, hkv, cap, d2 = k_cache.shape
     if d2 != d:
@@ -221,12 +383,19 @@ def attn_desc(q, k_cache, *, max_prefix_len, block_size=0, max_blocks=0, scale=0
                     cache_capacity=cap, max_prefix_len=int(max_prefix_len),
                     block_size=int(block_size), max_blocks=int(max_blocks),
                     softmax_scale=float(scale), num_splits=int(num_splits),
-                    tree_placement=int(tree_placement), reserved=0,
+                    tree_placement=int(tree_placement), kernel=int(kernel),
                     cache_seq_stride=int(k_cache.stride(0)))
 
 
 def attention_workspace_size(desc: AttnDesc) -> int:
     return int(lib().tv_tree_attention_workspace_size(ctypes.byref(desc)))
+
+
+def attention_workspace(desc: AttnDesc, device) -> torch.Tensor:
+    """A workspace for tv_tree_attention calls of `desc`, with the merge
+    counters at its start zeroed as the call requires.  Reuse it for later
+    calls (of any descriptor that fits) that do not overlap in time."""
+    return torch.zeros(attention_workspace_size(desc), dtype=torch.uint8, device=device)
 
 
 def attention_num_splits(desc: AttnDesc) -> int:
@@ -235,7 +404,7 @@ def attention_num_splits(desc: AttnDesc) -> int:
 
 def tree_attention(q, k_cache, v_cache, k_tree, v_tree, prefix_len, mask, *, max_prefix_len,
                    block_idx=None, n_blocks=None, block_size=0, scale=0.0, num_splits=0,
-                   tree_placement=TREE_AUTO,
+                   tree_placement=TREE_AUTO, kernel=KERNEL_AUTO,
                    want_lse=False, out=None, lse=None, workspace=None, dev_err=None,
                    parents=None, mask_out=None, depth_out=None):
     """bf16 tree-masked GQA attention.  Returns out (and lse if asked).
@@ -257,16 +426,19 @@ def tree_attention(q, k_cache, v_cache, k_tree, v_tree, prefix_len, mask, *, max
         for name, t in (("mask_out", mask_out), ("depth_out", depth_out)):
             if t is not None:
                 _on_gpu(name, t, torch.int32)
-    if v_cache.shape != k_cache.shape or v_cache.stride() != k_cache.stride():
-        raise ValueError("k_cache and v_cache must have the same shape and strides")
     partial = block_idx is not None
     if partial:
         _on_gpu("block_idx", block_idx, torch.int32)
         _on_gpu("n_blocks", n_blocks, torch.int32)
+    validate_attention(q, k_cache, v_cache, k_tree, v_tree, prefix_len, mask,
+                       block_idx=block_idx, n_blocks=n_blocks, out=out, lse=lse, parents=parents,
+                       mask_out=mask_out, depth_out=depth_out, workspace=workspace,
+                       dev_err=dev_err)
     desc = attn_desc(q, k_cache, max_prefix_len=max_prefix_len,
                      block_size=block_size if partial else 0,
                      max_blocks=block_idx.shape[1] if partial else 0,
-                     scale=scale, num_splits=num_splits, tree_placement=tree_placement)
+                     scale=scale, num_splits=num_splits, tree_placement=tree_placement,
+                     kernel=kernel)
     if out is None:
         out = torch.empty_like(q)
     if want_lse and lse is None:
@@ -275,7 +447,8 @@ def tree_attention(q, k_cache, v_cache, k_tree, v_tree, prefix_len, mask, *, max
     if ws_bytes == 0:
         raise TVError("tv_tree_attention_workspace_size", 2)
     if workspace is None or workspace.numel() < ws_bytes:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        # the leading merge counters must start at zero; calls keep them so
+        workspace = attention_workspace(desc, q.device)
     ptrs = AttnPtrs(q=q.data_ptr(), k_tree=k_tree.data_ptr(), v_tree=v_tree.data_ptr(),
                     k_cache=k_cache.data_ptr(), v_cache=v_cache.data_ptr(),
                     prefix_len=prefix_len.data_ptr(),
@@ -303,10 +476,10 @@ def greedy_accept(logits, parents, draft_tokens, *, vocab=None, workspace=None, 
     _on_gpu("logits", logits, (torch.bfloat16, torch.float32), contiguous=False)
     _on_gpu("parents", parents, torch.int32)
     _on_gpu("draft_tokens", draft_tokens, torch.int32)
+    validate_accept(logits, parents, draft_tokens, vocab, outputs)
+    _workspace_ok(workspace, parents)
+    _dev_err_ok(dev_err, parents)
     bsz, n = parents.shape
-    if logits.shape[:2] != (bsz, n) or logits.stride(2) != 1 or \
-            (bsz > 1 and logits.stride(0) != n * logits.stride(1)):
-        raise ValueError("logits must be [B][N][V] with unit vocab stride and uniform row stride")
     v = logits.shape[2] if vocab is None else int(vocab)
     dt = TV_BF16 if logits.dtype == torch.bfloat16 else TV_F32
     dev = parents.device
@@ -341,13 +514,14 @@ def greedy_accept_commit(logits, parents, draft_tokens, k_tree, v_tree, prefix_l
     _on_gpu("k_cache", k_cache, torch.bfloat16, contiguous=False)
     _on_gpu("v_cache", v_cache, torch.bfloat16, contiguous=False)
     _on_gpu("prefix_len", prefix_len, torch.int32)
+    validate_accept(logits, parents, draft_tokens, vocab, outputs)
     bsz, n = parents.shape
-    if logits.shape[:2] != (bsz, n) or logits.stride(2) != 1 or \
-            (bsz > 1 and logits.stride(0) != n * logits.stride(1)):
-        raise ValueError("logits must be [B][N][V] with unit vocab stride and uniform row stride")
+    validate_commit(k_tree, v_tree, k_cache, v_cache, prefix_len, new_prefix_len=new_prefix_len,
+                    n_nodes=n)
+    _workspace_ok(workspace, parents)
+    _dev_err_ok(dev_err, parents)
+    _same_device(parents, k_cache=k_cache)
     _, hkv, cap, d = k_cache.shape
-    if k_cache.stride()[1:] != (cap * d, d, 1) or v_cache.stride() != k_cache.stride():
-        raise ValueError("caches must be [B][Hkv][cap][D] with contiguous rows per sequence")
     v = logits.shape[2] if vocab is None else int(vocab)
     dt = TV_BF16 if logits.dtype == torch.bfloat16 else TV_F32
     dev = parents.device
@@ -392,6 +566,7 @@ def _layer_views(k_tree, v_tree, k_cache, v_cache):
     if v_cache.shape != k_cache.shape or v_cache.stride() != k_cache.stride() or \
             k_cache.stride()[2:] != (cap * d, d, 1):
         raise ValueError("caches must have contiguous rows per (layer, sequence)")
+    _same_device(k_tree, v_tree=v_tree, k_cache=k_cache, v_cache=v_cache)
     return nl, int(k_tree.stride(0)), int(k_cache.stride(0)), int(k_cache.stride(1))
 
 
@@ -407,6 +582,13 @@ def commit_kv_layers(k_tree, v_tree, accept_path, accept_len, prefix_len, k_cach
         _on_gpu(name, t, torch.int32)
     _, bsz, n, hkv, d = k_tree.shape
     cap = k_cache.shape[3]
+    _int_vec("accept_len", accept_len, bsz)
+    _int_vec("prefix_len", prefix_len, bsz)
+    _int_vec("new_prefix_len", new_prefix_len, bsz)
+    _shape("accept_path", accept_path, (bsz, n))
+    _dev_err_ok(dev_err, k_tree)
+    _same_device(k_tree, accept_path=accept_path, accept_len=accept_len, prefix_len=prefix_len,
+                 new_prefix_len=new_prefix_len)
     if new_prefix_len is None:
         new_prefix_len = torch.empty_like(prefix_len)
     _check("tv_commit_kv_layers", lib().tv_commit_kv_layers(
@@ -428,12 +610,15 @@ def greedy_accept_commit_layers(logits, parents, draft_tokens, k_tree, v_tree, p
     _on_gpu("parents", parents, torch.int32)
     _on_gpu("draft_tokens", draft_tokens, torch.int32)
     _on_gpu("prefix_len", prefix_len, torch.int32)
+    validate_accept(logits, parents, draft_tokens, vocab, outputs)
     bsz, n = parents.shape
-    if logits.shape[:2] != (bsz, n) or logits.stride(2) != 1 or \
-            (bsz > 1 and logits.stride(0) != n * logits.stride(1)):
-        raise ValueError("logits must be [B][N][V] with unit vocab stride and uniform row stride")
     if k_tree.shape[1:3] != (bsz, n):
         raise ValueError("k_tree must be [L][B][N][Hkv][D] for the parents' B and N")
+    _int_vec("prefix_len", prefix_len, bsz)
+    _int_vec("new_prefix_len", new_prefix_len, bsz)
+    _workspace_ok(workspace, parents)
+    _dev_err_ok(dev_err, parents)
+    _same_device(parents, k_tree=k_tree, prefix_len=prefix_len, new_prefix_len=new_prefix_len)
     _, _, _, hkv, d = k_tree.shape
     cap = k_cache.shape[3]
     v = logits.shape[2] if vocab is None else int(vocab)
@@ -488,10 +673,11 @@ def _stochastic(logits, parents, draft_tokens, temperature, filt, seed, step, vo
     _on_gpu("logits", logits, (torch.bfloat16, torch.float32), contiguous=False)
     _on_gpu("parents", parents, torch.int32)
     _on_gpu("draft_tokens", draft_tokens, torch.int32)
+    validate_accept(logits, parents, draft_tokens, vocab, outputs, n_outputs=3)
+    _workspace_ok(workspace, parents)
+    _dev_err_ok(dev_err, parents)
+    # temperature (finite, > 0) is checked by the library: TVError otherwise
     bsz, n = parents.shape
-    if logits.shape[:2] != (bsz, n) or logits.stride(2) != 1 or \
-            (bsz > 1 and logits.stride(0) != n * logits.stride(1)):
-        raise ValueError("logits must be [B][N][V] with unit vocab stride and uniform row stride")
     v = logits.shape[2] if vocab is None else int(vocab)
     dt = TV_BF16 if logits.dtype == torch.bfloat16 else TV_F32
     dev = parents.device
@@ -532,9 +718,10 @@ def commit_kv(k_tree, v_tree, accept_path, accept_len, prefix_len, k_cache, v_ca
     for name, t in (("accept_path", accept_path), ("accept_len", accept_len),
                     ("prefix_len", prefix_len)):
         _on_gpu(name, t, torch.int32)
+    validate_commit(k_tree, v_tree, k_cache, v_cache, prefix_len, accept_path=accept_path,
+                    accept_len=accept_len, new_prefix_len=new_prefix_len)
+    _dev_err_ok(dev_err, k_cache)
     bsz, hkv, cap, d = k_cache.shape
-    if k_cache.stride()[1:] != (cap * d, d, 1) or v_cache.stride() != k_cache.stride():
-        raise ValueError("caches must be [B][Hkv][cap][D] with contiguous rows per sequence")
     n = k_tree.shape[1]
     if new_prefix_len is None:
         new_prefix_len = torch.empty_like(prefix_len)
@@ -563,6 +750,12 @@ def block_summaries(k_cache, prefix_len, *, block_size, first_token=None, max_to
     bsz, hkv, cap, d = k_cache.shape
     if k_cache.stride()[1:] != (cap * d, d, 1):
         raise ValueError("k_cache must be [B][Hkv][cap][D] with contiguous rows per sequence")
+    if int(block_size) < 1:
+        raise ValueError("block_size must be >= 1")
+    _int_vec("prefix_len", prefix_len, bsz)
+    _int_vec("first_token", first_token, bsz)
+    _dev_err_ok(dev_err, k_cache)
+    _same_device(k_cache, prefix_len=prefix_len, first_token=first_token, summaries=summaries)
     shape = summaries_shape(k_cache, block_size)
     if summaries is None:
         summaries = torch.empty(shape, dtype=torch.bfloat16, device=k_cache.device)
@@ -606,8 +799,12 @@ def select_blocks(q, summaries, prefix_len, *, cache_capacity, max_prefix_len, b
     _on_gpu("prefix_len", prefix_len, torch.int32)
     bsz, n, hq, d = q.shape
     nb_cap = (int(cache_capacity) + int(block_size) - 1) // int(block_size)
-    if tuple(summaries.shape) != (bsz, summaries.shape[1], nb_cap, 2, d):
+    if summaries.dim() != 5 or tuple(summaries.shape) != (bsz, summaries.shape[1], nb_cap, 2, d):
         raise ValueError("summaries do not match q, cache_capacity and block_size")
+    _int_vec("prefix_len", prefix_len, bsz)
+    _workspace_ok(workspace, q)
+    _dev_err_ok(dev_err, q)
+    _same_device(q, summaries=summaries, prefix_len=prefix_len)
     desc = select_desc(q, summaries, cache_capacity=cache_capacity,
                        max_prefix_len=max_prefix_len, block_size=block_size, n_sink=n_sink,
                        n_window=n_window, top_k=top_k, reduction=reduction,
@@ -619,12 +816,16 @@ def select_blocks(q, summaries, prefix_len, *, cache_capacity, max_prefix_len, b
     block_idx, n_blocks = outputs
     _on_gpu("block_idx", block_idx, torch.int32)
     _on_gpu("n_blocks", n_blocks, torch.int32)
-    if tuple(block_idx.shape) != (bsz, desc.max_blocks):
-        raise ValueError("block_idx must be [B][max_blocks]")
+    if tuple(block_idx.shape) != (bsz, desc.max_blocks) or not block_idx.is_contiguous():
+        raise ValueError("block_idx must be a contiguous [B][max_blocks] tensor")
+    _int_vec("n_blocks", n_blocks, bsz)
+    _same_device(q, block_idx=block_idx, n_blocks=n_blocks)
     if want_scores and scores is None:
         scores = torch.empty((bsz, nb_cap), dtype=torch.float32, device=dev)
     if scores is not None:
         _on_gpu("scores", scores, torch.float32)
+        _shape("scores", scores, (bsz, nb_cap))
+        _same_device(q, scores=scores)
     ws_bytes = select_workspace_size(desc)
     if ws_bytes == 0:
         raise TVError("tv_select_blocks_workspace_size", 2)
