@@ -72,6 +72,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--kernel", default="auto", choices=["auto", "split16", "wide"],
+                    help="attention schedule (auto: the planner's choice)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the step with eager launches only (no HIP graph replay)")
     ap.add_argument("--no-secondary", action="store_true",
@@ -135,7 +137,7 @@ class InputSet:
 class StepRunner:
     """The four library calls of one verify step, on torch's current stream."""
 
-    def __init__(self, wl, partial, warm, num_splits, dev, specpv=False):
+    def __init__(self, wl, partial, warm, num_splits, dev, specpv=False, kernel="auto"):
         import numpy as np
         import torch
 
@@ -163,19 +165,20 @@ class StepRunner:
         self.graphs = []
         self.b, self.n = wl.parents.shape
         self.num_splits = num_splits
+        self.kernel = {"auto": binding.KERNEL_AUTO, "split16": binding.KERNEL_SPLIT16,
+                       "wide": binding.KERNEL_WIDE}[kernel]
         self.desc = binding.attn_desc(
             first.q, first.k_cache, max_prefix_len=wl.max_prefix_len,
             block_size=wl.block_size if partial else 0,
             max_blocks=(self.max_blocks if specpv else wl.max_blocks) if partial else 0,
-            num_splits=num_splits)
+            num_splits=num_splits, kernel=self.kernel)
         if specpv:
             self.sel_desc = binding.select_desc(
                 first.q, first.summ, cache_capacity=wl.capacity,
                 max_prefix_len=wl.max_prefix_len, block_size=wl.block_size, **self.sel)
             self.ws_sel = torch.empty(binding.select_workspace_size(self.sel_desc),
                                       dtype=torch.uint8, device=dev)
-        self.ws_attn = torch.empty(binding.attention_workspace_size(self.desc), dtype=torch.uint8,
-                                   device=dev)
+        self.ws_attn = binding.attention_workspace(self.desc, dev)
         self.ws_acc = torch.empty(binding.accept_workspace_size(self.b, self.n, wl.vocab),
                                   dtype=torch.uint8, device=dev)
         self.acc_out = (torch.empty((self.b, self.n), dtype=torch.int32, device=dev),
@@ -224,8 +227,8 @@ class StepRunner:
             s.q, s.k_cache, s.v_cache, s.k_tree, s.v_tree, s.prefix_len, None,
             max_prefix_len=wl.max_prefix_len, block_idx=bidx if p else None,
             n_blocks=nblk if p else None, block_size=wl.block_size if p else 0,
-            num_splits=self.num_splits, out=s.out, workspace=self.ws_attn, dev_err=self.err,
-            parents=s.parents, mask_out=s.mask)
+            num_splits=self.num_splits, kernel=self.kernel, out=s.out, workspace=self.ws_attn,
+            dev_err=self.err, parents=s.parents, mask_out=s.mask)
 
     def k_accept(self, s):
         self.binding.greedy_accept(s.logits, s.parents, s.draft, workspace=self.ws_acc,
@@ -371,11 +374,12 @@ class StepRunner:
         return prefix_tokens, kv, kv + qo + mask, wl.logits.nbytes
 
 
-def measure(wl, partial, steps, warmup, warm, num_splits, dev, graph=True, specpv=False):
+def measure(wl, partial, steps, warmup, warm, num_splits, dev, graph=True, specpv=False,
+            kernel="auto"):
     """Returns (runner, step_us, wall_us, eager_step_us, calls).  step_us is
     the graph-replayed step when `graph`, else the eager one."""
     import torch
-    r = StepRunner(wl, partial, warm, num_splits, dev, specpv=specpv)
+    r = StepRunner(wl, partial, warm, num_splits, dev, specpv=specpv, kernel=kernel)
     for k in range(warmup):
         r.step(r.sets[k % r.rot])
     torch.cuda.synchronize()
@@ -541,7 +545,7 @@ def multi_layer_line(steps, dev, layers=32):
 
     sets = [LayerSet(), LayerSet()]
     desc = binding.attn_desc(sets[0].q[0], sets[0].k_cache[0], max_prefix_len=wl.max_prefix_len)
-    ws_attn = torch.empty(binding.attention_workspace_size(desc), dtype=torch.uint8, device=dev)
+    ws_attn = binding.attention_workspace(desc, dev)
     ws_acc = torch.empty(binding.accept_workspace_size(b, n, wl.vocab), dtype=torch.uint8,
                          device=dev)
     acc_out = (torch.empty((b, n), dtype=torch.int32, device=dev),
@@ -673,7 +677,8 @@ def main():
     partial = specpv or (args.partial and wl.block_idx is not None)
     r, step_us, wall_us, eager_us, calls = measure(wl, partial, args.steps, args.warmup,
                                                    args.warm, args.num_splits, dev,
-                                                   graph=not args.no_graph, specpv=specpv)
+                                                   graph=not args.no_graph, specpv=specpv,
+                                                   kernel=args.kernel)
     prefix_tokens, kv_bytes, attn_bytes, logit_bytes = r.bytes()
     b, n = r.b, r.n
     dominant = max(("attention", "accept"), key=lambda c: calls[c])

@@ -77,6 +77,8 @@ typedef enum { TV_BF16 = 0, TV_F32 = 1 } tv_dtype;
 #define TV_DERR_CAPACITY 4    /* prefix_len + accept_len + 1 > cache_capacity */
 #define TV_DERR_BAD_PREFIX 8  /* prefix_len < 0, > cache_capacity or > max_prefix_len */
 #define TV_DERR_BAD_PATH 16   /* accept_len or an accept_path entry out of range */
+#define TV_DERR_SYNC 32       /* an in-launch merge waited past its bound for the
+                                 partials of its split workgroups (outputs undefined) */
 
 #define TV_MAX_NODES 256
 #define TV_MAX_LAYERS 4096  /* layers of one multi-layer commit */
@@ -134,7 +136,15 @@ tv_status tv_build_tree_mask(const int32_t* parents, int32_t batch, int32_t n_no
  *   that range (TV_DERR_BAD_PREFIX); a row that sees no key at all (possible
  *   only with a hand-made mask) gets out = 0 and lse = -inf.
  * Workspace: at least tv_tree_attention_workspace_size(desc) bytes, 256-byte
- *   aligned, contents undefined on entry and on exit.
+ *   aligned.  Its first TV_ATTN_WS_COUNTER_BYTES bytes are counters by which
+ *   the merge of the split partials waits for them inside the same launch:
+ *   they must be zero before the first call on the workspace (a hipMemset
+ *   once, at allocation), and every call leaves them zero, so later calls of
+ *   any descriptor may reuse the workspace.  Everything after them is
+ *   scratch, undefined on entry and exit.  Calls that share a workspace must
+ *   not overlap in time, and the workspace must not serve other calls in
+ *   between.  A call that raised TV_DERR_SYNC (a merge that waited past its
+ *   bound) may leave the counters non-zero: zero them again.
  */
 typedef struct {
   int32_t batch, n_nodes, n_q_heads, n_kv_heads, head_dim;
@@ -151,10 +161,18 @@ typedef struct {
                                planner), TV_TREE_OWN_WORKGROUP, or TV_TREE_IN_LAST_SPLIT
                                (after the prefix tiles of the last non-empty split).
                                Results are the same; only the schedule differs. */
-  int32_t reserved;         /* must be 0 */
+  int32_t kernel;           /* which schedule runs the call: TV_ATTN_KERNEL_AUTO (chosen by
+                               the planner), TV_ATTN_KERNEL_SPLIT16 (eight waves of 16-32
+                               rows on 16x16x32 MFMAs) or TV_ATTN_KERNEL_WIDE (four waves of
+                               32-64 rows on 32x32x16 MFMAs).  Results agree within the
+                               stated tolerance; only the schedule differs. */
 } tv_attn_desc;
 
 enum { TV_TREE_AUTO = 0, TV_TREE_OWN_WORKGROUP = 1, TV_TREE_IN_LAST_SPLIT = 2 };
+enum { TV_ATTN_KERNEL_AUTO = 0, TV_ATTN_KERNEL_SPLIT16 = 1, TV_ATTN_KERNEL_WIDE = 2 };
+/* counters at the start of every attention workspace (zero between calls);
+   batch * n_kv_heads above TV_ATTN_WS_COUNTER_BYTES / 8 merges in a second launch */
+#define TV_ATTN_WS_COUNTER_BYTES 32768
 
 typedef struct {
   const void* q;

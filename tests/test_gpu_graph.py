@@ -32,8 +32,7 @@ class _Step:
                          for s in ((b, n), (b,), (b, n), (b,)))
         self.new_prefix = torch.empty_like(dw.prefix_len)
         desc = binding.attn_desc(dw.q, dw.k_cache, max_prefix_len=wl.max_prefix_len)
-        self.ws_attn = torch.empty(binding.attention_workspace_size(desc), dtype=torch.uint8,
-                                   device=dev)
+        self.ws_attn = binding.attention_workspace(desc, dev)
         self.ws_acc = torch.empty(binding.accept_workspace_size(b, n, wl.vocab), dtype=torch.uint8,
                                   device=dev)
 
@@ -132,8 +131,7 @@ def test_specpv_step_graph_replays_match_eager():
                 dtype=torch.uint8, device="cuda")
             self.desc = binding.attn_desc(dw.q, dw.k_cache, max_prefix_len=wl.max_prefix_len,
                                           block_size=bs, max_blocks=n_sink + n_window + top_k)
-            self.ws_attn = torch.empty(binding.attention_workspace_size(self.desc),
-                                       dtype=torch.uint8, device="cuda")
+            self.ws_attn = binding.attention_workspace(self.desc, "cuda")
 
         def run(self):
             dw = self.dw
@@ -220,8 +218,7 @@ def test_multi_layer_and_filtered_calls_replay_to_eager():
                              for s in ((b,), (b, n), (b,)))
             self.new_prefix = torch.empty_like(self.dw.prefix_len)
             desc = binding.attn_desc(self.q[0], self.kc[0], max_prefix_len=wl.max_prefix_len)
-            self.ws_attn = torch.empty(binding.attention_workspace_size(desc), dtype=torch.uint8,
-                                       device="cuda")
+            self.ws_attn = binding.attention_workspace(desc, "cuda")
             self.ws_acc = torch.empty(binding.accept_workspace_size(b, n, wl.vocab),
                                       dtype=torch.uint8, device="cuda")
             self.ws_sto = torch.empty(binding.stochastic_accept_workspace_size(b, n, wl.vocab),

@@ -21,8 +21,11 @@ BUILD = os.path.join(CSRC, "_build")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtreeverify.so")
 
-SOURCES = ["tv_api.cpp", "tv_mask.hip", "tv_attention.hip", "tv_accept.hip", "tv_commit.hip",
-           "tv_select.hip", "tv_specpv.cpp", "tv_stochastic.hip"]
+SOURCES = ["tv_api.cpp", "tv_mask.hip", "tv_attention.hip", "tv_attn_wide.hip", "tv_accept.hip",
+           "tv_commit.hip", "tv_select.hip", "tv_specpv.cpp", "tv_stochastic.hip"]
+# per-source device-code options: the 32-row attention kernel keeps its MFMA
+# accumulators in VGPRs (VGPR-form MFMA), so its softmax reads them directly
+EXTRA_FLAGS = {"tv_attn_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 
@@ -45,7 +48,8 @@ def common_flags() -> list[str]:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + common_flags() + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + common_flags() + EXTRA_FLAGS.get(src, []) + \
+        ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compiling {src} failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")

@@ -60,7 +60,7 @@ tv_status check_attn_desc(const tv_attn_desc* d) {
   if (d->cache_capacity < 0) return TV_ERR_SHAPE;
   if (d->max_blocks < 0 || d->num_splits < 0 || d->num_splits > 4096) return TV_ERR_SHAPE;
   if (d->tree_placement < TV_TREE_AUTO || d->tree_placement > TV_TREE_IN_LAST_SPLIT ||
-      d->reserved != 0)
+      d->kernel < TV_ATTN_KERNEL_AUTO || d->kernel > TV_ATTN_KERNEL_WIDE)
     return TV_ERR_SHAPE;
   if (d->max_blocks > 0) {
     if (d->block_size < 1) return TV_ERR_SHAPE;
@@ -124,7 +124,7 @@ size_t tv_tree_attention_workspace_size(const tv_attn_desc* desc) {
   const int cus = cu_count_for_current_device();
   if (cus <= 0) return 0;
   const tv::AttnPlan p = tv::plan_attention(*desc, cus);
-  return p.ws_o_bytes + p.ws_ml_bytes;
+  return p.ws_bytes();
 }
 
 tv_status tv_tree_attention(const tv_attn_desc* desc, const tv_attn_ptrs* ptrs, void* workspace,
@@ -146,7 +146,7 @@ tv_status tv_tree_attention(const tv_attn_desc* desc, const tv_attn_ptrs* ptrs, 
   const int cus = cu_count_for_current_device();
   if (cus <= 0) return TV_ERR_DEVICE;
   const tv::AttnPlan plan = tv::plan_attention(*desc, cus);
-  if (!aligned(workspace, 16) || workspace_bytes < plan.ws_o_bytes + plan.ws_ml_bytes)
+  if (!aligned(workspace, 16) || workspace_bytes < plan.ws_bytes())
     return TV_ERR_WORKSPACE;
   return launch_status(tv::launch_attention(*desc, plan, p, workspace, dev_err, stream));
 }

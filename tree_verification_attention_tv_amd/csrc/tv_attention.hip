@@ -43,7 +43,7 @@
 //    exponent).  If a row's sum leaves [1, 2^100] or an output is not
 //    finite, the split is recomputed with the exact row max from a QK-only
 //    pre-pass (p <= 1 then).  Masked scores are -inf.
-#include "tv_internal.h"
+#include "tv_attn_common.h"
 
 #include <math.h>
 
@@ -53,122 +53,11 @@
 namespace tv {
 namespace {
 
+using namespace attn;
+
 constexpr int kThreads = 256;      // combine kernel
 constexpr int kWaves = 8;          // split kernel: 8 waves, two per SIMD
 constexpr int kSplitThreads = kWaves * 64;
-constexpr int kTile = 32;        // tokens per KV tile
-constexpr int kMinChunk = 128;   // minimum prefix slots per split
-constexpr float kSumMax = 1.2676506e30f;  // 2^100: largest accepted row sum
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-
-struct AttnArgs {
-  const bf16* q;
-  const bf16* k_tree;
-  const bf16* v_tree;
-  const bf16* k_cache;
-  const bf16* v_cache;
-  const int32_t* prefix_len;
-  const uint32_t* mask;      // null: built from `parents` by the tree workgroups
-  const int32_t* parents;    // [batch][n] when mask is null
-  uint32_t* mask_out;        // optional outputs of the in-kernel build (as tv_build_tree_mask)
-  int32_t* depth_out;
-  const int32_t* block_idx;
-  const int32_t* n_blocks;
-  bf16* part_o;     // [batch][nparts][hkv][rows][D], normalised by the row's own sum
-  float2* part_ml;  // [batch][nparts][hkv][rows]: (reference max, row sum)
-  int32_t* dev_err;
-  bf16* out;
-  float* lse;
-  int64_t seq_stride;
-  int batch, n, hq, hkv, grp, cap, words;
-  int block_size, block_shift, max_blocks, max_prefix;  // block_shift < 0: not a power of 2
-  int chunk, splits, row_groups, rows;
-  int tree_sep, nparts;  // tree in its own workgroup (split index `splits`); partials per sequence
-  float c;  // softmax scale * log2(e)
-};
-
-// Verified-prefix length of sequence b, clamped to what the grid covers.
-__device__ __forceinline__ int clamped_prefix(const AttnArgs& a, int b, int* err) {
-  int p = a.prefix_len[b];
-  const int lim = a.max_blocks ? a.cap : min(a.cap, a.max_prefix);
-  if (p < 0 || p > lim) {
-    *err |= TV_DERR_BAD_PREFIX;
-    p = p < 0 ? 0 : lim;
-  }
-  return p;
-}
-
-// Number of prefix slots of sequence b: prefix rows in full mode, listed
-// blocks times block size in partial mode.
-__device__ __forceinline__ int prefix_slots(const AttnArgs& a, int b, int p, int* err) {
-  if (a.max_blocks == 0) return p;
-  int nb = a.n_blocks[b];
-  if (nb < 0 || nb > a.max_blocks) {
-    *err |= TV_DERR_BAD_BLOCK;
-    nb = nb < 0 ? 0 : a.max_blocks;
-  }
-  return nb * a.block_size;
-}
-
-
-// Workgroup barrier for LDS hand-off only.  __syncthreads() would also wait
-// for every outstanding global load of the wave (vmcnt(0)), which would
-// drain the tile prefetches the pipeline keeps in flight across barriers.
-// Here each wave only waits for its own LDS accesses (lgkmcnt(0)); the
-// signal fences keep the compiler from moving memory operations across.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // gfx9 encoding: lgkmcnt(0), vmcnt/expcnt unconstrained
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// Reductions over the four 16-lane groups (lanes l, l^16, l^32, l^48) with
-// the gfx950 row-swap permutes: after swapping, the two results of each
-// swap hold the value of a lane and of its partner.
-__device__ __forceinline__ float xsum16_32(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-__device__ __forceinline__ float xmax16_32(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
-// ---- LDS DMA -----------------------------------------------------------------
-// global_load_lds_dwordx4: each lane loads 16 bytes from its own address and
-// the wave's 64 results land contiguously in LDS at M0 (lane i at M0 + 16 i).
-// Issued through inline asm so that the compiler neither reorders it nor
-// inserts its own (conservative) waits; completion is tracked by hand with
-// vmcnt, which counts these loads like any other vector-memory load.
-__device__ __forceinline__ void dma16(uint32_t lds_addr, const void* gptr) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(lds_addr), "v"(gptr)
-               : "memory");
-}
-
-// Same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane offset.
-__device__ __forceinline__ void dma16s(uint32_t lds_addr, const void* sbase, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(lds_addr), "v"(voff), "s"(sbase)
-               : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-
-constexpr int kRing = 4;        // LDS ring slots (tiles)
-constexpr int kBlkCache = 1024; // block ids of one split staged in LDS
 
 template <int D, int RB, bool PARTIAL>
 __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a) {
@@ -847,109 +736,14 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
   }
 }
 
-// Merge the split partials of one (sequence, node, head) row: with weights
-// w_s = 2^(m_s - m) l_s, m = max m_s, the output is sum w_s o_s / sum w_s
-// (o_s already divided by l_s) and the log-sum-exp is m + log2(sum w_s),
-// in natural-log units.  One wave per row: lane t C + c (C = D/8 chunks of
-// 8 elements, T = 64/C) folds the partials k = t, t+T, ... for elements
-// 8c..8c+7 into a running (max, sum, output), and the T running states are
-// merged across lanes in a fixed order.
+
+// One wave per row (combine_rows in tv_attn_common.h).
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
-  constexpr int C = D / 8;
-  constexpr int T = 64 / C;
-  constexpr int U = 8;  // partials per lane with loads in flight together
-  const int lane = threadIdx.x & 63;
   const int64_t rowid = (int64_t)blockIdx.x * (kThreads / 64) + threadIdx.x / 64;  // (b * n + i) * hq + h
   if (rowid >= (int64_t)a.batch * a.n * a.hq) return;
-  const int c = lane % C;
-  const int t = lane / C;
-  const int h = (int)(rowid % a.hq);
-  const int64_t bi = rowid / a.hq;
-  const int i = (int)(bi % a.n);
-  const int b = (int)(bi / a.n);
-  const int g = h / a.grp;
-  const int m_row = i * a.grp + h % a.grp;
-
-  // Every split writes a partial for every row (an empty one, m = -inf,
-  // where it sees no key), so all of them are merged and the prefix length
-  // is not needed here: the partial loads are this kernel's first and only
-  // memory round trip.
-  const int cnt = a.nparts;
-  const int64_t stride = (int64_t)a.hkv * a.rows;  // partial rows between splits
-  const int64_t p0 = ((int64_t)b * a.nparts * a.hkv + g) * a.rows + m_row;
-
-  float mx = -INFINITY, l = 0.f;
-  float acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int k0 = t; k0 < cnt; k0 += T * U) {
-    float2 ml[U];
-    bf16x8 ov[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = k0 + u * T;
-      if (k < cnt) {
-        const int64_t pi = p0 + k * stride;
-        ml[u] = a.part_ml[pi];
-        ov[u] = *reinterpret_cast<const bf16x8*>(a.part_o + pi * D + 8 * c);
-      } else {
-        ml[u] = make_float2(-INFINITY, 0.f);
-        ov[u] = bf16x8{};
-      }
-    }
-    float mb = mx;
-#pragma unroll
-    for (int u = 0; u < U; ++u) mb = fmaxf(mb, ml[u].x);
-    if (mb == -INFINITY) continue;
-    const float r = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx - mb);
-    l *= r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] *= r;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      // an empty partial (m = -inf) weighs 0 and its output is not read
-      const float w = ml[u].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[u].x - mb) * ml[u].y;
-      l += w;
-      if (w != 0.f) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(w, (float)ov[u][e], acc[e]);
-      }
-    }
-    mx = mb;
-  }
-  // merge the T states of a chunk (lanes c, c + C, ...)
-#pragma unroll
-  for (int off = C; off < 64; off <<= 1) {
-    const float mo = __shfl_xor(mx, off);
-    const float lo = __shfl_xor(l, off);
-    float ao[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ao[e] = __shfl_xor(acc[e], off);
-    const float mn = fmaxf(mx, mo);
-    if (mn != -INFINITY) {
-      const float r0 = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx - mn);
-      const float r1 = mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mo - mn);
-      l = l * r0 + lo * r1;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = acc[e] * r0 + ao[e] * r1;
-    }
-    mx = mn;
-  }
-  if (t != 0) return;
-  bf16x8 res;
-  float lse_v;
-  if (mx == -INFINITY) {
-    res = bf16x8{};
-    lse_v = -INFINITY;
-  } else {
-    const float inv = 1.f / l;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) res[e] = (bf16)(acc[e] * inv);
-    lse_v = (mx + log2f(l)) * 0.69314718055994530942f;
-  }
-  *reinterpret_cast<bf16x8*>(a.out + rowid * D + 8 * c) = res;
-  if (c == 0 && a.lse) a.lse[rowid] = lse_v;
+  const int64_t ids[1] = {rowid};
+  combine_rows<D, 1, false>(a, ids, threadIdx.x & 63);
 }
 
 template <int D, int RB>
@@ -1034,6 +828,7 @@ AttnPlan plan_rows(const tv_attn_desc& d, int cu_count, int max_rb, int* crit) {
   const size_t parts = (size_t)d.batch * (p.splits + p.tree_sep) * d.n_nodes * d.n_q_heads;
   p.ws_o_bytes = ((parts * d.head_dim * sizeof(uint16_t) + 255) / 256) * 256;  // bf16
   p.ws_ml_bytes = ((parts * sizeof(float2) + 255) / 256) * 256;
+  p.ws_sync_bytes = TV_ATTN_WS_COUNTER_BYTES;
   return p;
 }
 
@@ -1048,9 +843,21 @@ AttnPlan plan_rows(const tv_attn_desc& d, int cu_count, int max_rb, int* crit) {
 // workgroups lose).  The plan with the shorter longest workgroup wins.
 AttnPlan plan_attention(const tv_attn_desc& d, int cu_count) {
   int crit2 = 0, crit1 = 0;
-  const AttnPlan p2 = plan_rows(d, cu_count, 2, &crit2);
+  if (d.kernel == TV_ATTN_KERNEL_WIDE) {
+    // 32-row MFMA tiles, one or two per wave: 128 or 256 rows per workgroup;
+    // the merge runs in the same launch, about one workgroup per CU
+    AttnPlan p = plan_rows(d, cu_count, 2, &crit2);
+    p.kind = TV_ATTN_KERNEL_WIDE;
+    const int64_t all_rows = (int64_t)d.batch * d.n_kv_heads * p.rows;
+    p.rpw = (int)std::max<int64_t>(1, (all_rows + 4 * (int64_t)cu_count - 1) / (4 * (int64_t)cu_count));
+    p.ncw_unit = (p.rows + 4 * p.rpw - 1) / (4 * p.rpw);
+    return p;
+  }
+  AttnPlan p2 = plan_rows(d, cu_count, 2, &crit2);
+  p2.kind = TV_ATTN_KERNEL_SPLIT16;
   if (p2.row_blocks == 1) return p2;
-  const AttnPlan p1 = plan_rows(d, cu_count, 1, &crit1);
+  AttnPlan p1 = plan_rows(d, cu_count, 1, &crit1);
+  p1.kind = TV_ATTN_KERNEL_SPLIT16;
   return 13 * crit1 < 20 * crit2 ? p1 : p2;
 }
 
@@ -1069,8 +876,10 @@ hipError_t launch_attention(const tv_attn_desc& d, const AttnPlan& plan, const t
   a.depth_out = p.depth_out;
   a.block_idx = p.block_idx;
   a.n_blocks = p.n_blocks;
-  a.part_o = reinterpret_cast<bf16*>(workspace);
-  a.part_ml = reinterpret_cast<float2*>(reinterpret_cast<char*>(workspace) + plan.ws_o_bytes);
+  // workspace: [merge counters][partial outputs][partial (max, sum)]
+  char* const ws = reinterpret_cast<char*>(workspace);
+  a.part_o = reinterpret_cast<bf16*>(ws + plan.ws_sync_bytes);
+  a.part_ml = reinterpret_cast<float2*>(ws + plan.ws_sync_bytes + plan.ws_o_bytes);
   a.dev_err = dev_err;
   a.out = (bf16*)p.out;
   a.lse = p.lse;
@@ -1098,11 +907,27 @@ hipError_t launch_attention(const tv_attn_desc& d, const AttnPlan& plan, const t
   const float scale = d.softmax_scale > 0.f ? d.softmax_scale : 1.f / sqrtf((float)d.head_dim);
   a.c = scale * 1.44269504088896340736f;
 
-  const dim3 grid(plan.splits + plan.tree_sep, d.n_kv_heads * plan.row_groups, d.batch);
-  if (d.head_dim == 128)
-    launch_split_rb<128>(plan.row_blocks, a, grid, stream);
-  else
-    launch_split_rb<64>(plan.row_blocks, a, grid, stream);
+  if (plan.kind == TV_ATTN_KERNEL_WIDE) {
+    a.nsplit_wg = (plan.splits + plan.tree_sep) * d.batch * d.n_kv_heads * plan.row_groups;
+    const int64_t units_bg = (int64_t)d.batch * d.n_kv_heads;
+    if (2 * units_bg * (int64_t)sizeof(int) <= (int64_t)plan.ws_sync_bytes) {
+      // split and merge workgroups in one launch: no combine kernel
+      a.sync = reinterpret_cast<int*>(ws);
+      a.ncw_unit = plan.ncw_unit;
+      a.rpw = plan.rpw;
+      const unsigned grid = (unsigned)(a.nsplit_wg + units_bg * plan.ncw_unit);
+      return launch_wide(a, d.head_dim, plan.row_blocks, grid, stream);
+    }
+    a.sync = nullptr;  // too many units for the counters: merge in a second launch
+    hipError_t e = launch_wide(a, d.head_dim, plan.row_blocks, (unsigned)a.nsplit_wg, stream);
+    if (e != hipSuccess) return e;
+  } else {
+    const dim3 grid(plan.splits + plan.tree_sep, d.n_kv_heads * plan.row_groups, d.batch);
+    if (d.head_dim == 128)
+      launch_split_rb<128>(plan.row_blocks, a, grid, stream);
+    else
+      launch_split_rb<64>(plan.row_blocks, a, grid, stream);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 

@@ -32,7 +32,12 @@ struct AttnPlan {
                      // 0: it runs in the last non-empty prefix split
   int chunk;         // prefix slots per split (multiple of the 32-token tile)
   int prefix_slots;  // upper bound of prefix slots per sequence
+  int kind;          // TV_ATTN_KERNEL_SPLIT16 or TV_ATTN_KERNEL_WIDE
   size_t ws_o_bytes, ws_ml_bytes;
+  size_t ws_sync_bytes;  // counters of the in-launch merge, first in the workspace (zero between calls)
+  int ncw_unit;          // 32-row kernel: merge workgroups per (sequence, kv head)
+  int rpw;               // rows merged per wave
+  size_t ws_bytes() const { return ws_o_bytes + ws_ml_bytes + ws_sync_bytes; }
 };
 
 AttnPlan plan_attention(const tv_attn_desc& d, int cu_count);
