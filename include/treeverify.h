@@ -203,6 +203,27 @@ tv_status tv_tree_attention(const tv_attn_desc* desc, const tv_attn_ptrs* ptrs, 
                             size_t workspace_bytes, int32_t* dev_err, hipStream_t stream);
 
 /*
+ * tv_tree_attention_noalloc -- tv_tree_attention without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops or harnesses that forbid allocation).
+ *
+ * The workspace is a library-owned device array of
+ * TV_ATTN_NOALLOC_SCRATCH_BYTES on each device, held until the process
+ * ends; the call allocates nothing.  Same descriptor, pointers, results and
+ * errors as tv_tree_attention, plus TV_ERR_WORKSPACE when the descriptor
+ * needs more than TV_ATTN_NOALLOC_SCRATCH_BYTES
+ * (tv_tree_attention_workspace_size tells), and TV_ERR_DEVICE when the
+ * array's address cannot be found on the current device.  Every call on a
+ * device shares that device's array: calls that overlap in time on one
+ * device (other streams, other threads) race and must not be issued.  Each
+ * call first clears the array's merge counters with a small kernel on
+ * `stream`.
+ */
+#define TV_ATTN_NOALLOC_SCRATCH_BYTES 33554432
+tv_status tv_tree_attention_noalloc(const tv_attn_desc* desc, const tv_attn_ptrs* ptrs,
+                                    int32_t* dev_err, hipStream_t stream);
+
+/*
  * tv_greedy_accept -- temperature-0 acceptance of a verified tree.
  *
  * Sources: SpecBlock Sec. 4 (greedy decoding at T = 0), App. A.5 (the longest

@@ -211,6 +211,7 @@ def test_binding_constants_match_the_header():
     defs = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define\s+(TV_\w+)\s+(\d+)", text)}
     assert defs["TV_ATTN_WS_COUNTER_BYTES"] == binding.ATTN_WS_COUNTER_BYTES
     assert defs["TV_DERR_SYNC"] == binding.DERR_SYNC
+    assert defs["TV_ATTN_NOALLOC_SCRATCH_BYTES"] == binding.ATTN_NOALLOC_SCRATCH_BYTES
     enums = dict(re.findall(r"(TV_ATTN_KERNEL_\w+)\s*=\s*(\d+)", text))
     assert [int(enums[k]) for k in ("TV_ATTN_KERNEL_AUTO", "TV_ATTN_KERNEL_SPLIT16", "TV_ATTN_KERNEL_WIDE")] == \
         [binding.KERNEL_AUTO, binding.KERNEL_SPLIT16, binding.KERNEL_WIDE]

@@ -98,6 +98,9 @@ def lib() -> ctypes.CDLL:
             L.tv_tree_attention_num_splits.restype = i32
             L.tv_tree_attention.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(AttnPtrs),
                                             vp, sz, vp, vp]
+            L.tv_tree_attention_noalloc.argtypes = [ctypes.POINTER(AttnDesc),
+                                                    ctypes.POINTER(AttnPtrs), vp, vp]
+            L.tv_tree_attention_noalloc.restype = i32
             L.tv_tree_attention.restype = i32
             L.tv_greedy_accept_workspace_size.argtypes = [i32, i32, i64]
             L.tv_greedy_accept_workspace_size.restype = sz
@@ -402,14 +405,10 @@ def attention_num_splits(desc: AttnDesc) -> int:
     return int(lib().tv_tree_attention_num_splits(ctypes.byref(desc)))
 
 
-def tree_attention(q, k_cache, v_cache, k_tree, v_tree, prefix_len, mask, *, max_prefix_len,
-                   block_idx=None, n_blocks=None, block_size=0, scale=0.0, num_splits=0,
-                   tree_placement=TREE_AUTO, kernel=KERNEL_AUTO,
-                   want_lse=False, out=None, lse=None, workspace=None, dev_err=None,
-                   parents=None, mask_out=None, depth_out=None):
-    """bf16 tree-masked GQA attention.  Returns out (and lse if asked).
-    With mask=None and ``parents`` given, the kernel builds the tree mask
-    itself and writes it to ``mask_out`` / ``depth_out`` when given."""
+def _attention_args(q, k_cache, v_cache, k_tree, v_tree, prefix_len, mask, max_prefix_len,
+                    block_idx, n_blocks, block_size, scale, num_splits, tree_placement, kernel,
+                    out, lse, workspace, dev_err, parents, mask_out, depth_out):
+    """Checks shared by the attention calls -> (desc, ptrs)."""
     bf = torch.bfloat16
     _on_gpu("q", q, bf)
     _on_gpu("k_cache", k_cache, bf)
@@ -439,16 +438,6 @@ def tree_attention(q, k_cache, v_cache, k_tree, v_tree, prefix_len, mask, *, max
                      max_blocks=block_idx.shape[1] if partial else 0,
                      scale=scale, num_splits=num_splits, tree_placement=tree_placement,
                      kernel=kernel)
-    if out is None:
-        out = torch.empty_like(q)
-    if want_lse and lse is None:
-        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    ws_bytes = attention_workspace_size(desc)
-    if ws_bytes == 0:
-        raise TVError("tv_tree_attention_workspace_size", 2)
-    if workspace is None or workspace.numel() < ws_bytes:
-        # the leading merge counters must start at zero; calls keep them so
-        workspace = attention_workspace(desc, q.device)
     ptrs = AttnPtrs(q=q.data_ptr(), k_tree=k_tree.data_ptr(), v_tree=v_tree.data_ptr(),
                     k_cache=k_cache.data_ptr(), v_cache=v_cache.data_ptr(),
                     prefix_len=prefix_len.data_ptr(),
@@ -459,10 +448,59 @@ def tree_attention(q, k_cache, v_cache, k_tree, v_tree, prefix_len, mask, *, max
                     parents=parents.data_ptr() if parents is not None else None,
                     mask_out=mask_out.data_ptr() if mask_out is not None else None,
                     depth_out=depth_out.data_ptr() if depth_out is not None else None)
+    return desc, ptrs
+
+
+def tree_attention(q, k_cache, v_cache, k_tree, v_tree, prefix_len, mask, *, max_prefix_len,
+                   block_idx=None, n_blocks=None, block_size=0, scale=0.0, num_splits=0,
+                   tree_placement=TREE_AUTO, kernel=KERNEL_AUTO,
+                   want_lse=False, out=None, lse=None, workspace=None, dev_err=None,
+                   parents=None, mask_out=None, depth_out=None):
+    """bf16 tree-masked GQA attention.  Returns out (and lse if asked).
+    With mask=None and ``parents`` given, the kernel builds the tree mask
+    itself and writes it to ``mask_out`` / ``depth_out`` when given."""
+    if out is None:
+        _on_gpu("q", q, torch.bfloat16)
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    desc, ptrs = _attention_args(q, k_cache, v_cache, k_tree, v_tree, prefix_len, mask,
+                                 max_prefix_len, block_idx, n_blocks, block_size, scale,
+                                 num_splits, tree_placement, kernel, out, lse, workspace, dev_err,
+                                 parents, mask_out, depth_out)
+    ws_bytes = attention_workspace_size(desc)
+    if ws_bytes == 0:
+        raise TVError("tv_tree_attention_workspace_size", 2)
+    if workspace is None or workspace.numel() < ws_bytes:
+        # the leading merge counters must start at zero; calls keep them so
+        workspace = attention_workspace(desc, q.device)
     _check("tv_tree_attention", lib().tv_tree_attention(
         ctypes.byref(desc), ctypes.byref(ptrs), _ptr(workspace), workspace.numel(),
         _err_ptr(dev_err), _stream(q.device)))
     return (out, lse) if want_lse else out
+
+
+ATTN_NOALLOC_SCRATCH_BYTES = 33554432  # the library's per-device workspace of the no-alloc call
+
+
+def tree_attention_noalloc(q, k_cache, v_cache, k_tree, v_tree, prefix_len, mask, *,
+                           max_prefix_len, out, lse=None, block_idx=None, n_blocks=None,
+                           block_size=0, scale=0.0, num_splits=0, tree_placement=TREE_AUTO,
+                           kernel=KERNEL_AUTO, dev_err=None, parents=None, mask_out=None,
+                           depth_out=None):
+    """tv_tree_attention_noalloc: as tree_attention, with the workspace the
+    library's own device array, for callers that cannot allocate.  The
+    outputs are the caller's (``out``, and ``lse`` if wanted); nothing is
+    allocated here or in the call.  Calls on one device must not overlap."""
+    if out is None:
+        raise ValueError("out is required (the no-alloc call allocates nothing)")
+    desc, ptrs = _attention_args(q, k_cache, v_cache, k_tree, v_tree, prefix_len, mask,
+                                 max_prefix_len, block_idx, n_blocks, block_size, scale,
+                                 num_splits, tree_placement, kernel, out, lse, None, dev_err,
+                                 parents, mask_out, depth_out)
+    _check("tv_tree_attention_noalloc", lib().tv_tree_attention_noalloc(
+        ctypes.byref(desc), ctypes.byref(ptrs), _err_ptr(dev_err), _stream(q.device)))
+    return out
 
 
 def accept_workspace_size(batch, n_nodes, vocab) -> int:

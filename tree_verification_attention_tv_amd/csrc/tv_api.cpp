@@ -101,6 +101,33 @@ tv_status check_select_desc(const tv_select_desc* d) {
 
 }  // namespace
 
+namespace tv {
+
+tv_status prepare_attention(const tv_attn_desc* desc, const tv_attn_ptrs* ptrs,
+                            const void* workspace, AttnPlan* plan, bool* empty) {
+  const tv_status st = check_attn_desc(desc);
+  if (st != TV_OK) return st;
+  if (!ptrs) return TV_ERR_NULL;
+  const tv_attn_ptrs& p = *ptrs;
+  if (!p.q || !p.k_tree || !p.v_tree || !p.k_cache || !p.v_cache || !p.prefix_len || !p.out ||
+      !workspace)
+    return TV_ERR_NULL;
+  if (!p.mask && !p.parents) return TV_ERR_NULL;
+  if (p.mask && p.parents) return TV_ERR_SHAPE;
+  if (desc->max_blocks > 0 && (!p.block_idx || !p.n_blocks)) return TV_ERR_NULL;
+  if (!aligned(p.q, 16) || !aligned(p.k_tree, 16) || !aligned(p.v_tree, 16) ||
+      !aligned(p.k_cache, 16) || !aligned(p.v_cache, 16) || !aligned(p.out, 16))
+    return TV_ERR_UNSUPPORTED;
+  *empty = desc->batch == 0;
+  if (*empty) return TV_OK;
+  const int cus = cu_count_for_current_device();
+  if (cus <= 0) return TV_ERR_DEVICE;
+  *plan = plan_attention(*desc, cus);
+  return TV_OK;
+}
+
+}  // namespace tv
+
 extern "C" {
 
 tv_status tv_build_tree_mask(const int32_t* parents, int32_t batch, int32_t n_nodes,
@@ -119,6 +146,7 @@ int32_t tv_tree_attention_num_splits(const tv_attn_desc* desc) {
   return tv::plan_attention(*desc, cus).splits;
 }
 
+
 size_t tv_tree_attention_workspace_size(const tv_attn_desc* desc) {
   if (check_attn_desc(desc) != TV_OK) return 0;
   const int cus = cu_count_for_current_device();
@@ -129,26 +157,13 @@ size_t tv_tree_attention_workspace_size(const tv_attn_desc* desc) {
 
 tv_status tv_tree_attention(const tv_attn_desc* desc, const tv_attn_ptrs* ptrs, void* workspace,
                             size_t workspace_bytes, int32_t* dev_err, hipStream_t stream) {
-  const tv_status st = check_attn_desc(desc);
-  if (st != TV_OK) return st;
-  if (!ptrs) return TV_ERR_NULL;
-  const tv_attn_ptrs& p = *ptrs;
-  if (!p.q || !p.k_tree || !p.v_tree || !p.k_cache || !p.v_cache || !p.prefix_len || !p.out ||
-      !workspace)
-    return TV_ERR_NULL;
-  if (!p.mask && !p.parents) return TV_ERR_NULL;
-  if (p.mask && p.parents) return TV_ERR_SHAPE;
-  if (desc->max_blocks > 0 && (!p.block_idx || !p.n_blocks)) return TV_ERR_NULL;
-  if (!aligned(p.q, 16) || !aligned(p.k_tree, 16) || !aligned(p.v_tree, 16) ||
-      !aligned(p.k_cache, 16) || !aligned(p.v_cache, 16) || !aligned(p.out, 16))
-    return TV_ERR_UNSUPPORTED;
-  if (desc->batch == 0) return TV_OK;
-  const int cus = cu_count_for_current_device();
-  if (cus <= 0) return TV_ERR_DEVICE;
-  const tv::AttnPlan plan = tv::plan_attention(*desc, cus);
+  tv::AttnPlan plan{};
+  bool empty = false;
+  const tv_status st = tv::prepare_attention(desc, ptrs, workspace, &plan, &empty);
+  if (st != TV_OK || empty) return st;
   if (!aligned(workspace, 16) || workspace_bytes < plan.ws_bytes())
     return TV_ERR_WORKSPACE;
-  return launch_status(tv::launch_attention(*desc, plan, p, workspace, dev_err, stream));
+  return launch_status(tv::launch_attention(*desc, plan, *ptrs, workspace, dev_err, stream));
 }
 
 size_t tv_greedy_accept_workspace_size(int32_t batch, int32_t n_nodes, int64_t vocab) {

@@ -41,6 +41,10 @@ struct AttnPlan {
 };
 
 AttnPlan plan_attention(const tv_attn_desc& d, int cu_count);
+// Argument checks of tv_tree_attention other than the workspace size, then
+// the plan for the current device; *empty: batch 0, nothing to launch.
+tv_status prepare_attention(const tv_attn_desc* desc, const tv_attn_ptrs* ptrs,
+                            const void* workspace, AttnPlan* plan, bool* empty);
 
 hipError_t launch_attention(const tv_attn_desc& d, const AttnPlan& plan, const tv_attn_ptrs& p,
                             void* workspace, int32_t* dev_err, hipStream_t stream);
