@@ -76,10 +76,20 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
   __shared__ int s_par[TV_MAX_NODES];                             // parents (in-kernel mask)
   __shared__ int s_first, s_bad;
 
-  const int s = blockIdx.x;
-  const int g = blockIdx.y / a.row_groups;
-  const int rg = blockIdx.y % a.row_groups;
-  const int b = blockIdx.z;
+  if ((int)blockIdx.x >= a.nsplit_wg) {
+    merge_role<D, kWaves>(a, (int)blockIdx.x - a.nsplit_wg);
+    return;
+  }
+  // Workgroup -> (split, unit), units varying fastest: with a multiple of 8
+  // units every split of a unit lands on the same XCD (workgroups are dealt
+  // to the XCDs in turn).
+  const int units = a.batch * a.hkv * a.row_groups;
+  const int unit = (int)blockIdx.x % units;
+  const int s = (int)blockIdx.x / units;
+  const int b = unit / (a.hkv * a.row_groups);
+  const int g = (unit / a.row_groups) % a.hkv;
+  const int rg = unit % a.row_groups;
+  {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -242,9 +252,9 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
     // that the combine reads every split without the prefix length
     for (int mb = 0; mb < RB; ++mb) {
       const int m = row0 + 16 * mb + col;
-      if (active && m < a.rows && grp4 == 0) a.part_ml[prow0 + m] = make_float2(-INFINITY, 0.f);
+      if (active && m < a.rows && grp4 == 0) store_ml<true>(a.part_ml + prow0 + m, make_float2(-INFINITY, 0.f));
     }
-    return;
+    goto done;
   }
 
   // ---- per-split tables staged in LDS --------------------------------------
@@ -312,9 +322,9 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
         if (err) raise_err(a.dev_err, err);
         for (int mb = 0; mb < RB; ++mb) {
           const int m = row0 + 16 * mb + col;
-          if (active && m < a.rows && grp4 == 0) a.part_ml[prow0 + m] = make_float2(-INFINITY, 0.f);
+          if (active && m < a.rows && grp4 == 0) store_ml<true>(a.part_ml + prow0 + m, make_float2(-INFINITY, 0.f));
         }
-        return;
+        goto done;
       }
       np = 0;
     } else {
@@ -703,7 +713,7 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
   // runs.  Staging address of row r, 32-byte chunk ch: r * 2D + 32 (ch ^ z(r))
   // with z(r) = (r / RPB) mod DB, so that the 16 rows written by one
   // instruction, and the rows read back by one, cover all 64 banks.
-  if (!active) return;
+  if (!active) goto done;
   {
     constexpr int RPB = 128 / D;  // rows per 256-byte row of banks
     constexpr int RPI = 512 / D;  // rows per 1 KB store
@@ -723,7 +733,7 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
         *(__attribute__((address_space(3))) bf16x4*)lds_at(
             stage + r * (2 * D) + 32 * (db ^ ((r / RPB) & (DB - 1))) + 8 * grp4) = v;
       }
-      if (grp4 == 0 && row0 + r < a.rows) a.part_ml[prow0 + row0 + r] = make_float2(mref[mb], l);
+      if (grp4 == 0 && row0 + r < a.rows) store_ml<true>(a.part_ml + prow0 + row0 + r, make_float2(mref[mb], l));
     }
 #pragma unroll
     for (int j = 0; j < 16 * RB / RPI; ++j) {
@@ -731,9 +741,14 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
       const int q = lane % QPR;
       const bf16x8 v = *(__attribute__((address_space(3))) const bf16x8*)lds_at(
           stage + r * (2 * D) + 32 * ((q >> 1) ^ ((r / RPB) & (DB - 1))) + 16 * (q & 1));
-      if (row0 + r < a.rows) *reinterpret_cast<bf16x8*>(a.part_o + (prow0 + row0 + r) * D + 8 * q) = v;
+      if (row0 + r < a.rows) store_o<true>(a.part_o + (prow0 + row0 + r) * D + 8 * q, v);
     }
   }
+  }
+done:
+  // (every path of the split work ends here: the signal below counts the
+  // workgroup's partials, empty ones included)
+  if (a.sync) split_done(a, unit / a.row_groups);
 }
 
 
@@ -841,23 +856,39 @@ AttnPlan plan_rows(const tv_attn_desc& d, int cu_count, int max_rb, int* crit) {
 // prefix of an 8B layer, where each workgroup has 4 tiles either way; at a
 // 60000-token prefix, where the grid is already full, the doubled
 // workgroups lose).  The plan with the shorter longest workgroup wins.
+// The 16-row schedule merges in a second launch: measured on MI355X with
+// the 1000-token prefix of an 8B layer, its merge workgroups (dispatched
+// beside the splits, spinning from the start) ended the launch 21.5 us
+// after its start, against 11.4 + 4.7 us for the split and merge launches.
+// Merge workgroups of the in-launch merge: `waves` waves of rpw rows each
+// (rows go two to a wave's memory round trip, so rpw is even), about
+// `slots` workgroups over the whole chip.
+void set_merge_shape(const tv_attn_desc& d, int waves, int slots, AttnPlan* p) {
+  const int64_t all_rows = (int64_t)d.batch * d.n_kv_heads * p->rows;
+  const int64_t per = (all_rows + (int64_t)waves * slots - 1) / ((int64_t)waves * slots);
+  p->rpw = (int)std::max<int64_t>(2, (per + 1) / 2 * 2);
+  p->ncw_unit = (p->rows + waves * p->rpw - 1) / (waves * p->rpw);
+}
+
 AttnPlan plan_attention(const tv_attn_desc& d, int cu_count) {
   int crit2 = 0, crit1 = 0;
   if (d.kernel == TV_ATTN_KERNEL_WIDE) {
-    // 32-row MFMA tiles, one or two per wave: 128 or 256 rows per workgroup;
-    // the merge runs in the same launch, about one workgroup per CU
+    // 32-row MFMA tiles, one or two per wave: 128 or 256 rows per workgroup
+    // (one workgroup per CU)
     AttnPlan p = plan_rows(d, cu_count, 2, &crit2);
     p.kind = TV_ATTN_KERNEL_WIDE;
-    const int64_t all_rows = (int64_t)d.batch * d.n_kv_heads * p.rows;
-    p.rpw = (int)std::max<int64_t>(1, (all_rows + 4 * (int64_t)cu_count - 1) / (4 * (int64_t)cu_count));
-    p.ncw_unit = (p.rows + 4 * p.rpw - 1) / (4 * p.rpw);
+    set_merge_shape(d, 4, cu_count, &p);
+    p.merge_in_launch = true;
     return p;
   }
+  // 16-row MFMA tiles, two workgroups per CU
   AttnPlan p2 = plan_rows(d, cu_count, 2, &crit2);
   p2.kind = TV_ATTN_KERNEL_SPLIT16;
+  set_merge_shape(d, kWaves, 2 * cu_count, &p2);
   if (p2.row_blocks == 1) return p2;
   AttnPlan p1 = plan_rows(d, cu_count, 1, &crit1);
   p1.kind = TV_ATTN_KERNEL_SPLIT16;
+  set_merge_shape(d, kWaves, 2 * cu_count, &p1);
   return 13 * crit1 < 20 * crit2 ? p1 : p2;
 }
 
@@ -907,29 +938,27 @@ hipError_t launch_attention(const tv_attn_desc& d, const AttnPlan& plan, const t
   const float scale = d.softmax_scale > 0.f ? d.softmax_scale : 1.f / sqrtf((float)d.head_dim);
   a.c = scale * 1.44269504088896340736f;
 
+  // split workgroups, then (when the counters hold every unit) the merge
+  // workgroups of the same launch; else a second launch merges
+  a.nsplit_wg = (plan.splits + plan.tree_sep) * d.batch * d.n_kv_heads * plan.row_groups;
+  const int64_t units_bg = (int64_t)d.batch * d.n_kv_heads;
+  const bool merge_in_launch =
+      plan.merge_in_launch && 2 * units_bg * (int64_t)sizeof(int) <= (int64_t)plan.ws_sync_bytes;
+  a.sync = merge_in_launch ? reinterpret_cast<int*>(ws) : nullptr;
+  a.ncw_unit = plan.ncw_unit;
+  a.rpw = plan.rpw;
+  const unsigned grid = (unsigned)(a.nsplit_wg + (merge_in_launch ? units_bg * plan.ncw_unit : 0));
   if (plan.kind == TV_ATTN_KERNEL_WIDE) {
-    a.nsplit_wg = (plan.splits + plan.tree_sep) * d.batch * d.n_kv_heads * plan.row_groups;
-    const int64_t units_bg = (int64_t)d.batch * d.n_kv_heads;
-    if (2 * units_bg * (int64_t)sizeof(int) <= (int64_t)plan.ws_sync_bytes) {
-      // split and merge workgroups in one launch: no combine kernel
-      a.sync = reinterpret_cast<int*>(ws);
-      a.ncw_unit = plan.ncw_unit;
-      a.rpw = plan.rpw;
-      const unsigned grid = (unsigned)(a.nsplit_wg + units_bg * plan.ncw_unit);
-      return launch_wide(a, d.head_dim, plan.row_blocks, grid, stream);
-    }
-    a.sync = nullptr;  // too many units for the counters: merge in a second launch
-    hipError_t e = launch_wide(a, d.head_dim, plan.row_blocks, (unsigned)a.nsplit_wg, stream);
-    if (e != hipSuccess) return e;
+    hipError_t e = launch_wide(a, d.head_dim, plan.row_blocks, grid, stream);
+    if (e != hipSuccess || merge_in_launch) return e;
   } else {
-    const dim3 grid(plan.splits + plan.tree_sep, d.n_kv_heads * plan.row_groups, d.batch);
     if (d.head_dim == 128)
-      launch_split_rb<128>(plan.row_blocks, a, grid, stream);
+      launch_split_rb<128>(plan.row_blocks, a, dim3(grid), stream);
     else
-      launch_split_rb<64>(plan.row_blocks, a, grid, stream);
+      launch_split_rb<64>(plan.row_blocks, a, dim3(grid), stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || merge_in_launch) return e;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
 
   const int64_t rows_total = (int64_t)d.batch * d.n_nodes * d.n_q_heads;  // one wave each
   const dim3 cgrid((unsigned)((rows_total + kThreads / 64 - 1) / (kThreads / 64)));

@@ -197,7 +197,7 @@ template <int D, int NR, bool COH>
 __device__ __forceinline__ void combine_rows(const AttnArgs& a, const int64_t (&rowid)[NR], int lane) {
   constexpr int C = D / 8;
   constexpr int T = 64 / C;
-  constexpr int U = 8;
+  constexpr int U = 8 / NR;  // 8 partial loads in flight per lane
   const int c = lane % C;
   const int t = lane / C;
   // Every split writes a partial for every row (an empty one, m = -inf,
@@ -296,6 +296,70 @@ __device__ __forceinline__ void combine_rows(const AttnArgs& a, const int64_t (&
     *reinterpret_cast<bf16x8*>(a.out + rowid[r] * D + 8 * c) = res;
     if (c == 0 && a.lse) a.lse[rowid[r]] = lse_v;
   }
+}
+
+// ---- merge inside the launch ------------------------------------------------
+// The grid of a schedule holds nsplit_wg split workgroups, then ncw_unit
+// merge workgroups per (sequence, kv head) unit u = b * hkv + g.  A split
+// workgroup, once its partials are stored, adds 1 to sync[u]; the merge
+// workgroups of u wait until sync[u] counts all nparts * row_groups of them,
+// merge NW * rpw rows each, and count themselves in sync[batch * hkv + u];
+// the last one resets both counters to zero for the next call.  Merge
+// workgroups follow every split workgroup in dispatch order, so their wait
+// depends only on workgroups already running or done; it is bounded all the
+// same (TV_DERR_SYNC past the bound).
+constexpr unsigned kSpinLimit = 1u << 22;  // polls of the merge wait, s_sleep 2 apart
+
+template <int D, int NW>
+__device__ __forceinline__ void merge_role(const AttnArgs& a, int j) {
+  const int units_bg = a.batch * a.hkv;
+  const int u = j % units_bg;
+  const int slice = j / units_bg;
+  const int mb = u / a.hkv, mg = u % a.hkv;
+  if (threadIdx.x == 0) {
+    const int target = a.nparts * a.row_groups;
+    // The partials are read with device-coherent loads after the barrier
+    // below, so relaxed polls suffice (an acquire would also invalidate
+    // this XCD's L2 under the split workgroups still streaming).
+    int v = __hip_atomic_load(&a.sync[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (unsigned it = 0; v < target && it < kSpinLimit; ++it) {
+      __builtin_amdgcn_s_sleep(2);
+      v = __hip_atomic_load(&a.sync[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (v < target) raise_err(a.dev_err, TV_DERR_SYNC);
+  }
+  __syncthreads();
+  const int wv = threadIdx.x >> 6;
+  const int r0 = (slice * NW + wv) * a.rpw;  // first row of this wave: node * grp + head in group
+  auto rowid_of = [&](int r) -> int64_t {
+    if (r >= a.rows || r >= r0 + a.rpw) return -1;
+    const int i = r / a.grp;
+    return ((int64_t)mb * a.n + i) * a.hq + mg * a.grp + (r - i * a.grp);
+  };
+  for (int q = 0; q < a.rpw; q += 2) {
+    const int64_t ids[2] = {rowid_of(r0 + q), rowid_of(r0 + q + 1)};
+    combine_rows<D, 2, true>(a, ids, threadIdx.x & 63);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int done = __hip_atomic_fetch_add(&a.sync[units_bg + u], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == a.ncw_unit - 1) {
+      __hip_atomic_store(&a.sync[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.sync[units_bg + u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// A split workgroup of unit u has stored its partials.  They went out as
+// device-coherent stores: once they have completed (vmcnt 0 in every wave,
+// then the barrier) the merge's coherent loads see them on any XCD.  A
+// release fence would instead write back this XCD's whole L2, which
+// stretches the tail of the split workgroups still running by tens of
+// microseconds (measured at the 60000-token prefix).
+__device__ __forceinline__ void split_done(const AttnArgs& a, int u) {
+  vm_wait<0>();
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(&a.sync[u], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // launch of the 32-row kernel (tv_attn_wide.hip): grid of (splits + tree_sep)

@@ -36,7 +36,6 @@ constexpr int kWWaves = 4;
 constexpr int kWThreads = kWWaves * 64;
 constexpr int kWRing = 8;   // LDS ring slots, a power of two
 constexpr int kWAhead = 7;  // tiles requested ahead of the one in use (< kWRing)
-constexpr unsigned kSpinLimit = 1u << 22;  // merge wait bound (s_sleep 2 per poll: a fraction of a second)
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -78,49 +77,7 @@ void attn_wide_kernel(AttnArgs a) {
   __shared__ int s_first, s_bad, s_redo;
 
   if ((int)blockIdx.x >= a.nsplit_wg) {
-    // ---- merge role: rows of one (sequence, kv head) unit, after every
-    // split workgroup of that unit has written its partials.  These
-    // workgroups come after all split workgroups in dispatch order, so the
-    // wait below depends only on workgroups that are already running or
-    // done; it is bounded all the same (TV_DERR_SYNC past the limit).
-    const int units_bg = a.batch * a.hkv;
-    const int j = (int)blockIdx.x - a.nsplit_wg;
-    const int u = j % units_bg;
-    const int slice = j / units_bg;
-    const int mb = u / a.hkv, mg = u % a.hkv;
-    if (threadIdx.x == 0) {
-      const int target = a.nparts * a.row_groups;
-      // The partials are read with device-coherent loads after the barrier
-      // below, so relaxed polls suffice (an acquire would also invalidate
-      // this XCD's L2 under the split workgroups still streaming).
-      int v = __hip_atomic_load(&a.sync[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      for (unsigned it = 0; v < target && it < kSpinLimit; ++it) {
-        __builtin_amdgcn_s_sleep(2);
-        v = __hip_atomic_load(&a.sync[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      if (v < target) raise_err(a.dev_err, TV_DERR_SYNC);
-    }
-    __syncthreads();
-    const int wv = threadIdx.x >> 6;
-    const int r0 = (slice * kWWaves + wv) * a.rpw;  // first row of this wave: node * grp + head in group
-    auto rowid_of = [&](int r) -> int64_t {
-      if (r >= a.rows || r >= r0 + a.rpw) return -1;
-      const int i = r / a.grp;
-      return ((int64_t)mb * a.n + i) * a.hq + mg * a.grp + (r - i * a.grp);
-    };
-    for (int q = 0; q < a.rpw; q += 2) {
-      const int64_t ids[2] = {rowid_of(r0 + q), rowid_of(r0 + q + 1)};
-      combine_rows<D, 2, true>(a, ids, threadIdx.x & 63);
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      // the last merge of the unit leaves both counters at zero for the next call
-      const int done = __hip_atomic_fetch_add(&a.sync[units_bg + u], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (done == a.ncw_unit - 1) {
-        __hip_atomic_store(&a.sync[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&a.sync[units_bg + u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
+    merge_role<D, kWWaves>(a, (int)blockIdx.x - a.nsplit_wg);
     return;
   }
 
@@ -745,21 +702,7 @@ void attn_wide_kernel(AttnArgs a) {
 
   };
   split_role();
-  // Signal the merge workgroups of this (sequence, kv head).
-  if (!a.sync) return;  // merged by a second launch
-  // The partials went out as device-coherent stores: once they have
-  // completed (vmcnt 0 in every wave, then the barrier) they are visible to
-  // the merge's coherent loads on any XCD.  A release fence would instead
-  // write back this XCD's whole L2, which stretches the tail of the
-  // remaining split workgroups by tens of microseconds.
-  vm_wait<0>();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int units = a.batch * a.hkv * a.row_groups;
-    const int unit = blockIdx.x % units;
-    const int u = unit / a.row_groups;  // b * hkv + g
-    __hip_atomic_fetch_add(&a.sync[u], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (a.sync) split_done(a, (int)(blockIdx.x % (a.batch * a.hkv * a.row_groups)) / a.row_groups);
 }
 
 template <int D, int RT>

@@ -37,6 +37,7 @@ struct AttnPlan {
   size_t ws_sync_bytes;  // counters of the in-launch merge, first in the workspace (zero between calls)
   int ncw_unit;          // 32-row kernel: merge workgroups per (sequence, kv head)
   int rpw;               // rows merged per wave
+  bool merge_in_launch;  // merge workgroups in the split launch (else a second launch)
   size_t ws_bytes() const { return ws_o_bytes + ws_ml_bytes + ws_sync_bytes; }
 };
 
