@@ -338,8 +338,9 @@ def test_accept_workspace_reused_across_calls():
 # a7 commit
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["tiny", "8b_layer", "batched"])
+@pytest.mark.parametrize("name", NAMED)
 def test_commit_named(workloads, name):
+    # long_context: the accepted rows land at cache rows 60000 and after
     _say(f"[commit] {name}")
     dw = workloads(name)
     wl = dw.wl
@@ -528,6 +529,31 @@ def _accept_commit_vs_two_calls(dw, prefix=None, parents=None, alias=False, labe
 def test_accept_commit_matches_two_calls(workloads, name):
     _say(f"[accept+commit] {name}")
     assert _accept_commit_vs_two_calls(workloads(name), label=name) == 0
+
+
+@pytest.mark.parametrize("name", NAMED)
+def test_accept_commit_vs_oracle(workloads, name):
+    # the fused call against the oracle's acceptance followed by its commit
+    _say(f"[accept+commit vs oracle] {name}")
+    dw = workloads(name)
+    wl = dw.wl
+    kc, vc = dw.k_cache.clone(), dw.v_cache.clone()
+    pre = dw.prefix_len.clone()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    amax, alen, path, bonus, newp = binding.greedy_accept_commit(
+        dw.logits, dw.parents, dw.draft, dw.k_tree, dw.v_tree, pre, kc, vc, dev_err=err)
+    torch.cuda.synchronize()
+    r_amax, r_alen, r_path, r_bonus = oracle.greedy_accept(wl.logits, wl.parents, wl.draft_tokens)
+    assert np.array_equal(amax.cpu().numpy(), r_amax)
+    assert np.array_equal(alen.cpu().numpy(), r_alen)
+    assert np.array_equal(path.cpu().numpy(), r_path)
+    assert np.array_equal(bonus.cpu().numpy(), r_bonus)
+    rk, rv, rp = oracle.commit_kv(wl.k_tree, wl.v_tree, r_path, r_alen, wl.prefix_len,
+                                  wl.k_cache, wl.v_cache)
+    assert np.array_equal(newp.cpu().numpy(), rp)
+    assert np.array_equal(bf16_host(kc), rk)
+    assert np.array_equal(bf16_host(vc), rv)
+    assert int(err.item()) == 0
 
 
 def test_accept_commit_edge_cases(workloads):
