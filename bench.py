@@ -49,6 +49,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, vendor figure
+STREAM_BYTES = 2 << 30          # buffer of the measured stream-read peak
 MALL_BYTES = 256 * 1024 * 1024  # Infinity Cache
 COPY_BYTES = 256 * 1024 * 1024  # calibration copy size
 ATTN_SOURCE = os.path.join(ROOT, "tree_verification_attention_tv_amd", "csrc", "tv_attention.hip")
@@ -155,7 +157,9 @@ class StepRunner:
         self.wl, self.partial, self.dev = wl, partial, dev
         self.binding = binding
         first = InputSet(wl, dev, torch, np)
-        rot = 1 if warm else max(2, int(np.ceil(1.25 * MALL_BYTES / first.nbytes())))
+        # at least three copies, and together 1.25x the Infinity Cache, so
+        # that no call finds its inputs cached by the previous ones
+        rot = 1 if warm else max(3, int(np.ceil(1.25 * MALL_BYTES / first.nbytes())))
         self.rot = min(rot, 64)
         self.sets = [first] + [InputSet(wl, dev, torch, np) for _ in range(self.rot - 1)]
         for i, st in enumerate(self.sets):
@@ -293,23 +297,26 @@ class StepRunner:
     # -- timing ----------------------------------------------------------------
     def timed(self, fn, iters):
         """Average microseconds of `fn` over `iters` back-to-back calls, from
-        HIP events recorded on the stream the library launches on."""
+        HIP events recorded on the stream the library launches on; the
+        per-call times (an event between consecutive calls) go to
+        self.last_samples."""
         import torch
-        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
         torch.cuda.synchronize()
-        a.record(self.stream)
+        ev[0].record(self.stream)
         for k in range(iters):
             fn(self.sets[k % self.rot])
-        z.record(self.stream)
+            ev[k + 1].record(self.stream)
         torch.cuda.synchronize()
-        return a.elapsed_time(z) * 1e3 / iters
+        self.last_samples = [ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(iters)]
+        return ev[0].elapsed_time(ev[iters]) * 1e3 / iters
 
-    def timed_graph(self, fn, per_graph=20, reps=5):
+    def timed_graph(self, fn, per_graph=20, reps=10):
         """Average microseconds of one call of `fn` on the GPU: `per_graph`
         calls over the rotated input copies captured in one HIP graph, whose
         replays are timed with HIP events on the library's stream.  No host
         launch overhead enters; the dispatch gaps between the graph's kernels
-        do."""
+        do.  Per-call times of each replay go to self.last_samples."""
         import torch
         g = torch.cuda.CUDAGraph()
         torch.cuda.synchronize()
@@ -319,14 +326,15 @@ class StepRunner:
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(self.stream)
-        for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(self.stream)
+        for k in range(reps):
             g.replay()
-        z.record(self.stream)
+            ev[k + 1].record(self.stream)
         torch.cuda.synchronize()
         del g
-        return a.elapsed_time(z) * 1e3 / (reps * per_graph)
+        self.last_samples = [ev[k].elapsed_time(ev[k + 1]) * 1e3 / per_graph for k in range(reps)]
+        return ev[0].elapsed_time(ev[reps]) * 1e3 / (reps * per_graph)
 
     def check_errors(self):
         if int(self.err.item()) != 0:
@@ -388,6 +396,7 @@ def measure(wl, partial, steps, warmup, warm, num_splits, dev, graph=True, specp
     eager_us = r.timed(r.step, steps)
     wall_us = (time.perf_counter() - t0) * 1e6 / steps
     step_us = eager_us
+    r.step_stats = spread(r.last_samples)
     if graph:
         r.capture()
         for k in range(warmup):
@@ -395,44 +404,97 @@ def measure(wl, partial, steps, warmup, warm, num_splits, dev, graph=True, specp
         t0 = time.perf_counter()
         step_us = r.timed(r.replay, steps)
         wall_us = (time.perf_counter() - t0) * 1e6 / steps
+        r.step_stats = spread(r.last_samples)
     # per-call GPU time from graph replays (eager back-to-back calls would
     # also measure the host's launch rate)
-    tm = r.timed_graph if graph else (lambda fn, **kw: r.timed(fn, max(steps, 50)))
-    calls = {"mask": tm(r.k_mask), "attention": tm(r.k_attn), "accept": tm(r.k_accept),
-             "commit": tm(r.k_commit), "accept_commit": tm(r.k_accept_commit)}
+    tm0 = r.timed_graph if graph else (lambda fn, **kw: r.timed(fn, max(steps, 50)))
+    r.call_stats = {}
+
+    def tm(fn, name, **kw):
+        v = tm0(fn, **kw)
+        r.call_stats[name] = spread(r.last_samples)
+        return v
+    calls = {"mask": tm(r.k_mask, "mask"), "attention": tm(r.k_attn, "attention"),
+             "accept": tm(r.k_accept, "accept"), "commit": tm(r.k_commit, "commit"),
+             "accept_commit": tm(r.k_accept_commit, "accept_commit")}
     if not specpv and not partial:
-        calls["accept_stochastic"] = tm(r.k_accept_stochastic)
-        calls["accept_stochastic_filtered"] = tm(r.k_accept_stochastic_filtered)
-        calls["accept_stochastic_top_p"] = tm(r.k_accept_stochastic_top_p)
+        calls["accept_stochastic"] = tm(r.k_accept_stochastic, "accept_stochastic")
+        calls["accept_stochastic_filtered"] = tm(r.k_accept_stochastic_filtered,
+                                                 "accept_stochastic_filtered")
+        calls["accept_stochastic_top_p"] = tm(r.k_accept_stochastic_top_p,
+                                              "accept_stochastic_top_p")
     if specpv:
-        calls["select"] = tm(r.k_select)
-        calls["summaries_update"] = tm(r.k_summ_update)
-        calls["summaries_full"] = tm(r.k_summ_full, per_graph=5)
+        calls["select"] = tm(r.k_select, "select")
+        calls["summaries_update"] = tm(r.k_summ_update, "summaries_update")
+        calls["summaries_full"] = tm(r.k_summ_full, "summaries_full", per_graph=5)
     r.check_errors()
     return r, step_us, wall_us, eager_us, calls
 
 
-def secondary_line(name, partial, steps, dev):
+def spread(samples):
+    """p10 / p50 / p90 of per-call microseconds."""
+    import numpy as np
+    q = np.percentile(np.asarray(samples, dtype=np.float64), [10, 50, 90])
+    return {"p10": round(float(q[0]), 3), "p50": round(float(q[1]), 3),
+            "p90": round(float(q[2]), 3)}
+
+
+def attention_flops(wl, partial):
+    """Algorithmic MFMA work of one attention call: per (sequence, node,
+    query head) row and visible key, d multiply-adds for q.k and d for p.v
+    (4 d flops); visible keys = the prefix (or its selected blocks) plus the
+    node's ancestors and itself."""
+    import numpy as np
+    b, n = wl.parents.shape
+    depth = np.zeros((b, n), dtype=np.int64)   # parents precede their children
+    for i in range(1, n):
+        depth[:, i] = depth[np.arange(b), wl.parents[:, i]] + 1
+    total = 0
+    for s in range(b):
+        if partial:
+            vis = 0
+            for x in wl.block_idx[s, :int(wl.n_blocks[s])]:
+                lo = int(x) * wl.block_size
+                vis += max(0, min(wl.block_size, int(wl.prefix_len[s]) - lo))
+        else:
+            vis = int(wl.prefix_len[s])
+        total += int(np.sum(vis + depth[s] + 1))
+    return 4 * wl.head_dim * wl.n_q_heads * total
+
+
+def secondary_line(name, partial, steps, dev, stream_gbps=None):
     import torch
 
     from tree_verification_attention_tv_amd import workloads as W
     wl = W.make_workload(name)
     r, step_us, _, eager_us, calls = measure(wl, partial, steps, 5, False, 0, dev)
-    prefix_tokens, kv, attn_bytes, _ = r.bytes()
+    prefix_tokens, kv, attn_bytes, logit_bytes = r.bytes()
     gbps = attn_bytes / (calls["attention"] * 1e-6) / 1e9
+    flops = attention_flops(wl, partial)
+    tflops = flops / (calls["attention"] * 1e-6) / 1e12
     out = {
         "mode": "partial" if partial else "full",
+        "batch": r.b, "n_nodes": r.n,
         "step_us": round(step_us, 3),
+        "step_us_spread": r.step_stats,
         "eager_step_us": round(eager_us, 3),
         "attention_us": round(calls["attention"], 3),
         "kv_bytes": kv,
+        "attention_bytes": attn_bytes,
         "kv_gbps": round(kv / (calls["attention"] * 1e-6) / 1e9, 1),
         "attention_gbps": round(gbps, 1),
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
-        "prefix_tokens": prefix_tokens,
+        "hbm_frac_of_measured_read": round(gbps / stream_gbps, 4) if stream_gbps else None,
+        "attention_flops": flops,
+        "attention_tflops": round(tflops, 1),
+        "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "accept_gbps": round(logit_bytes / (calls["accept"] * 1e-6) / 1e9, 1),
+        "accept_hbm_frac": round(logit_bytes / (calls["accept"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "prefix_tokens": prefix_tokens if r.b <= 4 else [min(prefix_tokens), max(prefix_tokens)],
         "num_splits": r.binding.attention_num_splits(r.desc),
         "cache_rotation": r.rot,
         "call_us": {k: round(v, 3) for k, v in calls.items()},
+        "call_us_spread": r.call_stats,
     }
     del r
     torch.cuda.empty_cache()
@@ -672,6 +734,7 @@ def main():
         copy_calibration(torch, dev)
         return
 
+    stream_gbps = stream_read_gbps(torch, binding, dev)
     wl = W.make_workload(args.workload)
     specpv = args.specpv and args.workload == "long_context"
     partial = specpv or (args.partial and wl.block_idx is not None)
@@ -696,6 +759,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(step_us / 1e3, 6),
+        "step_us_spread": r.step_stats,
         "wall_ms_per_step": round(wall_us / 1e3, 6),
         "step_launch": "hip_graph_replay" if not args.no_graph else "eager",
         "eager_step_us": round(eager_us, 3),
@@ -715,6 +779,8 @@ def main():
         "kv_gbps": round(kv_bytes / (calls["attention"] * 1e-6) / 1e9, 1),
         "kv_hbm_frac": round(kv_bytes / (calls["attention"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "call_us": {k: round(v, 3) for k, v in calls.items()},
+        "call_us_spread": r.call_stats,
+        "stream_read_gbps": round(stream_gbps, 1),
         "accept_gbps": {k: round(logit_bytes / (calls[k] * 1e-6) / 1e9, 1)
                         for k in ("accept", "accept_stochastic", "accept_stochastic_filtered",
                                   "accept_stochastic_top_p") if k in calls},
@@ -729,6 +795,8 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
             "algorithmic_bytes": dom_bytes,
+            "measured_read_peak": round(stream_gbps, 1),
+            "frac_of_measured_read": round(achieved / stream_gbps, 4),
         },
         "secondary": None,
         "cpu_baseline": None,
@@ -738,8 +806,11 @@ def main():
         del r
         torch.cuda.empty_cache()
         result["secondary"] = {
-            "long_context_full": secondary_line("long_context", False, 40, dev),
-            "long_context_partial": secondary_line("long_context", True, 100, dev),
+            "tiny": secondary_line("tiny", False, 100, dev, stream_gbps),
+            "specblock_tree": secondary_line("specblock_tree", False, 100, dev, stream_gbps),
+            "batched": secondary_line("batched", False, 100, dev, stream_gbps),
+            "long_context_full": secondary_line("long_context", False, 40, dev, stream_gbps),
+            "long_context_partial": secondary_line("long_context", True, 100, dev, stream_gbps),
             "long_context_specpv": specpv_line(100, dev),
             "long_context_specpv_rectify": rectify_line(40, dev),
             "multi_layer_8b": multi_layer_line(50, dev),
@@ -747,6 +818,27 @@ def main():
     if not args.no_cpu_baseline and not specpv:
         result["cpu_baseline"] = cpu_baseline(wl, partial, first, acc_out, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def stream_read_gbps(torch, binding, dev, reps=10):
+    """Read bandwidth this device reaches: tv_stream_read over a 2 GiB
+    buffer (8x the Infinity Cache), timed with HIP events."""
+    x = torch.ones(STREAM_BYTES // 4, dtype=torch.int32, device=dev)
+    sink = torch.empty(binding.STREAM_READ_SINK_WORDS, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        binding.stream_read(x, sink)
+    stream = torch.cuda.current_stream(dev)
+    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        binding.stream_read(x, sink)
+    z.record(stream)
+    torch.cuda.synchronize()
+    gbps = STREAM_BYTES * reps / (a.elapsed_time(z) * 1e-3) / 1e9
+    del x
+    torch.cuda.empty_cache()
+    return gbps
 
 
 def cpu_baseline(wl, partial, dev_set, acc_out, seconds):

@@ -559,6 +559,18 @@ tv_status tv_specpv_rectify_tree(const int32_t* buffer_tokens, int32_t n_buffer,
                                  int32_t* parents_out, int32_t* tokens_out);
 
 /* human-readable name of a status code (static storage) */
+/*
+ * tv_stream_read -- measurement aid, not a step of the method: reads
+ * `bytes` (a multiple of 16) at `src` once with 16-byte loads spread over
+ * the whole chip and writes one folding word per workgroup to
+ * sink[0 .. TV_STREAM_READ_SINK_WORDS-1], so that timing it gives the read
+ * bandwidth this device reaches, the ceiling against which the other calls'
+ * bytes per second are judged.  src 16-byte aligned; sink device memory of
+ * TV_STREAM_READ_SINK_WORDS words.
+ */
+#define TV_STREAM_READ_SINK_WORDS 2048
+tv_status tv_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 const char* tv_status_string(tv_status status);
 /* library version: major * 10000 + minor * 100 + patch */
 int32_t tv_version(void);

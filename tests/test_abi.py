@@ -212,6 +212,7 @@ def test_binding_constants_match_the_header():
     assert defs["TV_ATTN_WS_COUNTER_BYTES"] == binding.ATTN_WS_COUNTER_BYTES
     assert defs["TV_DERR_SYNC"] == binding.DERR_SYNC
     assert defs["TV_ATTN_NOALLOC_SCRATCH_BYTES"] == binding.ATTN_NOALLOC_SCRATCH_BYTES
+    assert defs["TV_STREAM_READ_SINK_WORDS"] == binding.STREAM_READ_SINK_WORDS
     enums = dict(re.findall(r"(TV_ATTN_KERNEL_\w+)\s*=\s*(\d+)", text))
     assert [int(enums[k]) for k in ("TV_ATTN_KERNEL_AUTO", "TV_ATTN_KERNEL_SPLIT16", "TV_ATTN_KERNEL_WIDE")] == \
         [binding.KERNEL_AUTO, binding.KERNEL_SPLIT16, binding.KERNEL_WIDE]

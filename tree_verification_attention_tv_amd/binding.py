@@ -101,6 +101,8 @@ def lib() -> ctypes.CDLL:
             L.tv_tree_attention_noalloc.argtypes = [ctypes.POINTER(AttnDesc),
                                                     ctypes.POINTER(AttnPtrs), vp, vp]
             L.tv_tree_attention_noalloc.restype = i32
+            L.tv_stream_read.argtypes = [vp, sz, vp, vp]
+            L.tv_stream_read.restype = i32
             L.tv_tree_attention.restype = i32
             L.tv_greedy_accept_workspace_size.argtypes = [i32, i32, i64]
             L.tv_greedy_accept_workspace_size.restype = sz
@@ -501,6 +503,25 @@ def tree_attention_noalloc(q, k_cache, v_cache, k_tree, v_tree, prefix_len, mask
     _check("tv_tree_attention_noalloc", lib().tv_tree_attention_noalloc(
         ctypes.byref(desc), ctypes.byref(ptrs), _err_ptr(dev_err), _stream(q.device)))
     return out
+
+
+STREAM_READ_SINK_WORDS = 2048
+
+
+def stream_read(src, sink=None):
+    """tv_stream_read over the bytes of a contiguous device tensor (a
+    measurement aid: the read bandwidth the device reaches).  Returns sink."""
+    if not (isinstance(src, torch.Tensor) and src.is_cuda and src.is_contiguous()):
+        raise ValueError("src must be a contiguous device tensor")
+    if sink is None:
+        sink = torch.empty(STREAM_READ_SINK_WORDS, dtype=torch.int32, device=src.device)
+    _on_gpu("sink", sink, torch.int32)
+    if sink.numel() < STREAM_READ_SINK_WORDS:
+        raise ValueError(f"sink must hold {STREAM_READ_SINK_WORDS} words")
+    nbytes = src.numel() * src.element_size()
+    _check("tv_stream_read", lib().tv_stream_read(_ptr(src), nbytes - nbytes % 16, _ptr(sink),
+                                                  _stream(src.device)))
+    return sink
 
 
 def accept_workspace_size(batch, n_nodes, vocab) -> int:

@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libtreeverify.so")
 
 SOURCES = ["tv_api.cpp", "tv_mask.hip", "tv_attention.hip", "tv_attn_wide.hip", "tv_accept.hip",
            "tv_commit.hip", "tv_select.hip", "tv_specpv.cpp", "tv_stochastic.hip",
-           "tv_noalloc.hip"]
+           "tv_noalloc.hip", "tv_probe.hip"]
 # per-source device-code options: the 32-row attention kernel keeps its MFMA
 # accumulators in VGPRs (VGPR-form MFMA), so its softmax reads them directly
 EXTRA_FLAGS = {"tv_attn_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}

@@ -1,0 +1,50 @@
+// tv_stream_read: one pass of 16-byte non-temporal loads over a buffer,
+// grid-strided so that consecutive lanes read consecutive 16-byte pieces and
+// every workgroup keeps several loads in flight per lane.  The loaded words
+// are folded with XOR into one word per workgroup so that no load is dead.
+#include <hip/hip_runtime.h>
+
+#include "tv_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;  // loads in flight per lane
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* src, size_t n16,
+                                                               uint32_t* sink) {
+  const size_t stride = (size_t)gridDim.x * kThreads;
+  size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
+  }
+  for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(src + i);
+  uint32_t w = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  for (int off = 32; off > 0; off >>= 1) w ^= __shfl_xor(w, off);
+  __shared__ uint32_t part[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = w;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = 0;
+    for (int k = 0; k < kThreads / 64; ++k) r ^= part[k];
+    sink[blockIdx.x] = r;
+  }
+}
+
+}  // namespace
+
+tv_status tv_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (!src || !sink) return TV_ERR_NULL;
+  if (bytes % 16 || reinterpret_cast<uintptr_t>(src) % 16) return TV_ERR_UNSUPPORTED;
+  if (bytes == 0) return TV_OK;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(TV_STREAM_READ_SINK_WORDS), dim3(kThreads), 0, stream,
+                     static_cast<const u32x4*>(src), bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_LAUNCH;
+}
