@@ -85,6 +85,9 @@ def parse():
     ap.add_argument("--pmc-summary", nargs=4,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="summarise rocprofv3 FETCH_SIZE/WRITE_SIZE runs into a traffic text")
+    ap.add_argument("--counter-summary", nargs="+", metavar="DIR",
+                    help="condense rocprofv3 --pmc output directories (one per pass) into "
+                         "per-kernel counters and MFMA / VALU / LDS ratios")
     ap.add_argument("--trace-summary", nargs=2, metavar=("STATS_CSV", "COMMAND"),
                     help="condense a rocprofv3 kernel-stats CSV into a text summary")
     return ap.parse_args()
@@ -713,6 +716,9 @@ def main():
     if args.trace_summary:
         trace_summary(*args.trace_summary)
         return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU (asked for {args.gpus}); "
               "multi-GPU sharding is described in the design notes but not built.",
@@ -963,6 +969,59 @@ def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, workload="
                      f"WRITE_SIZE {write.get(k, 0.0):12.1f}")
     lines.append(f"    copy of {COPY_BYTES} B  FETCH_SIZE {cf_k:12.1f}  WRITE_SIZE {cw_k:12.1f}")
     print("\n".join(lines))
+
+
+def counter_summary(dirs, match="attn_", cus=256, simds_per_cu=4, shader_engines=32):
+    """Per kernel (template arguments kept), each counter summed over its
+    instances within a dispatch and averaged over dispatches, from
+    rocprofv3 --pmc output directories (one per pass); then ratios read off
+    them.  Units, as read on MI355X: SQ_VALU_MFMA_BUSY_CYCLES and
+    SQ_VALU_MFMA_COEXEC_CYCLES are cycles summed over SIMDs;
+    SQ_BUSY_CYCLES is cycles summed over the 32 shader engines (so /32 is
+    the dispatch's length in cycles); SQ_BUSY_CU_CYCLES is cycles summed
+    over CUs; SQ_ACTIVE_INST_*, SQ_WAIT_INST_ANY and SQ_WAVE_CYCLES are
+    quad-cycles summed over waves."""
+    per = {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for row in csv.DictReader(fh):
+                    if match not in row["Kernel_Name"]:
+                        continue
+                    k = short_name(row["Kernel_Name"], keep_template=True)
+                    c = per.setdefault(k, {}).setdefault(row["Counter_Name"], {})
+                    c[row["Dispatch_Id"]] = c.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+    print(f"source_sha256_16: {source_hash()}")
+    print("counter averages per dispatch; ratios below each kernel")
+    simds = cus * simds_per_cu
+    for k, cs in sorted(per.items()):
+        avg = {n: sum(v.values()) / len(v) for n, v in cs.items() if v}
+        print(f"\n{k}")
+        for n in sorted(avg):
+            print(f"  {n:32s} {avg[n]:16.1f}")
+        cyc = avg.get("SQ_BUSY_CYCLES", 0.0) / shader_engines
+        mfma = avg.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        if cyc:
+            print(f"  dispatch_cycles                  {cyc:16.1f}")
+        if mfma is not None and cyc:
+            print(f"  mfma_busy_frac (of SIMD cycles)  {mfma / (simds * cyc):16.4f}")
+        if mfma is not None and avg.get("SQ_BUSY_CU_CYCLES"):
+            print(f"  mfma_busy_frac (CU-busy cycles)  "
+                  f"{mfma / (simds_per_cu * avg['SQ_BUSY_CU_CYCLES']):16.4f}")
+        if mfma and "SQ_VALU_MFMA_COEXEC_CYCLES" in avg:
+            print(f"  valu_coexec_of_mfma_busy         {avg['SQ_VALU_MFMA_COEXEC_CYCLES'] / mfma:16.4f}")
+        waves_cyc = 4 * avg.get("SQ_WAVE_CYCLES", 0.0)
+        for n, lab in (("SQ_ACTIVE_INST_VALU", "valu_active_of_wave_cycles"),
+                       ("SQ_ACTIVE_INST_LDS", "lds_active_of_wave_cycles"),
+                       ("SQ_WAIT_INST_ANY", "issue_wait_of_wave_cycles")):
+            if waves_cyc and n in avg:
+                print(f"  {lab:32s} {4 * avg[n] / waves_cyc:16.4f}")
+        mops = avg.get("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        if mops is not None:
+            print(f"  mfma_bf16_flops                  {mops * 512:16.4e}")
+        if avg.get("SQ_ACTIVE_INST_LDS") and "SQ_LDS_BANK_CONFLICT" in avg:
+            print(f"  lds_bank_conflict_cycles_frac    "
+                  f"{avg['SQ_LDS_BANK_CONFLICT'] / (4 * avg['SQ_ACTIVE_INST_LDS']):16.4f}")
 
 
 def trace_summary(stats_csv, command):

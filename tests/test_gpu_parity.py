@@ -298,6 +298,18 @@ def test_accept_malformed_parents():
     assert int(err.item()) == binding.DERR_BAD_PARENT
 
 
+def test_accept_many_short_sequences():
+    # many short sequences: one walk workgroup each
+    _say("[accept] 1100 sequences")
+    bsz, n, v = 1100, 3, 96
+    parents, draft, logits = W.make_sampling_case(77, batch=bsz, n_nodes=n, vocab=v, dtype="f32")
+    got = binding.greedy_accept(torch.from_numpy(logits).cuda(), dev_i32(parents), dev_i32(draft))
+    torch.cuda.synchronize()
+    ref = oracle.greedy_accept(logits, parents, draft)
+    for k, (x, y) in enumerate(zip(got, ref)):
+        assert np.array_equal(x.cpu().numpy(), y), f"output {k}"
+
+
 def test_accept_workspace_reused_across_calls():
     """One workspace and one set of output buffers serve consecutive calls
     with different inputs: nothing from a previous call leaks into the next

@@ -111,11 +111,20 @@ void attn_wide_kernel(AttnArgs a) {
     const char* vt = reinterpret_cast<const char*>(a.v_tree + ((int64_t)b * a.n * a.hkv + g) * D);
     const int64_t tree_rowb = (int64_t)a.hkv * ROWB;
 
-    // ---- DMA: instruction k of this wave fills 1 KB column block cb of the K
-    // or V tile; lane i carries token i/2, 16-byte half i&1 (as the 16-row kernel).
+    // ---- DMA: instruction k of this wave fills 1 KB column block cb (16
+    // columns) of the K or V tile.  The block holds the columns' two 16-byte
+    // halves apart: half h of token t at 512 h + 16 (t ^ 4h ^ 8(cb&1)).  The
+    // 16-byte K reads of a wave (token l%32, half l/32) then cover each
+    // 512-byte half once, and the transposing V reads of the four 16-lane
+    // groups (4 tokens x 16 columns each, two groups per block of a pair)
+    // fall on disjoint banks: conflict-free both.  DMA lane i writes 16-byte
+    // slot i, so it carries half i/32 of token (i%32) ^ 4(i/32) ^ 8(cb&1);
+    // a wave's instructions alternate the block parity (DPW is even).
     const uint32_t ring_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)ring;
-    const int dtok = lane >> 1;
-    const int dhalf = lane & 1;
+    const int dhalf = lane >> 5;
+    const int dtok_e = (lane & 31) ^ (4 * dhalf);  // even column blocks
+    const int dtok_o = dtok_e ^ 8;                   // odd column blocks
+    static_assert(DPW % 2 == 0, "block parity of instruction k is k & 1");
     bool dvt[DPW];
     uint32_t ddst[DPW], dcol[DPW];
   #pragma unroll
@@ -130,7 +139,8 @@ void attn_wide_kernel(AttnArgs a) {
     // full-mode tiles use one scalar base per wave and one lane offset, the
     // instructions 32 bytes apart in the row and 1 KB apart in LDS.
     const char* fbase = (wave * DPW >= KC ? vc : kc) + (int64_t)begin * ROWB;
-    const uint32_t fvoff0 = dtok * ROWB + dcol[0];
+    const uint32_t fvoff_e = dtok_e * ROWB + dcol[0];
+    const uint32_t fvoff_o = dtok_o * ROWB + dcol[0];
     const uint32_t fdst0 = __builtin_amdgcn_readfirstlane(ring_base + ddst[0]);
     static_assert(KC % DPW == 0, "a wave's DMA instructions stay within one tensor");
 
@@ -143,10 +153,12 @@ void attn_wide_kernel(AttnArgs a) {
       if (tree_own) {
         spec = min(kWAhead, (a.n + kTile - 1) / kTile);
         for (int t = 0; t < spec; ++t) {
-          const int64_t off = (int64_t)min(t * kTile + dtok, a.n - 1) * tree_rowb;
+          const int64_t off_e = (int64_t)min(t * kTile + dtok_e, a.n - 1) * tree_rowb;
+          const int64_t off_o = (int64_t)min(t * kTile + dtok_o, a.n - 1) * tree_rowb;
   #pragma unroll
           for (int k = 0; k < DPW; ++k)
-            dma16(__builtin_amdgcn_readfirstlane(ring_base + t * SLOT_B + ddst[k]), (dvt[k] ? vt : kt) + off + dcol[k]);
+            dma16(__builtin_amdgcn_readfirstlane(ring_base + t * SLOT_B + ddst[k]),
+                  (dvt[k] ? vt : kt) + ((k & 1) ? off_o : off_e) + dcol[k]);
         }
       } else {
         const int lim = min(begin + a.chunk, a.max_prefix);
@@ -154,7 +166,8 @@ void attn_wide_kernel(AttnArgs a) {
         for (int t = 0; t < spec; ++t) {
   #pragma unroll
           for (int k = 0; k < DPW; ++k)
-            dma16s(fdst0 + t * SLOT_B + 1024 * k, fbase + (int64_t)t * (kTile * ROWB), fvoff0 + 32 * k);
+            dma16s(fdst0 + t * SLOT_B + 1024 * k, fbase + (int64_t)t * (kTile * ROWB),
+                   ((k & 1) ? fvoff_o : fvoff_e) + 32 * k);
         }
       }
     }
@@ -319,7 +332,8 @@ void attn_wide_kernel(AttnArgs a) {
     auto dma_whole = [&](int slot, int it) {
   #pragma unroll
       for (int k = 0; k < DPW; ++k)
-        dma16s(fdst0 + slot * SLOT_B + 1024 * k, fbase + (int64_t)it * (kTile * ROWB), fvoff0 + 32 * k);
+        dma16s(fdst0 + slot * SLOT_B + 1024 * k, fbase + (int64_t)it * (kTile * ROWB),
+               ((k & 1) ? fvoff_o : fvoff_e) + 32 * k);
     };
     auto dma_tile = [&](int slot, int it) {
       if (it < nfull) {
@@ -328,20 +342,23 @@ void attn_wide_kernel(AttnArgs a) {
       }
       const char* kb;
       const char* vb;
-      int64_t off;
+      int64_t off_e, off_o;
       if (it < np) {
         bool valid;
-        off = (int64_t)slot_row(begin + it * kTile + dtok, valid) * ROWB;
+        off_e = (int64_t)slot_row(begin + it * kTile + dtok_e, valid) * ROWB;
+        off_o = (int64_t)slot_row(begin + it * kTile + dtok_o, valid) * ROWB;
         kb = kc;
         vb = vc;
       } else {
-        off = (int64_t)min((it - np) * kTile + dtok, a.n - 1) * tree_rowb;
+        off_e = (int64_t)min((it - np) * kTile + dtok_e, a.n - 1) * tree_rowb;
+        off_o = (int64_t)min((it - np) * kTile + dtok_o, a.n - 1) * tree_rowb;
         kb = kt;
         vb = vt;
       }
   #pragma unroll
       for (int k = 0; k < DPW; ++k)
-        dma16(__builtin_amdgcn_readfirstlane(ring_base + slot * SLOT_B + ddst[k]), (dvt[k] ? vb : kb) + off + dcol[k]);
+        dma16(__builtin_amdgcn_readfirstlane(ring_base + slot * SLOT_B + ddst[k]),
+              (dvt[k] ? vb : kb) + ((k & 1) ? off_o : off_e) + dcol[k]);
     };
     auto tile_bits = [&](int it) -> uint32_t {
       int cnt;
@@ -359,24 +376,34 @@ void attn_wide_kernel(AttnArgs a) {
 
     // ---- LDS operand addressing ------------------------------------------------
     // K fragment kc (A operand, token col, columns 16kc + 8half..+7): column
-    // block kc, a contiguous 1 KB over the wave.
-    const uint32_t koff = 32u * col + 16u * half;
+    // block kc, each half a contiguous 512 bytes over its 32 lanes.
+    const uint32_t koff_e = 512u * half + 16u * (col ^ (4 * half));
+    const uint32_t koff_o = 512u * half + 16u * (col ^ (4 * half) ^ 8);
     // V^T fragment (dt, kt): in 16-lane group q the transposing read returns
     // column 16(q&1) + j of tokens T0..T0+3 to lane j when lane j addresses
-    // token T0 + j/4, bytes 8(j&3) of column block 2dt + (q&1).  T0 = 16kt +
-    // 4(q>>1) for k-slots 0-3, and 8 tokens later for k-slots 4-7: the tokens
-    // of registers 8kt..8kt+7 of the S^T accumulator of lane half q>>1.
+    // token T0 + j/4, columns 4(j&3)..+3 (half (j&3)/2, bytes 8(j&1)) of
+    // column block 2dt + (q&1).  T0 = 16kt + 4(q>>1) for k-slots 0-3, and 8
+    // tokens later for k-slots 4-7: the tokens of registers 8kt..8kt+7 of
+    // the S^T accumulator of lane half q>>1.  The token XORs flip bits 2
+    // and 3 of a token below 8, so the 16kt step stays a plain offset (256
+    // kt) while the 8-token step (bit 3) is +128 bytes in even blocks and
+    // -128 in odd ones: voff_hi.
     const int q16 = lane >> 4, j16 = lane & 15;
-    const uint32_t voff = TILE_B + 1024u * (q16 & 1) + 32u * (4 * (q16 >> 1) + (j16 >> 2)) + 8u * (j16 & 3);
+    const int vh = (j16 & 3) >> 1;
+    const uint32_t voff = TILE_B + 1024u * (q16 & 1) + 512u * vh +
+                          16u * ((4 * (q16 >> 1) + (j16 >> 2)) ^ (4 * vh) ^ (8 * (q16 & 1))) +
+                          8u * (j16 & 1);
+    const uint32_t voff_hi = voff + ((q16 & 1) ? -128u : 128u);
     typedef __attribute__((address_space(3))) char lds_char;
     auto lds_at = [&](uint32_t addr) { return (lds_char*)(uintptr_t)addr; };
     auto kfrag = [&](uint32_t sa, int kc2) -> bf16x8 {
-      return *(__attribute__((address_space(3))) const bf16x8*)lds_at(sa + koff + 1024 * kc2);
+      return *(__attribute__((address_space(3))) const bf16x8*)lds_at(sa + ((kc2 & 1) ? koff_o : koff_e) + 1024 * kc2);
     };
     auto vfrag = [&](uint32_t sa, int dt, int ktk) -> bf16x8 {
-      const uint32_t ad = sa + voff + 2048 * dt + 512 * ktk;
+      const uint32_t ad = sa + voff + 2048 * dt + 256 * ktk;
+      const uint32_t ad2 = sa + voff_hi + 2048 * dt + 256 * ktk;
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)lds_at(ad));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)lds_at(ad + 256));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)lds_at(ad2));
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 
@@ -433,21 +460,24 @@ void attn_wide_kernel(AttnArgs a) {
     // Operand reads of a tile (K, or V^T): the loop reads the next tile's
     // operands while the current tile's MFMAs run.
     auto read_k = [&](int it, bf16x8 (&kf)[KC]) {
-      const uint32_t kaddr = koff + (ring_base + (it & (kWRing - 1)) * SLOT_B);
+      const uint32_t kbase = ring_base + (it & (kWRing - 1)) * SLOT_B;
+      const uint32_t kaddr_e = koff_e + kbase, kaddr_o = koff_o + kbase;
   #pragma unroll
       for (int kc2 = 0; kc2 < KC; ++kc2) {
-        kf[kc2] = *(__attribute__((address_space(3))) const bf16x8*)lds_at(kaddr + 1024 * kc2);
+        kf[kc2] = *(__attribute__((address_space(3))) const bf16x8*)lds_at(((kc2 & 1) ? kaddr_o : kaddr_e) + 1024 * kc2);
       }
     };
     auto read_v = [&](int it, bf16x8 (&vf)[DT][2]) {
-      const uint32_t vaddr = voff + (ring_base + (it & (kWRing - 1)) * SLOT_B);
+      const uint32_t vbase = ring_base + (it & (kWRing - 1)) * SLOT_B;
+      const uint32_t vaddr = voff + vbase, vaddr2 = voff_hi + vbase;
   #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
   #pragma unroll
         for (int ktk = 0; ktk < 2; ++ktk) {
-          const uint32_t ad = vaddr + 2048 * dt + 512 * ktk;
+          const uint32_t ad = vaddr + 2048 * dt + 256 * ktk;
+          const uint32_t ad2 = vaddr2 + 2048 * dt + 256 * ktk;
           const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)lds_at(ad));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)lds_at(ad + 256));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)lds_at(ad2));
           vf[dt][ktk] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
     };
@@ -530,8 +560,10 @@ void attn_wide_kernel(AttnArgs a) {
           issued = t + kWAhead;
         }
         if (!FAST && !active) return;
-        const uint32_t kaddr = koff + (ring_base + ((t + 2) & (kWRing - 1)) * SLOT_B);
-        const uint32_t vaddr = voff + (ring_base + (t & (kWRing - 1)) * SLOT_B);
+        const uint32_t kbase = ring_base + ((t + 2) & (kWRing - 1)) * SLOT_B;
+        const uint32_t kaddr_e = koff_e + kbase, kaddr_o = koff_o + kbase;
+        const uint32_t vbase = ring_base + (t & (kWRing - 1)) * SLOT_B;
+        const uint32_t vaddr = voff + vbase, vaddr2 = voff_hi + vbase;
         TV_SCHED_FENCE;
         softmax(cur[0], 0, pcur[0]);
   #pragma unroll
@@ -539,7 +571,7 @@ void attn_wide_kernel(AttnArgs a) {
   #pragma unroll
           for (int rt = 0; rt < RT; ++rt)
             nxt[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kc2], qf[rt][kc2], kc2 == 0 ? f32x16{} : nxt[rt], 0, 0, 0);
-          kf[kc2] = *(__attribute__((address_space(3))) const bf16x8*)lds_at(kaddr + 1024 * kc2);
+          kf[kc2] = *(__attribute__((address_space(3))) const bf16x8*)lds_at(((kc2 & 1) ? kaddr_o : kaddr_e) + 1024 * kc2);
         }
   #pragma unroll
         for (int i = 0; i < KC * RT; ++i) {
@@ -557,9 +589,10 @@ void attn_wide_kernel(AttnArgs a) {
   #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
               o[dt][rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt][ktk], pprev[rt][ktk], o[dt][rt], 0, 0, 0);
-            const uint32_t ad = vaddr + 2048 * dt + 512 * ktk;
+            const uint32_t ad = vaddr + 2048 * dt + 256 * ktk;
+            const uint32_t ad2 = vaddr2 + 2048 * dt + 256 * ktk;
             const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)lds_at(ad));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)lds_at(ad + 256));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)lds_at(ad2));
             vf[dt][ktk] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           }
   #pragma unroll
