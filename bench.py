@@ -53,7 +53,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, vendor figure
 STREAM_BYTES = 2 << 30          # buffer of the measured stream-read peak
 MALL_BYTES = 256 * 1024 * 1024  # Infinity Cache
 COPY_BYTES = 256 * 1024 * 1024  # calibration copy size
-ATTN_SOURCE = os.path.join(ROOT, "tree_verification_attention_tv_amd", "csrc", "tv_attention.hip")
+ATTN_SOURCES = [os.path.join(ROOT, "tree_verification_attention_tv_amd", "csrc", f)
+                for f in ("tv_attention.hip", "tv_attn_wide.hip", "tv_attn_common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_8b_layer_hbm_traffic.txt")
 ATTN_KERNELS = ("attn_split_kernel", "attn_combine_kernel")
 
@@ -94,8 +95,13 @@ def parse():
 
 
 def source_hash() -> str:
-    with open(ATTN_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the attention kernels' sources (both schedules and their
+    shared header): a counter summary is current only for the same hash."""
+    h = hashlib.sha256()
+    for path in ATTN_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 # ---------------------------------------------------------------------------
@@ -950,6 +956,8 @@ def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, workload="
     tot_w = sum(write.get(k, 0.0) for k in ATTN_KERNELS)
     hbm = int(round(tot_f * f_scale + tot_w * w_scale))
     what = {"8b_layer": "8B-layer workload (bench.py default",
+            "specblock_tree": "SpecBlock-tree workload, 96 nodes (bench.py --workload specblock_tree",
+            "batched": "16-sequence batch (bench.py --workload batched",
             "long_context": "60K-prefix workload, full KV (bench.py --workload long_context"}
     lines = [
         f"HBM traffic of one tv_tree_attention call, {what.get(workload, workload + ' (')},",
@@ -981,21 +989,28 @@ def counter_summary(dirs, match="attn_", cus=256, simds_per_cu=4, shader_engines
     the dispatch's length in cycles); SQ_BUSY_CU_CYCLES is cycles summed
     over CUs; SQ_ACTIVE_INST_*, SQ_WAIT_INST_ANY and SQ_WAVE_CYCLES are
     quad-cycles summed over waves."""
+    # per (pass, kernel, counter): the dispatch sums, averaged; a counter
+    # read in several passes is averaged over them
     per = {}
     for d in dirs:
+        one = {}
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             with open(f) as fh:
                 for row in csv.DictReader(fh):
                     if match not in row["Kernel_Name"]:
                         continue
                     k = short_name(row["Kernel_Name"], keep_template=True)
-                    c = per.setdefault(k, {}).setdefault(row["Counter_Name"], {})
+                    c = one.setdefault(k, {}).setdefault(row["Counter_Name"], {})
                     c[row["Dispatch_Id"]] = c.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+        for k, cs in one.items():
+            for n, v in cs.items():
+                if v:
+                    per.setdefault(k, {}).setdefault(n, []).append(sum(v.values()) / len(v))
     print(f"source_sha256_16: {source_hash()}")
     print("counter averages per dispatch; ratios below each kernel")
     simds = cus * simds_per_cu
     for k, cs in sorted(per.items()):
-        avg = {n: sum(v.values()) / len(v) for n, v in cs.items() if v}
+        avg = {n: sum(v) / len(v) for n, v in cs.items()}
         print(f"\n{k}")
         for n in sorted(avg):
             print(f"  {n:32s} {avg[n]:16.1f}")

@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
     // that the combine reads every split without the prefix length
     for (int mb = 0; mb < RB; ++mb) {
       const int m = row0 + 16 * mb + col;
-      if (active && m < a.rows && grp4 == 0) store_ml<true>(a.part_ml + prow0 + m, make_float2(-INFINITY, 0.f));
+      if (active && m < a.rows && grp4 == 0) store_part_ml(a, a.part_ml + prow0 + m, make_float2(-INFINITY, 0.f));
     }
     goto done;
   }
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
         if (err) raise_err(a.dev_err, err);
         for (int mb = 0; mb < RB; ++mb) {
           const int m = row0 + 16 * mb + col;
-          if (active && m < a.rows && grp4 == 0) store_ml<true>(a.part_ml + prow0 + m, make_float2(-INFINITY, 0.f));
+          if (active && m < a.rows && grp4 == 0) store_part_ml(a, a.part_ml + prow0 + m, make_float2(-INFINITY, 0.f));
         }
         goto done;
       }
@@ -733,7 +733,7 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
         *(__attribute__((address_space(3))) bf16x4*)lds_at(
             stage + r * (2 * D) + 32 * (db ^ ((r / RPB) & (DB - 1))) + 8 * grp4) = v;
       }
-      if (grp4 == 0 && row0 + r < a.rows) store_ml<true>(a.part_ml + prow0 + row0 + r, make_float2(mref[mb], l));
+      if (grp4 == 0 && row0 + r < a.rows) store_part_ml(a, a.part_ml + prow0 + row0 + r, make_float2(mref[mb], l));
     }
 #pragma unroll
     for (int j = 0; j < 16 * RB / RPI; ++j) {
@@ -741,7 +741,7 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
       const int q = lane % QPR;
       const bf16x8 v = *(__attribute__((address_space(3))) const bf16x8*)lds_at(
           stage + r * (2 * D) + 32 * ((q >> 1) ^ ((r / RPB) & (DB - 1))) + 16 * (q & 1));
-      if (row0 + r < a.rows) store_o<true>(a.part_o + (prow0 + row0 + r) * D + 8 * q, v);
+      if (row0 + r < a.rows) store_part_o(a, a.part_o + (prow0 + row0 + r) * D + 8 * q, v);
     }
   }
   }

@@ -184,6 +184,19 @@ __device__ __forceinline__ bf16x8 load_o(const bf16* p) {
   }
 }
 
+// Partial stores of the split work: device-coherent when the merge runs in
+// the same launch (sync set), plain otherwise -- coherent stores also write
+// through to memory, which doubles the partials' HBM write traffic
+// (measured with WRITE_SIZE).
+__device__ __forceinline__ void store_part_ml(const AttnArgs& a, float2* p, float2 v) {
+  if (a.sync) store_ml<true>(p, v);
+  else store_ml<false>(p, v);
+}
+__device__ __forceinline__ void store_part_o(const AttnArgs& a, bf16* p, bf16x8 v) {
+  if (a.sync) store_o<true>(p, v);
+  else store_o<false>(p, v);
+}
+
 // Merge the split partials of NR (sequence, node, head) rows -- rowid =
 // (b * n + i) * hq + h, negative for none -- by the wave of `lane`: with
 // weights w_s = 2^(m_s - m) l_s, m = max m_s, the output is

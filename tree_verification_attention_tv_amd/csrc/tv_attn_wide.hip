@@ -236,7 +236,7 @@ void attn_wide_kernel(AttnArgs a) {
   #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const int m = row0 + 32 * rt + col;
-        if (active && m < a.rows && half == 0) store_ml<true>(a.part_ml + prow0 + m, make_float2(-INFINITY, 0.f));
+        if (active && m < a.rows && half == 0) store_part_ml(a, a.part_ml + prow0 + m, make_float2(-INFINITY, 0.f));
       }
     };
     if (np == 0 && nt == 0) {
@@ -722,14 +722,14 @@ void attn_wide_kernel(AttnArgs a) {
             const int c = 4 * dt + q;
             *(__attribute__((address_space(3))) bf16x4*)lds_at(stage + r * ROWB + 16 * (c ^ (r & (CH - 1))) + 8 * half) = v;
           }
-        if (half == 0 && row0 + r < a.rows) store_ml<true>(a.part_ml + prow0 + row0 + r, make_float2(mref[rt], l));
+        if (half == 0 && row0 + r < a.rows) store_part_ml(a, a.part_ml + prow0 + row0 + r, make_float2(mref[rt], l));
       }
   #pragma unroll
       for (int j = 0; j < WROWS / RPI; ++j) {
         const int r = j * RPI + lane / CH;
         const int p = lane % CH;
         const bf16x8 v = *(__attribute__((address_space(3))) const bf16x8*)lds_at(stage + r * ROWB + 16 * p);
-        if (row0 + r < a.rows) store_o<true>(a.part_o + (prow0 + row0 + r) * D + 8 * (p ^ (r & (CH - 1))), v);
+        if (row0 + r < a.rows) store_part_o(a, a.part_o + (prow0 + row0 + r) * D + 8 * (p ^ (r & (CH - 1))), v);
       }
     }
 
