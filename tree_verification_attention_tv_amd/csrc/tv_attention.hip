@@ -186,13 +186,15 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
 #pragma unroll
   for (int mb = 0; mb < RB; ++mb) {
     const int m = row0 + 16 * mb + col;
+    // a row past the last (m >= rows) reads row 0 of the group: finite
+    // values whose results are never stored
     const bool real = m < a.rows;
     const int i = real ? m / a.grp : 0;
     const int h = g * a.grp + (real ? m - i * a.grp : 0);
     const bf16* qrow = a.q + (((int64_t)b * a.n + i) * a.hq + h) * D + 8 * grp4;
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
-      qf[mb][dc] = real ? *reinterpret_cast<const bf16x8*>(qrow + 32 * dc) : bf16x8{};
+      qf[mb][dc] = *reinterpret_cast<const bf16x8*>(qrow + 32 * dc);
   }
   constexpr int kMaskPer = TV_MAX_NODES * (TV_MAX_NODES / 32) / kSplitThreads;  // words per thread
   const int node1 = min(a.n, (wg_row0 + 16 * kWaves * RB + a.grp - 1) / a.grp);

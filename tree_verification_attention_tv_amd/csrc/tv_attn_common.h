@@ -48,8 +48,17 @@ struct AttnArgs {
 };
 
 // Verified-prefix length of sequence b, clamped to what the grid covers.
+// A workgroup-uniform int32 read through the scalar cache (constant address
+// space): its wait is on lgkmcnt, so it never drains the tile requests in
+// flight, which the vector-memory counter also counts.  The arrays read
+// this way (prefix lengths, list lengths) are not written by the kernel.
+__device__ __forceinline__ int load_uniform(const int32_t* p) {
+  return *reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+      reinterpret_cast<uintptr_t>(p));
+}
+
 __device__ __forceinline__ int clamped_prefix(const AttnArgs& a, int b, int* err) {
-  int p = a.prefix_len[b];
+  int p = load_uniform(a.prefix_len + b);
   const int lim = a.max_blocks ? a.cap : min(a.cap, a.max_prefix);
   if (p < 0 || p > lim) {
     *err |= TV_DERR_BAD_PREFIX;
@@ -62,7 +71,7 @@ __device__ __forceinline__ int clamped_prefix(const AttnArgs& a, int b, int* err
 // blocks times block size in partial mode.
 __device__ __forceinline__ int prefix_slots(const AttnArgs& a, int b, int p, int* err) {
   if (a.max_blocks == 0) return p;
-  int nb = a.n_blocks[b];
+  int nb = load_uniform(a.n_blocks + b);
   if (nb < 0 || nb > a.max_blocks) {
     *err |= TV_DERR_BAD_BLOCK;
     nb = nb < 0 ? 0 : a.max_blocks;

@@ -36,6 +36,14 @@ constexpr int kWWaves = 4;
 constexpr int kWThreads = kWWaves * 64;
 constexpr int kWRing = 8;   // LDS ring slots, a power of two
 constexpr int kWAhead = 7;  // tiles requested ahead of the one in use (< kWRing)
+// Tiles requested before the first step; the others follow two per step
+// over the first kWAhead - kWFirst steps.  All workgroups start at once and
+// a wave cannot issue past a tile request the memory system has not yet
+// accepted, so requesting the whole ring first stalls the waves for several
+// microseconds (about 7 at the 60000-token prefix) -- but requesting 3
+// first and catching up over 4 steps measured slower still (the catch-up
+// steps stalled longer), so the whole ring goes first.
+constexpr int kWFirst = kWAhead;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -69,6 +77,8 @@ void attn_wide_kernel(AttnArgs a) {
   constexpr int GROWS = kWWaves * WROWS;
   static_assert(DPW >= 1 && DPW * kWWaves == NDMA, "DMA split across waves");
   static_assert(kWAhead >= 3 && kWAhead < kWRing, "prefetch distance within the ring");
+  static_assert(kWFirst >= 3 && kWFirst <= kWAhead && (kWAhead - kWFirst) % 2 == 0,
+                "the first steps need tiles 0-2; the catch-up takes an even number of steps");
 
   __shared__ __attribute__((aligned(1024))) char ring[kWRing * SLOT_B];
   __shared__ uint32_t smask[TV_MAX_NODES * (TV_MAX_NODES / 32)];
@@ -144,47 +154,25 @@ void attn_wide_kernel(AttnArgs a) {
     const uint32_t fdst0 = __builtin_amdgcn_readfirstlane(ring_base + ddst[0]);
     static_assert(KC % DPW == 0, "a wave's DMA instructions stay within one tensor");
 
-    // ---- first tiles before the prefix length is known (full mode): whole
-    // tiles below the declared maximum prefix, or the tree of a tree-only
-    // workgroup.  Their rows do not depend on the prefix length.
-    const bool tree_own = a.tree_sep && s == a.splits;
-    int spec = 0;
-    if (!PARTIAL) {
-      if (tree_own) {
-        spec = min(kWAhead, (a.n + kTile - 1) / kTile);
-        for (int t = 0; t < spec; ++t) {
-          const int64_t off_e = (int64_t)min(t * kTile + dtok_e, a.n - 1) * tree_rowb;
-          const int64_t off_o = (int64_t)min(t * kTile + dtok_o, a.n - 1) * tree_rowb;
-  #pragma unroll
-          for (int k = 0; k < DPW; ++k)
-            dma16(__builtin_amdgcn_readfirstlane(ring_base + t * SLOT_B + ddst[k]),
-                  (dvt[k] ? vt : kt) + ((k & 1) ? off_o : off_e) + dcol[k]);
-        }
-      } else {
-        const int lim = min(begin + a.chunk, a.max_prefix);
-        spec = begin < lim ? min(kWAhead, (lim - begin) / kTile) : 0;
-        for (int t = 0; t < spec; ++t) {
-  #pragma unroll
-          for (int k = 0; k < DPW; ++k)
-            dma16s(fdst0 + t * SLOT_B + 1024 * k, fbase + (int64_t)t * (kTile * ROWB),
-                   ((k & 1) ? fvoff_o : fvoff_e) + 32 * k);
-        }
-      }
-    }
-
     // ---- Q^T fragments (B operand of S^T = K Q^T): lane (half, col) of row
     // tile rt holds row row0 + 32 rt + col, columns 16 kc + 8 half .. +7.
     bf16x8 qf[RT][KC];
   #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int m = row0 + 32 * rt + col;
+      // a row past the last (m >= rows) reads row 0 of the group: finite
+      // values whose results are never stored
       const bool real = m < a.rows;
       const int i = real ? m / a.grp : 0;
       const int h = g * a.grp + (real ? m - i * a.grp : 0);
       const bf16* qrow = a.q + (((int64_t)b * a.n + i) * a.hq + h) * D + 8 * half;
   #pragma unroll
       for (int kc2 = 0; kc2 < KC; ++kc2)
-        qf[rt][kc2] = real ? *reinterpret_cast<const bf16x8*>(qrow + 16 * kc2) : bf16x8{};
+        // straight into accumulation registers, outside the compiler's wait
+        // tracking: the tile requests below are inline assembly it does not
+        // count, so its own wait for these loads would drain them too.  The
+        // waits before the first use are explicit (pin_q).
+        asm volatile("global_load_dwordx4 %0, %1, off" : "=a"(qf[rt][kc2]) : "v"(qrow + 16 * kc2) : "memory");
     }
     constexpr int kMaskPer = TV_MAX_NODES * (TV_MAX_NODES / 32) / kWThreads;
     const int node1 = min(a.n, (wg_row0 + GROWS + a.grp - 1) / a.grp);
@@ -214,16 +202,65 @@ void attn_wide_kernel(AttnArgs a) {
       }
     }
 
+    __builtin_amdgcn_sched_barrier(0);  // the loads above stay ahead of the tile requests
+    // ---- first tiles before the prefix length is known (full mode): whole
+    // tiles below the declared maximum prefix, or the tree of a tree-only
+    // workgroup.  Their rows do not depend on the prefix length.  They are
+    // requested after the loads above, and the wait below is for those loads
+    // only when all kWFirst tiles went out in straight-line code (the usual
+    // case): the first step then waits for its own tiles, not the whole ring.
+    // Q^T stays in the accumulation registers (MFMA reads its A/B operands
+    // from either file; the VGPRs hold the score tiles); pin_q, after the
+    // explicit wait of each branch, orders every use after that wait.
+    const bool tree_own = a.tree_sep && s == a.splits;
+    int spec = 0;
+    int spec_landed = 0;  // first tiles known to have landed
+    auto pin_q = [&]() {
+  #pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+  #pragma unroll
+        for (int kc2 = 0; kc2 < KC; ++kc2) asm volatile("" : "+a"(qf[rt][kc2]));
+    };
+    const int lim = min(begin + a.chunk, a.max_prefix);
+    if (!PARTIAL && !tree_own && begin < lim && (lim - begin) / kTile >= kWFirst) {
+      spec = kWFirst;
+  #pragma unroll
+      for (int t = 0; t < kWFirst; ++t)
+  #pragma unroll
+        for (int k = 0; k < DPW; ++k)
+          dma16s(fdst0 + t * SLOT_B + 1024 * k, fbase + (int64_t)t * (kTile * ROWB),
+                 ((k & 1) ? fvoff_o : fvoff_e) + 32 * k);
+      vm_wait<kWFirst * DPW>();  // the loads above, not the tiles
+      pin_q();
+    } else {
+      if (!PARTIAL) {
+        if (tree_own) {
+          spec = min(kWFirst, (a.n + kTile - 1) / kTile);
+          for (int t = 0; t < spec; ++t) {
+            const int64_t off_e = (int64_t)min(t * kTile + dtok_e, a.n - 1) * tree_rowb;
+            const int64_t off_o = (int64_t)min(t * kTile + dtok_o, a.n - 1) * tree_rowb;
+  #pragma unroll
+            for (int k = 0; k < DPW; ++k)
+              dma16(__builtin_amdgcn_readfirstlane(ring_base + t * SLOT_B + ddst[k]),
+                    (dvt[k] ? vt : kt) + ((k & 1) ? off_o : off_e) + dcol[k]);
+          }
+        } else {
+          spec = begin < lim ? min(kWFirst, (lim - begin) / kTile) : 0;
+          for (int t = 0; t < spec; ++t) {
+  #pragma unroll
+            for (int k = 0; k < DPW; ++k)
+              dma16s(fdst0 + t * SLOT_B + 1024 * k, fbase + (int64_t)t * (kTile * ROWB),
+                     ((k & 1) ? fvoff_o : fvoff_e) + 32 * k);
+          }
+        }
+      }
+      vm_wait<0>();  // the loads above and the first tiles
+      pin_q();
+      spec_landed = spec;
+    }
     int err = 0;
     const int p_len = clamped_prefix(a, b, &err);
     const int slots = prefix_slots(a, b, p_len, &err);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the loads above and the first tiles
-    // Q^T stays in accumulation registers (MFMA reads its A/B operands from
-    // either file); the VGPRs hold the score tiles the softmax works on.
-  #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-  #pragma unroll
-      for (int kc2 = 0; kc2 < KC; ++kc2) asm volatile("" : "+a"(qf[rt][kc2]));
     if (err && s == 0 && unit == 0 && tid == 0) raise_err(a.dev_err, err);
     err = 0;
     const int ns = (slots + a.chunk - 1) / a.chunk;
@@ -241,6 +278,7 @@ void attn_wide_kernel(AttnArgs a) {
     };
     if (np == 0 && nt == 0) {
       write_empty();
+      vm_wait<0>();  // no first-tile request outlives the workgroup's LDS
       return;
     }
 
@@ -302,6 +340,7 @@ void attn_wide_kernel(AttnArgs a) {
         if (!has_tree) {
           if (err) raise_err(a.dev_err, err);
           write_empty();
+          vm_wait<0>();  // no first-tile request outlives the workgroup's LDS
           return;
         }
         np = 0;
@@ -313,6 +352,12 @@ void attn_wide_kernel(AttnArgs a) {
     const int nfull = PARTIAL ? 0 : (end - begin) / kTile;
     // requested tiles that are this split's own first tiles
     const int skip = tree_own ? spec : max(0, min(spec, nfull));
+    // first tiles that are not this split's own are requested again into
+    // the same slots: the speculative requests must have landed before.
+    // Of the first tiles, those below skip count as landed only when waited
+    // for; the ones requested again have not.
+    if (skip < spec && spec_landed < spec) vm_wait<0>();
+    spec_landed = spec_landed > 0 || skip < spec ? skip : 0;
     auto slot_row = [&](int u, bool& valid) -> int {
       if (u >= end) {
         valid = false;
@@ -492,20 +537,22 @@ void attn_wide_kernel(AttnArgs a) {
     // tile (listed blocks may be invalid or past the prefix), the tree tiles
     auto needs_mask = [&](int it) { return PARTIAL || it >= nfull; };
 
-    auto run = [&](int skip_tiles, bool track) {
+    // run(skip_tiles, landed_tiles, track): tiles below skip_tiles were
+    // requested already, those below landed_tiles have landed
+    auto run = [&](int skip_tiles, int landed_tiles, bool track) {
   #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         lsum[rt] = 0.f;
   #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[dt][rt] = f32x16{};
       }
-      // tiles skip_tiles .. kWAhead-1 (those that exist) into their slots
-      for (int t = skip_tiles; t < min(kWAhead, ntiles); ++t) dma_tile(t & (kWRing - 1), t);
-      int issued = min(kWAhead, ntiles) - 1;  // last requested tile
-      // wait until tile x has landed (tiles below skip_tiles landed before);
-      // in the steady state kWAhead - 3 later tiles are in flight
+      // tiles skip_tiles .. kWFirst-1 (those that exist) into their slots
+      for (int t = skip_tiles; t < min(kWFirst, ntiles); ++t) dma_tile(t & (kWRing - 1), t);
+      int issued = min(kWFirst, ntiles) - 1;  // last requested tile
+      // wait until tile x has landed (tiles below landed_tiles landed
+      // before); in the steady state kWAhead - 3 later tiles are in flight
       auto wait_tile = [&](int x) {
-        if (x < skip_tiles) return;
+        if (x < landed_tiles) return;
         const int c = issued - x;
         if (c >= kWAhead - 3) vm_wait<(kWAhead - 3) * DPW>();
         else vm_wait_tiles<DPW>(c);
@@ -555,9 +602,19 @@ void attn_wide_kernel(AttnArgs a) {
         lds_barrier();
         if (FAST) {
           dma_whole((t + kWAhead) & (kWRing - 1), t + kWAhead);
-        } else if (t + kWAhead < ntiles) {
-          dma_tile((t + kWAhead) & (kWRing - 1), t + kWAhead);
-          issued = t + kWAhead;
+        } else {
+          // up to tile t + kWAhead, at most two per step (the first steps
+          // catch up with the tiles not requested before the first step);
+          // tile x goes to the slot of tile x - kWRing <= t - 1, free now
+          const int want = min(t + kWAhead, ntiles - 1);
+          if (issued < want) {
+            ++issued;
+            dma_tile(issued & (kWRing - 1), issued);
+          }
+          if (issued < want) {
+            ++issued;
+            dma_tile(issued & (kWRing - 1), issued);
+          }
         }
         if (!FAST && !active) return;
         const uint32_t kbase = ring_base + ((t + 2) & (kWRing - 1)) * SLOT_B;
@@ -604,26 +661,36 @@ void attn_wide_kernel(AttnArgs a) {
         TV_SCHED_FENCE;
         if (!FAST && t + 1 < ntiles && needs_mask(t + 1)) mask_tile(t + 1, nxt);
       };
-      // Steady steps t < nfast: every wave is active, tiles t+1 and t+2
-      // exist, tile t+1 needs no mask and tile t + kWAhead is a whole tile.
-      // An even count keeps the roles of the two score and P buffers.
+      // Steps go in pairs, which keeps the roles of the two score and P
+      // buffers.  The first kWAhead - kWFirst steps catch up with the tile
+      // requests (general steps); then steady steps t < nfast: every wave is
+      // active, tiles t+1 and t+2 exist, tile t+1 needs no mask and tile
+      // t + kWAhead is a whole tile, requested with no branch.
+      constexpr int kRamp = kWAhead - kWFirst;
       int nfast = active_all ? min(nfull - kWAhead, min(ntiles - 2, nfull - 1)) : 0;
-      nfast = nfast > 0 ? (nfast & ~1) : 0;
+      nfast = nfast > kRamp ? (nfast & ~1) : 0;
       int t = 0;
-      for (; t < nfast; t += 2) {
-        step(std::true_type{}, t, sA, sB, pA, pB);
-        step(std::true_type{}, t + 1, sB, sA, pB, pA);
-      }
-      if (nfast > 0) issued = nfast - 1 + kWAhead;
       bool last_in_b = true;  // which P buffer holds the last tile's weights
-      for (; t < ntiles; t += 2) {
-        step(std::false_type{}, t, sA, sB, pA, pB);
-        last_in_b = false;
-        if (t + 1 < ntiles) {
-          step(std::false_type{}, t + 1, sB, sA, pB, pA);
-          last_in_b = true;
+      auto general_pairs = [&](int t_end) {
+        for (; t < t_end; t += 2) {
+          step(std::false_type{}, t, sA, sB, pA, pB);
+          last_in_b = false;
+          if (t + 1 < ntiles) {
+            step(std::false_type{}, t + 1, sB, sA, pB, pA);
+            last_in_b = true;
+          }
         }
+      };
+      if (nfast > 0) {
+        general_pairs(kRamp);  // issued == kRamp - 1 + kWAhead afterwards
+        for (; t < nfast; t += 2) {
+          step(std::true_type{}, t, sA, sB, pA, pB);
+          step(std::true_type{}, t + 1, sB, sA, pB, pA);
+        }
+        issued = nfast - 1 + kWAhead;
+        last_in_b = true;
       }
+      general_pairs(ntiles);
       // PV of the last tile (V read in the last step)
       if (active) {
         vm_wait<0>();
@@ -644,7 +711,7 @@ void attn_wide_kernel(AttnArgs a) {
 
   #pragma unroll
     for (int rt = 0; rt < RT; ++rt) mref[rt] = -INFINITY;
-    run(skip, true);
+    run(skip, spec_landed, true);
 
     // ---- overflow check; exact two-pass recompute when needed ------------------
     if (tid == 0) s_redo = 0;
@@ -694,7 +761,7 @@ void attn_wide_kernel(AttnArgs a) {
         }
         lds_barrier();
       }
-      run(0, false);
+      run(0, 0, false);
     }
     if (err) raise_err(a.dev_err, err);
 
