@@ -19,17 +19,23 @@
 // residual by inverse CDF in vocabulary order.
 //
 // Kernels:
-//  0. filter_threshold_kernel (only with a filter): one 1024-thread
-//     workgroup per row finds tau by radix selection over order-preserving
-//     32-bit keys of the logits (11-bit digits, histograms in LDS): top-k by
-//     counts, then top-p by masses 2^((l - M) c) in 2^-40 fixed point (integer
-//     sums, so the result does not depend on the order of the atomics).
+//  0. the filter's threshold tau (only with a filter), by radix selection
+//     over order-preserving 32-bit keys of the logits (11-bit digits,
+//     histograms in LDS): top-k by counts, then top-p by masses 2^((l - M) c)
+//     in 2^-40 fixed point (integer sums, so the result does not depend on
+//     the order of the atomics).  Top-k of at most 1024 goes through
+//     candidate lists: filter_threshold_kernel over four slices per row keeps
+//     each slice's elements at or above a lower bound of its top-k, then one
+//     workgroup per row selects among them.  Otherwise the selection is
+//     spread over 8192-element slices (sel_*_kernel): a launch per digit,
+//     each adding its slices' histograms into the row's in global memory.
 //  1. softmax_stats_kernel: one workgroup per (row chunk, logits row), the
 //     same streaming layout as the greedy argmax: each thread's 16-byte loads
 //     are all in flight at once.  Per chunk it writes (m, s): the chunk's max
 //     logit and sum_v 2^((l_v - m) c), c = log2(e) / T, summed in a fixed
 //     order (thread, then DPP/lane tree, then waves in order), over the
-//     tokens at or above the row's tau.  HBM-bound: the B*N*V logits are read
+//     tokens at or above the row's tau (after the spread selection, derived
+//     here from its last histogram).  HBM-bound: the B*N*V logits are read
 //     once.
 //  2. stochastic_walk_kernel: one workgroup per sequence.  Every input of
 //     the walk is fetched in parallel first: each node's row statistics
@@ -41,6 +47,8 @@
 #include "tv_internal.h"
 
 #include <limits.h>
+
+#include <type_traits>
 
 namespace tv {
 namespace {
@@ -145,81 +153,6 @@ __device__ __forceinline__ float philox_uniform(uint64_t step, uint64_t seq, uin
   return (float)(uint32_t)(philox_first_word(step, seq, node, slot, k0, k1) >> 40) * 0x1.0p-24f;
 }
 
-// ---- kernel 1: per-chunk softmax statistics ---------------------------------------------
-template <typename T, bool kVector>
-__global__ __launch_bounds__(kThreads) void softmax_stats_kernel(const T* __restrict__ logits,
-                                                                 int64_t vocab, int64_t row_stride,
-                                                                 int64_t chunk_len, int chunks,
-                                                                 float c2,
-                                                                 const float* __restrict__ tau,
-                                                                 float2* __restrict__ stats) {
-  constexpr int VEC = 16 / sizeof(T);
-  constexpr int U = kUnroll * 8 / VEC;
-  __shared__ float s_red[kWaves];
-  const int chunk = blockIdx.x;
-  const int64_t row = blockIdx.y;
-  const T* src = logits + row * row_stride;
-  const int64_t begin = (int64_t)chunk * chunk_len;
-  const int64_t end = begin + chunk_len < vocab ? begin + chunk_len : vocab;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-
-  // every value of the thread's share, in registers (vector u of thread t
-  // covers begin + (u * kThreads + t) * VEC .. +VEC-1)
-  float v[U][VEC];
-  if (kVector) {
-    typedef T vec_t __attribute__((ext_vector_type(VEC)));
-    vec_t x[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t base = begin + ((int64_t)u * kThreads + threadIdx.x) * VEC;
-      if (base + VEC <= end) x[u] = *reinterpret_cast<const vec_t*>(src + base);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t base = begin + ((int64_t)u * kThreads + threadIdx.x) * VEC;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e)
-        v[u][e] = base + VEC <= end ? to_f32<T>(x[u][e])
-                                    : (base + e < end ? to_f32<T>(src[base + e]) : -INFINITY);
-    }
-  } else {
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const int64_t k = begin + ((int64_t)u * kThreads + threadIdx.x) * VEC + e;
-        v[u][e] = k < end ? to_f32<T>(src[k]) : -INFINITY;
-      }
-  }
-  float m = -INFINITY;
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) m = fmaxf(m, v[u][e]);
-  m = wave_max(m);
-  if (lane == 0) s_red[wave] = m;
-  __syncthreads();
-  m = s_red[0];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) m = fmaxf(m, s_red[w]);
-  __syncthreads();
-  float s = 0.f;
-  const float lo = tau ? tau[row] : -INFINITY;  // kept: l >= lo
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) s += v[u][e] >= lo ? exp2f((v[u][e] - m) * c2) : 0.f;  // -inf -> 0
-  s = wave_sum(s);
-  if (lane == 0) s_red[wave] = s;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float t = s_red[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) t += s_red[w];
-    stats[row * chunks + chunk] = make_float2(m, t);
-  }
-}
-
 // ---- kernel 0: the filter's threshold -------------------------------------------------
 constexpr int kFiltThreads = 1024;
 constexpr int kFiltWaves = kFiltThreads / kWave;
@@ -229,6 +162,9 @@ constexpr float kFix = 1099511627776.0f;  // 2^40: masses in fixed point
 constexpr int kCand = 4096;                // top-k candidate list in LDS
 constexpr int kSlices = 4;                 // workgroups per row collecting top-k candidates
 constexpr int kSliceCand = 256;            // candidates kept per (row, slice)
+// top-k of at most kFiltThreads through the slices' candidate lists (else
+// through the spread selection)
+constexpr bool kTopKCandidates = true;
 
 // Order-preserving key of a logit: larger value, larger key; -0 and +0 share
 // the key of +0 (they compare equal).
@@ -534,6 +470,454 @@ __global__ __launch_bounds__(kFiltThreads) void filter_threshold_kernel(
   }
 }
 
+// ---- kernel 0': the filter's threshold by radix selection spread over the row ------------
+// The same selection as above (top-k by counts, then top-p by 2^-40 fixed-point
+// masses), with every pass a launch of its own over (slice, row) workgroups:
+// each builds its slice's histogram of the pass's digit in LDS and adds the
+// nonzero bins into the row's histogram in global memory (integer atomics:
+// the sums do not depend on their order).  At the start of the next pass
+// every workgroup of the row derives the chosen bin from that histogram
+// itself; the row's first workgroup records the state for the pass after.  A
+// first launch takes the slice maxima (the masses are relative to the row
+// maximum) and clears the row's histograms; the statistics kernel after the
+// last pass turns the final state into tau.  Keys here map -0 and +0 to one key (2^31 plus the value's
+// integer-ordered bits), so a threshold at zero keeps both.
+constexpr int kSelThreads = 256;
+constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kSelVecs = 4;    // 16-byte vectors per thread and slice
+constexpr int kSelPasses = 6;  // top-k digits, then top-p digits: 3 each at most
+
+// A row's selection before one pass: the range of keys still searched is
+// key & fixed == prefix.
+struct SelState {
+  uint32_t prefix, fixed;
+  uint32_t tau_k;            // the top-k threshold key, once found (else 0)
+  int32_t whole;             // top-p: the range holds less than the target, kept whole
+  unsigned long long above;  // count or mass of the keys above the range
+  double target;             // the count or mass the descending sum has to reach
+};
+
+struct SelArgs {
+  const void* logits;
+  int64_t vocab, row_stride;
+  int slices;              // slices of kSelThreads * kSelVecs vectors per row
+  int top_k, nk, np;       // nk / np: digits of the top-k / top-p selection (0: off)
+  float top_p, c2;
+  float* slice_max;          // [rows][slices]
+  unsigned long long* hist;  // [rows][kSelPasses][kBins]
+  SelState* state;           // [rows][kSelPasses]
+  float* tau;                // [rows]
+};
+
+// order-preserving key of fp32 bits u: 2^31 + (u's sign-magnitude value as a
+// two's complement integer), so that -0 and +0 share 2^31
+__device__ __forceinline__ uint32_t sel_key(uint32_t u) {
+  const uint32_t s = (uint32_t)((int32_t)u >> 31);
+  return (u ^ (s | 0x80000000u)) - s;
+}
+
+__device__ __forceinline__ float sel_key_value(uint32_t k) {
+  return __uint_as_float(k >= 0x80000000u ? k & 0x7FFFFFFFu : 0x80000000u | (0x80000000u - k));
+}
+
+// shift and width of digit d of the key, high digit first (bf16 values fill
+// the top 16 bits of the key: two digits; fp32: three)
+__device__ __forceinline__ void sel_digit(int key_bytes, int d, int& sh, int& width) {
+  if (d == 0) {
+    sh = 21;
+    width = 11;
+  } else if (key_bytes == 2) {
+    sh = 16;
+    width = 5;
+  } else {
+    sh = d == 1 ? 10 : 0;
+    width = d == 1 ? 11 : 10;
+  }
+}
+
+struct SelScratch {
+  unsigned long long wsum[kSelWaves];
+  unsigned long long above;
+  float m[kSelWaves];
+  int sel, cross;
+};
+
+// The largest bin d, in descending order, of the row's histogram h (nbins
+// bins) with above + sum(h[d..]) >= target (target = frac * total when
+// frac > 0): every thread gets it (-1 when even the whole range falls short),
+// the sum above it and the histogram's total.  Thread t holds bins
+// nbins - 1 - t * per down to nbins - t * per - per.
+__device__ void block_select(const unsigned long long* __restrict__ h, int nbins,
+                             unsigned long long above, double target, double frac,
+                             SelScratch& sc, int& sel, unsigned long long& above_out,
+                             unsigned long long& total) {
+  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
+  const int per = nbins >= kSelThreads ? nbins / kSelThreads : 1;  // at most 8
+  const int hi = nbins - 1 - t * per;
+  unsigned long long v[8], mine = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int k = hi - j;
+    const unsigned long long x = h[k > 0 ? k : 0];  // in bounds for every thread
+    v[j] = j < per && k >= 0 ? x : 0ull;
+    mine += v[j];
+  }
+  unsigned long long incl = mine;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const unsigned long long o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == kWave - 1) sc.wsum[wave] = incl;
+  if (t == 0) sc.cross = kSelThreads;
+  __syncthreads();
+  unsigned long long tot = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    incl += w < wave ? sc.wsum[w] : 0ull;
+    tot += sc.wsum[w];
+  }
+  if (frac > 0.0) target = frac * (double)tot;
+  const uint64_t ball = __ballot((double)(above + incl) >= target);
+  if (ball && lane == __builtin_ctzll(ball)) atomicMin(&sc.cross, t);
+  __syncthreads();
+  const int ct = sc.cross;
+  if (t == ct) {
+    unsigned long long run = above + incl - mine;
+    int d = hi;
+    bool done = false;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (!done && j < per && hi - j >= 0) {
+        d = hi - j;
+        if ((double)(run + v[j]) >= target)
+          done = true;
+        else
+          run += v[j];
+      }
+    }
+    sc.sel = d;
+    sc.above = run;
+  } else if (ct == kSelThreads && t == 0) {
+    sc.sel = -1;
+    sc.above = above + tot;
+  }
+  __syncthreads();
+  sel = sc.sel;
+  above_out = sc.above;
+  total = tot;
+  __syncthreads();  // sc may be written again
+}
+
+// The state after pass q (top-k digits first, then top-p digits) from the
+// state before it and the pass's histogram.
+__device__ SelState sel_advance(const SelArgs& a, int key_bytes, SelState st,
+                                const unsigned long long* __restrict__ h, int q,
+                                SelScratch& sc) {
+  const bool mass = q >= a.nk;
+  const int d = mass ? q - a.nk : q;
+  int sh, width;
+  sel_digit(key_bytes, d, sh, width);
+  if (!(mass && st.whole)) {
+    int sel;
+    unsigned long long ab, total;
+    block_select(h, 1 << width, st.above, mass ? st.target : (double)a.top_k,
+                 mass && d == 0 ? (double)a.top_p : 0.0, sc, sel, ab, total);
+    // the first top-p digit's histogram holds the whole kept mass
+    if (mass && d == 0) st.target = (double)a.top_p * (double)total;
+    if (sel < 0) {
+      st.whole = 1;  // rounding: the range holds less than the target, keep it all
+    } else {
+      st.prefix |= (uint32_t)sel << sh;
+      st.fixed |= (uint32_t)((1 << width) - 1) << sh;
+      st.above = ab;
+    }
+  }
+  if (!mass && d == a.nk - 1) {
+    // the k-th largest key found: top-p starts over on the keys at or above it
+    st.tau_k = st.prefix;
+    st.prefix = st.fixed = 0u;
+    st.whole = 0;
+    st.above = 0ull;
+    st.target = 0.0;
+  }
+  return st;
+}
+
+// A slice's elements as fp32 bits, one 16-byte vector per (i, thread): vector
+// i of thread t starts at element lo + (i * kSelThreads + t) * VEC.  Vectors
+// past the slice's last whole vector read the slice's first one (in bounds)
+// and are masked by the caller; the partial vector at the row's end, if
+// any, is left to sel_tail.
+template <typename T, bool kVector>
+struct SelSlice {
+  static constexpr int VEC = 16 / sizeof(T);
+  static constexpr int kWords = 16 / 4;
+  uint32_t w[kSelVecs][kWords];
+  int lo, hi, hi_full;  // [lo, hi): the slice; [lo, hi_full): its whole vectors
+
+  __device__ __forceinline__ void load(const T* __restrict__ src, int64_t vocab, int s) {
+    constexpr int cap = kSelThreads * kSelVecs * VEC;
+    lo = s * cap;
+    hi = (int)(vocab - lo < cap ? vocab - lo : cap) + lo;
+    hi_full = kVector ? lo + (hi - lo) / VEC * VEC : lo;
+#pragma unroll
+    for (int i = 0; i < kSelVecs; ++i) {
+      const int k0 = lo + (i * kSelThreads + (int)threadIdx.x) * VEC;
+      const int kc = k0 + VEC <= hi_full ? k0 : lo;
+      if (kVector && hi_full > lo) {
+        const uint4 x = *reinterpret_cast<const uint4*>(src + kc);
+        w[i][0] = x.x;
+        w[i][1] = x.y;
+        w[i][2] = x.z;
+        w[i][3] = x.w;
+      }
+    }
+  }
+  // element e of vector i as fp32 bits
+  __device__ __forceinline__ uint32_t bits(int i, int e) const {
+    if (sizeof(T) == 2) {
+      const uint32_t x = w[i][e / 2];
+      return e % 2 == 0 ? x << 16 : x & 0xFFFF0000u;
+    }
+    return w[i][e];
+  }
+  __device__ __forceinline__ bool whole(int i) const {
+    return lo + (i * kSelThreads + (int)threadIdx.x) * VEC + VEC <= hi_full;
+  }
+};
+
+__device__ __forceinline__ uint32_t elem_bits(bf16 x) {
+  return (uint32_t)__builtin_bit_cast(unsigned short, x) << 16;
+}
+__device__ __forceinline__ uint32_t elem_bits(float x) { return __float_as_uint(x); }
+
+// f(bits) for the elements of [from, hi) one lane at a time: the partial
+// vector at the row's end, or a whole slice of a row read element-wise
+template <typename T, typename F>
+__device__ __forceinline__ void sel_tail(const T* __restrict__ src, int from, int hi, F&& f) {
+  for (int k = from + (int)threadIdx.x; k < hi; k += kSelThreads) f(elem_bits(src[k]));
+}
+
+// the row maximum from its slice maxima, for every thread
+__device__ __forceinline__ float sel_row_max(const SelArgs& a, int64_t row, SelScratch& sc) {
+  float m = -INFINITY;
+  for (int i = (int)threadIdx.x; i < a.slices; i += kSelThreads)
+    m = fmaxf(m, a.slice_max[row * a.slices + i]);
+  m = wave_max(m);
+  if (threadIdx.x % kWave == 0) sc.m[threadIdx.x / kWave] = m;
+  __syncthreads();
+  m = sc.m[0];
+#pragma unroll
+  for (int w = 1; w < kSelWaves; ++w) m = fmaxf(m, sc.m[w]);
+  return m;
+}
+
+// first launch: the slice maxima (for top-p) and cleared histograms
+template <typename T, bool kVector>
+__global__ __launch_bounds__(kSelThreads) void sel_start_kernel(SelArgs a) {
+  constexpr int VEC = 16 / sizeof(T);
+  __shared__ float s_red[kSelWaves];
+  const int s = blockIdx.x, t = threadIdx.x;
+  const int64_t row = blockIdx.y;
+  // the row's histograms of the passes to come, cleared by its workgroups in turn
+  const int words = (a.nk + a.np) * kBins;
+  const int per = (words + a.slices - 1) / a.slices;
+  unsigned long long* h = a.hist + row * kSelPasses * kBins;
+  for (int i = s * per + t; i < min(words, s * per + per); i += kSelThreads) h[i] = 0ull;
+  if (a.np == 0) return;  // uniform: counts need no maximum
+  const T* src = reinterpret_cast<const T*>(a.logits) + row * a.row_stride;
+  SelSlice<T, kVector> sl;
+  sl.load(src, a.vocab, s);
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kSelVecs; ++i) {
+    const bool ok = sl.whole(i);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) m = fmaxf(m, ok ? __uint_as_float(sl.bits(i, e)) : -INFINITY);
+  }
+  sel_tail(src, sl.hi_full, sl.hi, [&](uint32_t u) { m = fmaxf(m, __uint_as_float(u)); });
+  m = wave_max(m);
+  if (t % kWave == 0) s_red[t / kWave] = m;
+  __syncthreads();
+  if (t == 0) {
+    for (int w = 1; w < kSelWaves; ++w) m = fmaxf(m, s_red[w]);
+    a.slice_max[row * a.slices + s] = fmaxf(m, s_red[0]);
+  }
+}
+
+// pass g: the histogram of its digit over the keys still in range (counts
+// for a top-k digit, masses for a top-p one)
+template <typename T, bool kVector, bool kMass>
+__global__ __launch_bounds__(kSelThreads) void sel_pass_kernel(SelArgs a, int g) {
+  constexpr int VEC = 16 / sizeof(T);
+  __shared__ unsigned long long hist[kBins];  // counts: the first kBins words as uint32
+  __shared__ SelScratch sc;
+  const int s = blockIdx.x, t = threadIdx.x;
+  const int64_t row = blockIdx.y;
+  const T* src = reinterpret_cast<const T*>(a.logits) + row * a.row_stride;
+  // the elements first: the state below does not depend on them
+  SelSlice<T, kVector> sl;
+  sl.load(src, a.vocab, s);
+  for (int i = t; i < kBins; i += kSelThreads) hist[i] = 0ull;
+  SelState st{0u, 0u, 0u, 0, 0ull, 0.0};
+  if (g > 0)
+    st = sel_advance(a, (int)sizeof(T), a.state[row * kSelPasses + g - 1],
+                     a.hist + (row * kSelPasses + g - 1) * kBins, g - 1, sc);
+  if (s == 0 && t == 0) a.state[row * kSelPasses + g] = st;
+  if (kMass && st.whole) return;  // uniform over the workgroup
+  // log2 of an element's fixed-point mass: l c2 + (40 - M c2)
+  const float base = kMass ? 40.f - sel_row_max(a, row, sc) * a.c2 : 0.f;
+  if (!kMass) __syncthreads();  // the cleared histogram (sel_row_max's barrier otherwise)
+  int sh, width;
+  sel_digit((int)sizeof(T), kMass ? g - a.nk : g, sh, width);
+  const uint32_t mask = (1u << width) - 1u;
+  uint32_t* hist32 = reinterpret_cast<uint32_t*>(hist);
+  const uint32_t fixed = st.fixed, prefix = st.prefix, tau_k = st.tau_k;
+  const float c2 = a.c2;
+  auto add = [&](uint32_t u, auto first) {
+    const uint32_t key = sel_key(u);
+    if (!decltype(first)::value && (key & fixed) != prefix) return;
+    const uint32_t bin = (key >> sh) & mask;
+    if (kMass) {
+      // 2^40 exp2((l - M) c2) as an integer: high and low 32-bit halves
+      const float w = __builtin_amdgcn_exp2f(fmaf(__uint_as_float(u), c2, base));
+      if (key < tau_k || !(w >= 1.f)) return;
+      const uint32_t h32 = (uint32_t)(w * 0x1p-32f);
+      const uint32_t l32 = (uint32_t)fmaf((float)h32, -0x1p32f, w);
+      atomicAdd(&hist[bin], ((unsigned long long)h32 << 32) | l32);
+    } else {
+      atomicAdd(&hist32[bin], 1u);
+    }
+  };
+  auto run = [&](auto first) {
+#pragma unroll
+    for (int i = 0; i < kSelVecs; ++i) {
+      const bool ok = sl.whole(i);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e)
+        if (ok) add(sl.bits(i, e), first);
+    }
+    sel_tail(src, sl.hi_full, sl.hi, [&](uint32_t u) { add(u, first); });
+  };
+  if (fixed == 0u)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
+  __syncthreads();
+  unsigned long long* gh = a.hist + (row * kSelPasses + g) * kBins;
+  for (int i = t; i <= (int)mask; i += kSelThreads) {
+    const unsigned long long c = kMass ? hist[i] : hist32[i];
+    if (c) atomicAdd(&gh[i], c);
+  }
+}
+
+// ---- kernel 1: per-chunk softmax statistics ---------------------------------------------
+// Vector u of thread t covers elements begin + (u * kThreads + t) * VEC ..
+// +VEC-1.  Every vector load is issued unconditionally (vectors past the
+// chunk's last whole one re-read its first and are masked), so all of them
+// are in flight together; the partial vector at the row's end is read
+// element-wise afterwards.  With kDerive the workgroup first turns the
+// spread selection's last histogram into the row's threshold (the chunk-0
+// workgroup records it for the walk).
+template <typename T, bool kVector, bool kDerive>
+__global__ __launch_bounds__(kThreads) void softmax_stats_kernel(const T* __restrict__ logits,
+                                                                 int64_t vocab, int64_t row_stride,
+                                                                 int64_t chunk_len, int chunks,
+                                                                 float c2, float* __restrict__ tau,
+                                                                 float2* __restrict__ stats,
+                                                                 SelArgs sel) {
+  static_assert(kThreads == kSelThreads, "one selection per workgroup");
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int U = kUnroll * 8 / VEC;
+  __shared__ float s_red[kWaves];
+  __shared__ SelScratch sc;
+  const int chunk = blockIdx.x, t = threadIdx.x;
+  const int64_t row = blockIdx.y;
+  const T* src = logits + row * row_stride;
+  const int64_t begin = (int64_t)chunk * chunk_len;
+  const int64_t end = begin + chunk_len < vocab ? begin + chunk_len : vocab;
+  const int64_t end_full = kVector ? begin + (end - begin) / VEC * VEC : begin;
+  const int lane = t % kWave, wave = t / kWave;
+
+  uint4 x[U];
+  if (kVector && end_full > begin) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t base = begin + ((int64_t)u * kThreads + t) * VEC;
+      x[u] = *reinterpret_cast<const uint4*>(src + (base + VEC <= end_full ? base : begin));
+    }
+  }
+  // element e of vector u as a float (-inf past the whole vectors)
+  auto val = [&](int u, int e) -> float {
+    const int64_t base = begin + ((int64_t)u * kThreads + t) * VEC;
+    uint32_t b;
+    if (sizeof(T) == 2) {
+      const uint32_t w = (&x[u].x)[e / 2];
+      b = e % 2 == 0 ? w << 16 : w & 0xFFFF0000u;
+    } else {
+      b = (&x[u].x)[e];
+    }
+    return base + VEC <= end_full ? __uint_as_float(b) : -INFINITY;
+  };
+  float lo = -INFINITY;  // kept: l >= lo
+  if (kDerive) {
+    const int q = sel.nk + sel.np - 1;
+    const SelState st = sel_advance(sel, (int)sizeof(T), sel.state[row * kSelPasses + q],
+                                    sel.hist + (row * kSelPasses + q) * kBins, q, sc);
+    lo = sel_key_value(sel.np > 0 && st.prefix > st.tau_k ? st.prefix : st.tau_k);
+    if (chunk == 0 && t == 0) tau[row] = lo;
+  } else if (tau) {
+    lo = tau[row];
+  }
+  // the elements read one at a time: [end_full, end), at most one per thread
+  // for whole-vector rows
+  const int64_t kt = end_full + t;
+  float tail = -INFINITY;
+  for (int64_t k = kt; k < end; k += kThreads) tail = fmaxf(tail, to_f32<T>(src[k]));
+  const bool has_tail = kt < end && end - end_full <= kThreads;
+
+  float m = tail;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) m = fmaxf(m, val(u, e));
+  m = wave_max(m);
+  if (lane == 0) s_red[wave] = m;
+  __syncthreads();
+  m = s_red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) m = fmaxf(m, s_red[w]);
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const float v = val(u, e);
+      s += v >= lo ? __builtin_amdgcn_exp2f((v - m) * c2) : 0.f;  // -inf -> 0
+    }
+  if (has_tail) {
+    s += tail >= lo ? __builtin_amdgcn_exp2f((tail - m) * c2) : 0.f;
+  } else {
+    // element-wise rows (or a tail longer than a workgroup): the rest in order
+    for (int64_t k = kt; k < end; k += kThreads) {
+      const float v = to_f32<T>(src[k]);
+      s += v >= lo ? __builtin_amdgcn_exp2f((v - m) * c2) : 0.f;
+    }
+  }
+  if (m == -INFINITY) s = 0.f;  // no finite logit: (l - m) would be NaN
+  s = wave_sum(s);
+  if (lane == 0) s_red[wave] = s;
+  __syncthreads();
+  if (t == 0) {
+    float sum = s_red[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) sum += s_red[w];
+    stats[row * chunks + chunk] = make_float2(m, sum);
+  }
+}
+
 // ---- kernel 2: the walk ------------------------------------------------------------------
 struct WalkArgs {
   const void* logits;
@@ -814,6 +1198,25 @@ __global__ __launch_bounds__(kWalkThreads) void stochastic_walk_kernel(WalkArgs 
 
 }  // namespace
 
+namespace {
+
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+// slices per row of the spread selection: up to kSelVecs vectors per thread
+int sel_slices(int64_t vocab, size_t elem) {
+  const int64_t cap = (int64_t)kSelThreads * kSelVecs * (int64_t)(16 / elem);
+  return (int)((vocab + cap - 1) / cap);
+}
+
+// workspace: chunk statistics, thresholds, the slices' top-k candidates,
+// then the spread selection's slice maxima, histograms and states
+size_t sel_offset(size_t rows, int chunks) {
+  return round256(rows * chunks * sizeof(float2)) + round256(rows * sizeof(float)) +
+         round256(rows * kSlices * (kSliceCand * sizeof(uint32_t) + sizeof(int) + sizeof(float)));
+}
+
+}  // namespace
+
 AcceptPlan plan_stochastic(int batch, int n, int64_t vocab) {
   AcceptPlan p;
   const int64_t per_pass = (int64_t)kThreads * 8;
@@ -825,9 +1228,10 @@ AcceptPlan plan_stochastic(int batch, int n, int64_t vocab) {
   p.chunks = (int)((vocab + chunk - 1) / chunk);
   // chunk statistics, one threshold per row, then the slices' top-k candidates
   const size_t rows = (size_t)batch * n;
-  p.ws_bytes = ((rows * p.chunks * sizeof(float2) + 255) / 256) * 256 +
-               ((rows * sizeof(float) + 255) / 256) * 256 +
-               rows * kSlices * (kSliceCand * sizeof(uint32_t) + sizeof(int) + sizeof(float)) + 256;
+  p.ws_bytes = sel_offset(rows, p.chunks) +
+               round256(rows * sel_slices(vocab, sizeof(float)) * sizeof(float)) +
+               round256(rows * kSelPasses * kBins * sizeof(unsigned long long)) +
+               rows * kSelPasses * sizeof(SelState);
   return p;
 }
 
@@ -838,13 +1242,15 @@ void launch_typed(const void* logits, int64_t vocab, int64_t row_stride, int bat
                   float c2, int top_k, float top_p, const AcceptPlan& plan, float2* stats,
                   float* tau, const WalkArgs& w, hipStream_t stream) {
   const unsigned rows = (unsigned)((size_t)batch * n);
+  SelArgs sa{};
+  bool derive = false;
   if (tau) {
     // the slices' candidate buffers follow the thresholds in the workspace
     char* base = reinterpret_cast<char*>(tau) + (((size_t)rows * sizeof(float) + 255) / 256) * 256;
     uint32_t* cand_keys = reinterpret_cast<uint32_t*>(base);
     int* cand_count = reinterpret_cast<int*>(cand_keys + (size_t)rows * kSlices * kSliceCand);
     float* slice_max = reinterpret_cast<float*>(cand_count + (size_t)rows * kSlices);
-    if (top_k > 0 && top_k <= kFiltThreads && (int64_t)top_k < vocab) {
+    if (kTopKCandidates && top_k > 0 && top_k <= kFiltThreads && (int64_t)top_k < vocab) {
       hipLaunchKernelGGL((filter_threshold_kernel<T, kVector>), dim3(rows, kSlices),
                          dim3(kFiltThreads), 0, stream, (const T*)logits, vocab, row_stride,
                          top_k, top_p, c2, tau, 1, cand_keys, cand_count, slice_max);
@@ -852,14 +1258,45 @@ void launch_typed(const void* logits, int64_t vocab, int64_t row_stride, int bat
                          stream, (const T*)logits, vocab, row_stride, top_k, top_p, c2, tau, 2,
                          cand_keys, cand_count, slice_max);
     } else {
-      hipLaunchKernelGGL((filter_threshold_kernel<T, kVector>), dim3(rows), dim3(kFiltThreads), 0,
-                         stream, (const T*)logits, vocab, row_stride, top_k, top_p, c2, tau, 0,
-                         cand_keys, cand_count, slice_max);
+      // the spread selection
+      constexpr int kDigits = sizeof(T) == 2 ? 2 : 3;
+      sa.logits = logits;
+      sa.vocab = vocab;
+      sa.row_stride = row_stride;
+      sa.slices = sel_slices(vocab, sizeof(T));
+      sa.top_k = top_k;
+      sa.nk = top_k > 0 && (int64_t)top_k < vocab ? kDigits : 0;
+      sa.np = top_p < 1.f ? kDigits : 0;
+      sa.top_p = top_p;
+      sa.c2 = c2;
+      char* sel = reinterpret_cast<char*>(stats) + sel_offset(rows, plan.chunks);
+      sa.slice_max = reinterpret_cast<float*>(sel);
+      sel += round256((size_t)rows * sel_slices(vocab, sizeof(float)) * sizeof(float));
+      sa.hist = reinterpret_cast<unsigned long long*>(sel);
+      sel += round256((size_t)rows * kSelPasses * kBins * sizeof(unsigned long long));
+      sa.state = reinterpret_cast<SelState*>(sel);
+      sa.tau = tau;
+      const dim3 grid(sa.slices, rows);
+      hipLaunchKernelGGL((sel_start_kernel<T, kVector>), grid, dim3(kSelThreads), 0, stream, sa);
+      for (int g = 0; g < sa.nk + sa.np; ++g) {
+        if (g < sa.nk)
+          hipLaunchKernelGGL((sel_pass_kernel<T, kVector, false>), grid, dim3(kSelThreads), 0,
+                             stream, sa, g);
+        else
+          hipLaunchKernelGGL((sel_pass_kernel<T, kVector, true>), grid, dim3(kSelThreads), 0,
+                             stream, sa, g);
+      }
+      derive = true;  // the stats kernel takes tau from the last histogram
     }
   }
-  hipLaunchKernelGGL((softmax_stats_kernel<T, kVector>), dim3(plan.chunks, rows), dim3(kThreads),
-                     0, stream, (const T*)logits, vocab, row_stride, plan.chunk_len, plan.chunks,
-                     c2, (const float*)tau, stats);
+  if (derive)
+    hipLaunchKernelGGL((softmax_stats_kernel<T, kVector, true>), dim3(plan.chunks, rows),
+                       dim3(kThreads), 0, stream, (const T*)logits, vocab, row_stride,
+                       plan.chunk_len, plan.chunks, c2, tau, stats, sa);
+  else
+    hipLaunchKernelGGL((softmax_stats_kernel<T, kVector, false>), dim3(plan.chunks, rows),
+                       dim3(kThreads), 0, stream, (const T*)logits, vocab, row_stride,
+                       plan.chunk_len, plan.chunks, c2, tau, stats, sa);
   hipLaunchKernelGGL((stochastic_walk_kernel<T, kVector>), dim3(batch), dim3(kWalkThreads), 0,
                      stream, w);
 }
