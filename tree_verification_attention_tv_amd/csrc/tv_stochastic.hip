@@ -160,11 +160,7 @@ constexpr int kBinBits = 11;
 constexpr int kBins = 1 << kBinBits;
 constexpr float kFix = 1099511627776.0f;  // 2^40: masses in fixed point
 constexpr int kCand = 4096;                // top-k candidate list in LDS
-constexpr int kSlices = 4;                 // workgroups per row collecting top-k candidates
 constexpr int kSliceCand = 256;            // candidates kept per (row, slice)
-// top-k of at most kFiltThreads through the slices' candidate lists (else
-// through the spread selection)
-constexpr bool kTopKCandidates = true;
 
 // Order-preserving key of a logit: larger value, larger key; -0 and +0 share
 // the key of +0 (they compare equal).
@@ -221,252 +217,6 @@ __device__ void select_bin(const unsigned long long* hist, int nbins, unsigned l
     }
     *s_sel = d;
     *s_above = run;
-  }
-}
-
-template <typename T, bool kVector>
-__global__ __launch_bounds__(kFiltThreads) void filter_threshold_kernel(
-    const T* __restrict__ logits, int64_t vocab, int64_t row_stride, int top_k, float top_p,
-    float c2, float* __restrict__ tau, int phase, uint32_t* __restrict__ cand_keys,
-    int* __restrict__ cand_count, float* __restrict__ slice_max) {
-  // phase 0: the whole search in this workgroup.
-  // phase 1 (grid rows x kSlices, top_k <= kFiltThreads): each workgroup
-  //   collects its slice's top-k candidates (the elements at or above the
-  //   top_k-th largest of its threads' maxima: the row's top-k elements are
-  //   among them, since each is in its slice's top-k) and the slice maximum.
-  // phase 2: the search from those candidates (the row itself if a slice
-  //   had more than kSliceCand).
-  constexpr int VEC = 16 / sizeof(T);
-  __shared__ unsigned long long hist[kBins];
-  __shared__ uint32_t c_key[kCand];  // candidates: the elements at or above a lower bound
-  __shared__ float c_val[kCand];
-  __shared__ int s_ncand;
-  __shared__ float s_red[kFiltWaves];
-  __shared__ int s_sel;
-  __shared__ unsigned long long s_above, s_total;
-  const int64_t row = blockIdx.x;
-  const T* src = logits + row * row_stride;
-  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
-  // elements [lo, hi) of the row (a slice of VEC-multiple length in phase 1)
-  int lo = 0, hi = (int)vocab;
-  if (phase == 1) {
-    const int sl = (((int)vocab + kSlices - 1) / kSlices + VEC - 1) / VEC * VEC;
-    lo = min((int)blockIdx.y * sl, (int)vocab);
-    hi = min(lo + sl, (int)vocab);
-  }
-  // Every value of the row this thread owns: elements k0 .. k0 + VEC - 1 for
-  // k0 = (t + i * kFiltThreads) * VEC, read with 8 loads in flight per
-  // thread (the row stays in L2 between passes).
-  typedef T vec_t __attribute__((ext_vector_type(VEC)));
-  constexpr int kBatch = 8;
-  auto visit = [&](auto&& f) {
-    for (int b0 = lo + t * VEC; b0 < hi; b0 += kBatch * kFiltThreads * VEC) {
-      vec_t x[kBatch];
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-        const int k0 = b0 + i * kFiltThreads * VEC;
-        if (kVector && k0 + VEC <= hi) {
-          x[i] = *reinterpret_cast<const vec_t*>(src + k0);
-        } else {
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) x[i][e] = k0 + e < hi ? src[k0 + e] : (T)0.f;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-        const int k0 = b0 + i * kFiltThreads * VEC;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e)
-          if (k0 + e < hi) f(to_f32<T>(x[i][e]));
-      }
-    }
-  };
-  // digits of the key, high first: bf16 values fill the top 16 bits
-  constexpr int kDigits = sizeof(T) == 2 ? 2 : 3;
-  const int shifts[3] = {21, sizeof(T) == 2 ? 16 : 10, 0};
-  const int widths[3] = {11, sizeof(T) == 2 ? 5 : 11, 10};
-
-  auto clear = [&]() {
-    for (int i = t; i < kBins; i += kFiltThreads) hist[i] = 0ull;
-    __syncthreads();
-  };
-  // Element sources: f(key, value) for every element of the row, or of the
-  // candidate list collected in LDS (below).
-  auto row_src = [&](auto&& f) { visit([&](float v) { f(order_key(v), v); }); };
-  auto cand_src = [&](auto&& f) {
-    const int nc = s_ncand;
-    for (int i = t; i < nc; i += kFiltThreads) f(c_key[i], c_val[i]);
-  };
-
-  // ---- phase 2: the candidates the slices collected, when none overflowed ----
-  bool pre = false;
-  float M = -INFINITY, m_t = -INFINITY;
-  if (phase == 2) {
-    const int64_t r0 = row * kSlices;
-    if (t == 0) {
-      int total = 0;
-      bool ok = true;
-      for (int q = 0; q < kSlices; ++q) {
-        const int c = cand_count[r0 + q];
-        ok = ok && c <= kSliceCand;
-        total += c;
-      }
-      s_ncand = ok ? total : -1;
-    }
-    __syncthreads();
-    pre = s_ncand >= 0;
-    if (pre) {
-      // slice q's candidates go to c_key[off_q ..] with off_q the counts before it
-      for (int q = 0, off = 0; q < kSlices; ++q) {
-        const int c = cand_count[r0 + q];
-        for (int i = t; i < c; i += kFiltThreads) {
-          const uint32_t key = cand_keys[(r0 + q) * kSliceCand + i];
-          c_key[off + i] = key;
-          c_val[off + i] = key_value(key);
-        }
-        off += c;
-        M = fmaxf(M, slice_max[r0 + q]);
-      }
-      __syncthreads();
-    }
-  }
-  if (!pre) {
-    // ---- the row's (or slice's) maximum, and each thread's own maximum ----
-    visit([&](float v) { m_t = fmaxf(m_t, v); });
-    const float wm = wave_max(m_t);
-    if (lane == 0) s_red[wave] = wm;
-    __syncthreads();
-    M = s_red[0];
-    for (int w = 1; w < kFiltWaves; ++w) M = fmaxf(M, s_red[w]);
-  }
-
-  // ---- top-k: the k-th largest key (ties at it are kept) ----
-  // kth(src): the top_k-th largest of the keys src hands over (radix
-  // selection, counts in LDS)
-  auto kth = [&](auto&& src) -> uint32_t {
-    uint32_t prefix = 0u, fixed = 0u;
-    unsigned long long above = 0ull;
-    for (int g = 0; g < kDigits; ++g) {
-      const int sh = shifts[g], mask = (1 << widths[g]) - 1;
-      clear();
-      src([&](uint32_t key, float) {
-        if ((key & fixed) == prefix) atomicAdd(&hist[(key >> sh) & mask], 1ull);
-      });
-      __syncthreads();
-      if (wave == 0)
-        select_bin(hist, mask + 1, above, (double)top_k, 0.0, &s_sel, &s_above, &s_total);
-      __syncthreads();
-      prefix |= (uint32_t)s_sel << sh;  // a count of >= top_k always exists
-      fixed |= (uint32_t)mask << sh;
-      above = s_above;
-      __syncthreads();
-    }
-    return prefix;
-  };
-  uint32_t tau_k = 0u;
-  bool use_cand = pre;  // every key >= tau_k is in the candidate list
-  if (pre) {
-    tau_k = kth(cand_src);
-  } else if (top_k > 0 && (int64_t)top_k < vocab) {
-    // A lower bound first: the top_k-th largest of the threads' maxima (top_k
-    // threads hold an element at or above it, so the answer is at or above
-    // it too).  The elements at or above it are few: they are collected
-    // once into LDS, and the selections run on them instead of the row.
-    uint32_t lower = 0u;
-    if (top_k <= kFiltThreads) {
-      const uint32_t mk = order_key(m_t);
-      lower = kth([&](auto&& f) { f(mk, m_t); });
-      if (t == 0) s_ncand = 0;
-      __syncthreads();
-      visit([&](float v) {
-        const uint32_t key = order_key(v);
-        const bool c = key >= lower;
-        const uint64_t bal = __ballot(c);
-        if (bal) {  // one atomic per wave and element slot
-          const int leader = __builtin_ctzll(bal);
-          int base = 0;
-          if (lane == leader) base = atomicAdd(&s_ncand, __builtin_popcountll(bal));
-          base = __shfl(base, leader);
-          if (c) {
-            const int i = base + __builtin_popcountll(bal & ((1ull << lane) - 1ull));
-            if (i < kCand) {
-              c_key[i] = key;
-              c_val[i] = v;
-            }
-          }
-        }
-      });
-      __syncthreads();
-      if (phase == 1) {
-        // this slice's candidates and maximum for phase 2
-        const int64_t q = row * kSlices + blockIdx.y;
-        const int c = s_ncand;
-        for (int i = t; i < min(c, kSliceCand); i += kFiltThreads)
-          cand_keys[q * kSliceCand + i] = c_key[i];
-        if (t == 0) {
-          cand_count[q] = c;
-          slice_max[q] = M;
-        }
-        return;  // uniform over the workgroup
-      }
-      use_cand = s_ncand <= kCand;  // else (many ties) the row is used
-      __syncthreads();
-    }
-    if (use_cand) {
-      tau_k = kth(cand_src);
-    } else {
-      tau_k = kth([&](auto&& f) {
-        row_src([&](uint32_t key, float v) {
-          if (key >= lower) f(key, v);
-        });
-      });
-    }
-  }
-
-  // ---- top-p: the last key (descending) whose strictly larger keys hold
-  // less than top_p of the mass kept by top-k ----
-  uint32_t tau_p = 0u;
-  if (top_p < 1.f) {
-    uint32_t prefix = 0u, fixed = 0u;
-    unsigned long long above = 0ull;
-    double target = 0.0;
-    bool whole = false;  // every remaining key is kept
-    auto pass = [&](auto&& src, int sh, int mask) {
-      src([&](uint32_t key, float v) {
-        if (key >= tau_k && (key & fixed) == prefix) {
-          const unsigned long long w = (unsigned long long)(exp2f((v - M) * c2) * kFix);
-          atomicAdd(&hist[(key >> sh) & mask], w);
-        }
-      });
-    };
-    for (int g = 0; g < kDigits && !whole; ++g) {
-      const int sh = shifts[g], mask = (1 << widths[g]) - 1;
-      clear();
-      if (use_cand)
-        pass(cand_src, sh, mask);
-      else
-        pass(row_src, sh, mask);
-      __syncthreads();
-      // the first digit's histogram holds the whole kept mass: target = top_p * it
-      if (wave == 0)
-        select_bin(hist, mask + 1, above, target, g == 0 ? (double)top_p : 0.0, &s_sel, &s_above,
-                   &s_total);
-      __syncthreads();
-      if (g == 0) target = (double)top_p * (double)s_total;
-      if (s_sel < 0) {
-        whole = true;  // rounding: the range holds less than the target, keep it all
-      } else {
-        prefix |= (uint32_t)s_sel << sh;
-        fixed |= (uint32_t)mask << sh;
-        above = s_above;
-      }
-      __syncthreads();
-    }
-    tau_p = prefix;
-  }
-  if (t == 0) {
-    const bool any = (top_k > 0 && (int64_t)top_k < vocab) || top_p < 1.f;
-    tau[row] = any ? key_value(tau_k > tau_p ? tau_k : tau_p) : -INFINITY;
   }
 }
 
@@ -809,6 +559,442 @@ __global__ __launch_bounds__(kSelThreads) void sel_pass_kernel(SelArgs a, int g)
   for (int i = t; i <= (int)mask; i += kSelThreads) {
     const unsigned long long c = kMass ? hist[i] : hist32[i];
     if (c) atomicAdd(&gh[i], c);
+  }
+}
+
+// ---- top-k of at most kCandMaxK: candidates per slice, then one workgroup per row ----
+// cand_collect_kernel, over the same (slice, row) grid as the spread
+// selection: the slice's elements at or above the top_k-th largest of its
+// threads' maxima (top_k threads hold an element at or above it, so the
+// slice's top-k, and with them the row's top-k elements of the slice, are
+// among them), at most kSliceCand of them (the count says when there were
+// more), and the slice maximum.  filter_threshold_kernel then takes the k-th
+// largest of the row's candidates (one per thread) and top-p among the keys
+// at or above it in one wave.
+constexpr int kCandMaxK = 32;  // largest top_k taking this path
+
+// The k-th largest of the keys the workgroup's NT threads hold (key valid
+// where ok), by radix selection over 8-bit digits from the top, counts in an
+// LDS histogram of 256 bins (hist); digits below bit `low` are not looked at
+// (bf16 keys have 16 zero low bits).  Every thread gets the key.
+struct KthScratch {
+  uint32_t hist[256];
+  int sel, need;
+};
+
+template <int NT>
+__device__ uint32_t block_kth_key(uint32_t key, bool ok, int k, int low, KthScratch& sc) {
+  const int t = threadIdx.x, lane = t % kWave;
+  uint32_t prefix = 0u, fixed = 0u;
+  int need = k;  // the rank still looked for inside the current range
+  for (int sh = 24; sh >= low; sh -= 8) {
+    for (int i = t; i < 256; i += NT) sc.hist[i] = 0u;
+    __syncthreads();
+    if (ok && (key & fixed) == prefix) atomicAdd(&sc.hist[(key >> sh) & 255u], 1u);
+    __syncthreads();
+    if (t < kWave) {
+      // lane l holds bins 255 - 4l down to 252 - 4l; a descending inclusive scan
+      uint32_t h[4], mine = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        h[j] = sc.hist[255 - 4 * lane - j];
+        mine += h[j];
+      }
+      uint32_t incl = mine;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      const uint64_t b = __ballot((int)incl >= need);  // some lane crosses: need <= count
+      if (lane == (b ? __builtin_ctzll(b) : kWave - 1)) {
+        int run = (int)(incl - mine), d = 255 - 4 * lane;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (run + (int)h[j] >= need) {
+            d = 255 - 4 * lane - j;
+            break;
+          }
+          run += (int)h[j];
+        }
+        sc.sel = d;
+        sc.need = need - run;
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sc.sel << sh;
+    fixed |= 255u << sh;
+    need = sc.need;
+    __syncthreads();  // sc is written again in the next round
+  }
+  return prefix;
+}
+
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long x) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    const uint32_t o = __shfl_xor(x, off);
+    x = o > x ? o : x;
+  }
+  return x;
+}
+
+// 2^40 exp2((l - M) c2) as an integer, from y = l c2 + 40 - M c2 (0 below 1)
+__device__ __forceinline__ unsigned long long fixed_mass(float y) {
+  const float w = __builtin_amdgcn_exp2f(y);
+  if (!(w >= 1.f)) return 0ull;
+  const uint32_t h32 = (uint32_t)(w * 0x1p-32f);
+  const uint32_t l32 = (uint32_t)fmaf((float)h32, -0x1p32f, w);
+  return ((unsigned long long)h32 << 32) | l32;
+}
+
+template <typename T, bool kVector>
+__global__ __launch_bounds__(kSelThreads) void cand_collect_kernel(
+    const T* __restrict__ logits, int64_t vocab, int64_t row_stride, int top_k, int slices,
+    uint32_t* __restrict__ cand_keys, int* __restrict__ cand_count, float* __restrict__ slice_max) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int kLow = sizeof(T) == 2 ? 16 : 0;
+  __shared__ uint32_t s_cand[kSliceCand];
+  __shared__ uint32_t s_max[kSelWaves];
+  __shared__ KthScratch ks;
+  __shared__ int s_n;
+  const int s = blockIdx.x, t = threadIdx.x, lane = t % kWave, wave = t / kWave;
+  const int64_t row = blockIdx.y;
+  const T* src = reinterpret_cast<const T*>(logits) + row * row_stride;
+  SelSlice<T, kVector> sl;
+  sl.load(src, vocab, s);
+  uint32_t mk = 0u;
+#pragma unroll
+  for (int i = 0; i < kSelVecs; ++i) {
+    const bool ok = sl.whole(i);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const uint32_t key = sel_key(sl.bits(i, e));
+      mk = ok && key > mk ? key : mk;
+    }
+  }
+  sel_tail(src, sl.hi_full, sl.hi, [&](uint32_t u) {
+    const uint32_t key = sel_key(u);
+    mk = key > mk ? key : mk;
+  });
+  if (t == 0) s_n = 0;
+  {
+    const uint32_t mx = wave_max_u32(mk);
+    if (lane == 0) s_max[wave] = mx;
+  }
+  // the bound: the top_k-th largest of the threads' largest keys (threads
+  // without an element hold 0, below every key)
+  const uint32_t lower = block_kth_key<kSelThreads>(mk, true, top_k, kLow, ks);
+  // one LDS atomic per wave and element slot that has candidates
+  auto push = [&](uint32_t key, bool take) {
+    const uint64_t b = __ballot(take);
+    if (b) {
+      const int leader = __builtin_ctzll(b);
+      int base = 0;
+      if (lane == leader) base = atomicAdd(&s_n, __builtin_popcountll(b));
+      base = __shfl(base, leader);
+      const int i = base + __builtin_popcountll(b & ((1ull << lane) - 1ull));
+      if (take && i < kSliceCand) s_cand[i] = key;
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < kSelVecs; ++i) {
+    const bool ok = sl.whole(i);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const uint32_t key = sel_key(sl.bits(i, e));
+      push(key, ok && key >= lower);
+    }
+  }
+  sel_tail(src, sl.hi_full, sl.hi, [&](uint32_t u) {
+    const uint32_t key = sel_key(u);
+    push(key, key >= lower);
+  });
+  __syncthreads();
+  const int n = s_n;
+  const int64_t q = row * slices + s;
+  for (int i = t; i < min(n, kSliceCand); i += kSelThreads) cand_keys[q * kSliceCand + i] = s_cand[i];
+  if (t == 0) {
+    uint32_t mx = s_max[0];
+#pragma unroll
+    for (int w = 1; w < kSelWaves; ++w) mx = s_max[w] > mx ? s_max[w] : mx;
+    cand_count[q] = n;
+    slice_max[q] = mx ? sel_key_value(mx) : -INFINITY;
+  }
+}
+
+// Top-p among the candidates at or above tau_k (wave 0): the kept keys are
+// packed into kk with their 2^-40 fixed-point masses in kw; each lane takes
+// some of them and sums the masses of the kept keys at or above its own; the
+// threshold is the largest key whose sum reaches top_p of the kept mass.
+__device__ uint32_t wave_top_p_key(const uint32_t* cand, int n, uint32_t tau_k, float M,
+                                   float top_p, float c2, uint32_t* kk,
+                                   unsigned long long* kw) {
+  const int lane = threadIdx.x % kWave;
+  const float base = 40.f - M * c2;
+  int nk = 0;
+  unsigned long long tot = 0ull;
+  for (int i0 = 0; i0 < n; i0 += kWave) {
+    const int i = i0 + lane;
+    const uint32_t key = i < n ? cand[i] : 0u;
+    const bool kp = i < n && key >= tau_k;
+    const uint64_t b = __ballot(kp);
+    if (kp) {
+      const int j = nk + __builtin_popcountll(b & ((1ull << lane) - 1ull));
+      const unsigned long long w = fixed_mass(fmaf(sel_key_value(key), c2, base));
+      kk[j] = key;
+      kw[j] = w;
+      tot += w;
+    }
+    nk += __builtin_popcountll(b);
+  }
+  const double target = (double)top_p * (double)wave_sum_u64(tot);
+  uint32_t best = 0u;
+  for (int i = lane; i < nk; i += kWave) {
+    const uint32_t key = kk[i];
+    unsigned long long cum = 0ull;
+#pragma unroll 4
+    for (int j = 0; j < nk; ++j) cum += kk[j] >= key ? kw[j] : 0ull;
+    if ((double)cum >= target && key > best) best = key;
+  }
+  return wave_max_u32(best);
+}
+
+template <typename T, bool kVector>
+__global__ __launch_bounds__(kFiltThreads) void filter_threshold_kernel(
+    const T* __restrict__ logits, int64_t vocab, int64_t row_stride, int top_k, float top_p,
+    float c2, float* __restrict__ tau, const uint32_t* __restrict__ cand_keys,
+    const int* __restrict__ cand_count, const float* __restrict__ slice_max, int slices) {
+  // One workgroup per row.  The candidates cand_collect_kernel left for the
+  // row's slices go to LDS and wave 0 selects among them; when a slice had
+  // more than kSliceCand (many ties) the whole search runs here over the row.
+  constexpr int VEC = 16 / sizeof(T);
+  __shared__ unsigned long long hist[kBins];
+  __shared__ uint32_t c_key[kCand];  // candidates: the elements at or above a lower bound
+  __shared__ float c_val[kCand];
+  __shared__ int s_ncand;
+  __shared__ float s_red[kFiltWaves];
+  __shared__ int s_sel;
+  __shared__ unsigned long long s_above, s_total;
+  const int64_t row = blockIdx.x;
+  const T* src = logits + row * row_stride;
+  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
+  const int lo = 0, hi = (int)vocab;
+  // Every value of the row this thread owns: elements k0 .. k0 + VEC - 1 for
+  // k0 = (t + i * kFiltThreads) * VEC, read with 8 loads in flight per
+  // thread (the row stays in L2 between passes).
+  typedef T vec_t __attribute__((ext_vector_type(VEC)));
+  constexpr int kBatch = 8;
+  auto visit = [&](auto&& f) {
+    for (int b0 = lo + t * VEC; b0 < hi; b0 += kBatch * kFiltThreads * VEC) {
+      vec_t x[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int k0 = b0 + i * kFiltThreads * VEC;
+        if (kVector && k0 + VEC <= hi) {
+          x[i] = *reinterpret_cast<const vec_t*>(src + k0);
+        } else {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) x[i][e] = k0 + e < hi ? src[k0 + e] : (T)0.f;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int k0 = b0 + i * kFiltThreads * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          if (k0 + e < hi) f(to_f32<T>(x[i][e]));
+      }
+    }
+  };
+  // digits of the key, high first: bf16 values fill the top 16 bits
+  constexpr int kDigits = sizeof(T) == 2 ? 2 : 3;
+  const int shifts[3] = {21, sizeof(T) == 2 ? 16 : 10, 0};
+  const int widths[3] = {11, sizeof(T) == 2 ? 5 : 11, 10};
+
+  auto clear = [&]() {
+    for (int i = t; i < kBins; i += kFiltThreads) hist[i] = 0ull;
+    __syncthreads();
+  };
+  // Element sources: f(key, value) for every element of the row, or of the
+  // candidate list collected in LDS (below).
+  auto row_src = [&](auto&& f) { visit([&](float v) { f(order_key(v), v); }); };
+  auto cand_src = [&](auto&& f) {
+    const int nc = s_ncand;
+    for (int i = t; i < nc; i += kFiltThreads) f(c_key[i], c_val[i]);
+  };
+
+  float M = -INFINITY, m_t = -INFINITY;
+  // ---- the slices' candidates: every wave reads the counts (lane = slice) ----
+  {
+    const int64_t r0 = row * slices;
+    const int c = lane < slices ? cand_count[r0 + lane] : 0;
+    const float sm = lane < slices ? slice_max[r0 + lane] : -INFINITY;
+    int incl = c;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    const int n = __shfl(incl, kWave - 1);
+    if (slices <= kWave && __ballot(c > kSliceCand) == 0 && n <= kFiltThreads) {  // uniform
+      // slice q's candidates to c_key[off_q ..], off_q the counts before it
+      for (int q = wave; q < slices; q += kFiltWaves) {
+        const int cq = __shfl(c, q), oq = __shfl(incl - c, q);
+        uint32_t k4[kSliceCand / kWave];
+#pragma unroll
+        for (int r = 0; r < kSliceCand / kWave; ++r)
+          k4[r] = cand_keys[(r0 + q) * kSliceCand + lane + r * kWave];  // in the slice's block
+#pragma unroll
+        for (int r = 0; r < kSliceCand / kWave; ++r)
+          if (lane + r * kWave < cq) c_key[oq + lane + r * kWave] = k4[r];
+      }
+      __syncthreads();
+      constexpr int kLow = sizeof(T) == 2 ? 16 : 0;
+      KthScratch& ks = *reinterpret_cast<KthScratch*>(hist);
+      const uint32_t tk = block_kth_key<kFiltThreads>(t < n ? c_key[t] : 0u, t < n, top_k, kLow, ks);
+      if (wave == 0) {
+        uint32_t key = tk;
+        if (top_p < 1.f) {
+          const uint32_t tp = wave_top_p_key(c_key, n, tk, wave_max(sm), top_p, c2,
+                                             reinterpret_cast<uint32_t*>(c_val),
+                                             hist + kBins / 2);
+          key = tp > tk ? tp : tk;
+        }
+        if (lane == 0) tau[row] = sel_key_value(key);
+      }
+      return;
+    }
+  }
+  {
+    // ---- the row's maximum, and each thread's own maximum ----
+    visit([&](float v) { m_t = fmaxf(m_t, v); });
+    const float wm = wave_max(m_t);
+    if (lane == 0) s_red[wave] = wm;
+    __syncthreads();
+    M = s_red[0];
+    for (int w = 1; w < kFiltWaves; ++w) M = fmaxf(M, s_red[w]);
+  }
+
+  // ---- top-k: the k-th largest key (ties at it are kept) ----
+  // kth(src): the top_k-th largest of the keys src hands over (radix
+  // selection, counts in LDS)
+  auto kth = [&](auto&& src) -> uint32_t {
+    uint32_t prefix = 0u, fixed = 0u;
+    unsigned long long above = 0ull;
+    for (int g = 0; g < kDigits; ++g) {
+      const int sh = shifts[g], mask = (1 << widths[g]) - 1;
+      clear();
+      src([&](uint32_t key, float) {
+        if ((key & fixed) == prefix) atomicAdd(&hist[(key >> sh) & mask], 1ull);
+      });
+      __syncthreads();
+      if (wave == 0)
+        select_bin(hist, mask + 1, above, (double)top_k, 0.0, &s_sel, &s_above, &s_total);
+      __syncthreads();
+      prefix |= (uint32_t)s_sel << sh;  // a count of >= top_k always exists
+      fixed |= (uint32_t)mask << sh;
+      above = s_above;
+      __syncthreads();
+    }
+    return prefix;
+  };
+  uint32_t tau_k = 0u;
+  bool use_cand = false;  // every key >= tau_k is in the candidate list
+  if (top_k > 0 && (int64_t)top_k < vocab) {
+    // A lower bound first: the top_k-th largest of the threads' maxima (top_k
+    // threads hold an element at or above it, so the answer is at or above
+    // it too).  The elements at or above it are few: they are collected
+    // once into LDS, and the selections run on them instead of the row.
+    uint32_t lower = 0u;
+    if (top_k <= kFiltThreads) {
+      const uint32_t mk = order_key(m_t);
+      lower = kth([&](auto&& f) { f(mk, m_t); });
+      if (t == 0) s_ncand = 0;
+      __syncthreads();
+      visit([&](float v) {
+        const uint32_t key = order_key(v);
+        const bool c = key >= lower;
+        const uint64_t bal = __ballot(c);
+        if (bal) {  // one atomic per wave and element slot
+          const int leader = __builtin_ctzll(bal);
+          int base = 0;
+          if (lane == leader) base = atomicAdd(&s_ncand, __builtin_popcountll(bal));
+          base = __shfl(base, leader);
+          if (c) {
+            const int i = base + __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+            if (i < kCand) {
+              c_key[i] = key;
+              c_val[i] = v;
+            }
+          }
+        }
+      });
+      __syncthreads();
+      use_cand = s_ncand <= kCand;  // else (many ties) the row is used
+      __syncthreads();
+    }
+    if (use_cand) {
+      tau_k = kth(cand_src);
+    } else {
+      tau_k = kth([&](auto&& f) {
+        row_src([&](uint32_t key, float v) {
+          if (key >= lower) f(key, v);
+        });
+      });
+    }
+  }
+
+  // ---- top-p: the last key (descending) whose strictly larger keys hold
+  // less than top_p of the mass kept by top-k ----
+  uint32_t tau_p = 0u;
+  if (top_p < 1.f) {
+    uint32_t prefix = 0u, fixed = 0u;
+    unsigned long long above = 0ull;
+    double target = 0.0;
+    bool whole = false;  // every remaining key is kept
+    auto pass = [&](auto&& src, int sh, int mask) {
+      src([&](uint32_t key, float v) {
+        if (key >= tau_k && (key & fixed) == prefix) {
+          const unsigned long long w = (unsigned long long)(exp2f((v - M) * c2) * kFix);
+          atomicAdd(&hist[(key >> sh) & mask], w);
+        }
+      });
+    };
+    for (int g = 0; g < kDigits && !whole; ++g) {
+      const int sh = shifts[g], mask = (1 << widths[g]) - 1;
+      clear();
+      if (use_cand)
+        pass(cand_src, sh, mask);
+      else
+        pass(row_src, sh, mask);
+      __syncthreads();
+      // the first digit's histogram holds the whole kept mass: target = top_p * it
+      if (wave == 0)
+        select_bin(hist, mask + 1, above, target, g == 0 ? (double)top_p : 0.0, &s_sel, &s_above,
+                   &s_total);
+      __syncthreads();
+      if (g == 0) target = (double)top_p * (double)s_total;
+      if (s_sel < 0) {
+        whole = true;  // rounding: the range holds less than the target, keep it all
+      } else {
+        prefix |= (uint32_t)s_sel << sh;
+        fixed |= (uint32_t)mask << sh;
+        above = s_above;
+      }
+      __syncthreads();
+    }
+    tau_p = prefix;
+  }
+  if (t == 0) {
+    const bool any = (top_k > 0 && (int64_t)top_k < vocab) || top_p < 1.f;
+    tau[row] = any ? key_value(tau_k > tau_p ? tau_k : tau_p) : -INFINITY;
   }
 }
 
@@ -1210,9 +1396,12 @@ int sel_slices(int64_t vocab, size_t elem) {
 
 // workspace: chunk statistics, thresholds, the slices' top-k candidates,
 // then the spread selection's slice maxima, histograms and states
-size_t sel_offset(size_t rows, int chunks) {
+int sel_slices_max(int64_t vocab) { return sel_slices(vocab, sizeof(float)); }
+
+size_t sel_offset(size_t rows, int chunks, int64_t vocab) {
   return round256(rows * chunks * sizeof(float2)) + round256(rows * sizeof(float)) +
-         round256(rows * kSlices * (kSliceCand * sizeof(uint32_t) + sizeof(int) + sizeof(float)));
+         round256(rows * sel_slices_max(vocab) *
+                  (kSliceCand * sizeof(uint32_t) + sizeof(int) + sizeof(float)));
 }
 
 }  // namespace
@@ -1228,7 +1417,7 @@ AcceptPlan plan_stochastic(int batch, int n, int64_t vocab) {
   p.chunks = (int)((vocab + chunk - 1) / chunk);
   // chunk statistics, one threshold per row, then the slices' top-k candidates
   const size_t rows = (size_t)batch * n;
-  p.ws_bytes = sel_offset(rows, p.chunks) +
+  p.ws_bytes = sel_offset(rows, p.chunks, vocab) +
                round256(rows * sel_slices(vocab, sizeof(float)) * sizeof(float)) +
                round256(rows * kSelPasses * kBins * sizeof(unsigned long long)) +
                rows * kSelPasses * sizeof(SelState);
@@ -1246,17 +1435,19 @@ void launch_typed(const void* logits, int64_t vocab, int64_t row_stride, int bat
   bool derive = false;
   if (tau) {
     // the slices' candidate buffers follow the thresholds in the workspace
-    char* base = reinterpret_cast<char*>(tau) + (((size_t)rows * sizeof(float) + 255) / 256) * 256;
+    const size_t smax = (size_t)sel_slices_max(vocab);
+    char* base = reinterpret_cast<char*>(tau) + round256((size_t)rows * sizeof(float));
     uint32_t* cand_keys = reinterpret_cast<uint32_t*>(base);
-    int* cand_count = reinterpret_cast<int*>(cand_keys + (size_t)rows * kSlices * kSliceCand);
-    float* slice_max = reinterpret_cast<float*>(cand_count + (size_t)rows * kSlices);
-    if (kTopKCandidates && top_k > 0 && top_k <= kFiltThreads && (int64_t)top_k < vocab) {
-      hipLaunchKernelGGL((filter_threshold_kernel<T, kVector>), dim3(rows, kSlices),
-                         dim3(kFiltThreads), 0, stream, (const T*)logits, vocab, row_stride,
-                         top_k, top_p, c2, tau, 1, cand_keys, cand_count, slice_max);
-      hipLaunchKernelGGL((filter_threshold_kernel<T, kVector>), dim3(rows), dim3(kFiltThreads), 0,
-                         stream, (const T*)logits, vocab, row_stride, top_k, top_p, c2, tau, 2,
+    int* cand_count = reinterpret_cast<int*>(cand_keys + rows * smax * kSliceCand);
+    float* slice_max = reinterpret_cast<float*>(cand_count + rows * smax);
+    const int slices = sel_slices(vocab, sizeof(T));
+    if (top_k > 0 && top_k <= kCandMaxK && (int64_t)top_k < vocab && slices <= kWave) {
+      hipLaunchKernelGGL((cand_collect_kernel<T, kVector>), dim3(slices, rows), dim3(kSelThreads),
+                         0, stream, (const T*)logits, vocab, row_stride, top_k, slices,
                          cand_keys, cand_count, slice_max);
+      hipLaunchKernelGGL((filter_threshold_kernel<T, kVector>), dim3(rows), dim3(kFiltThreads), 0,
+                         stream, (const T*)logits, vocab, row_stride, top_k, top_p, c2, tau,
+                         cand_keys, cand_count, slice_max, slices);
     } else {
       // the spread selection
       constexpr int kDigits = sizeof(T) == 2 ? 2 : 3;
@@ -1269,7 +1460,7 @@ void launch_typed(const void* logits, int64_t vocab, int64_t row_stride, int bat
       sa.np = top_p < 1.f ? kDigits : 0;
       sa.top_p = top_p;
       sa.c2 = c2;
-      char* sel = reinterpret_cast<char*>(stats) + sel_offset(rows, plan.chunks);
+      char* sel = reinterpret_cast<char*>(stats) + sel_offset(rows, plan.chunks, vocab);
       sa.slice_max = reinterpret_cast<float*>(sel);
       sel += round256((size_t)rows * sel_slices(vocab, sizeof(float)) * sizeof(float));
       sa.hist = reinterpret_cast<unsigned long long*>(sel);
