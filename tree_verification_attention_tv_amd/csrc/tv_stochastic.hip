@@ -1153,6 +1153,7 @@ __global__ __launch_bounds__(kWalkThreads) void stochastic_walk_kernel(WalkArgs 
   __shared__ __attribute__((aligned(16))) int s_par[TV_MAX_NODES];
   __shared__ __attribute__((aligned(16))) int s_tok[TV_MAX_NODES];
   __shared__ int s_first[TV_MAX_NODES], s_next[TV_MAX_NODES], s_path[TV_MAX_NODES];
+  __shared__ int s_rank[TV_MAX_NODES];  // node j: sibling rank, bit 30: its token repeats
   __shared__ float s_M[TV_MAX_NODES], s_Z[TV_MAX_NODES];  // row statistics of every node
   __shared__ float s_p[TV_MAX_NODES];  // node j: p_parent(token_j), 0 if invalid or repeated
   __shared__ float s_u[TV_MAX_NODES];  // node j: its acceptance uniform
@@ -1166,87 +1167,109 @@ __global__ __launch_bounds__(kWalkThreads) void stochastic_walk_kernel(WalkArgs 
   const int64_t row0 = (int64_t)b * n;
   const T* logits = reinterpret_cast<const T*>(a.logits);
   if (t == 0) s_bad = 0;
-  // every input of the walk is requested at once: tree, chunk statistics
+  static_assert(kWalkThreads >= 4 * TV_MAX_NODES, "four thread slots per node");
+  // Three jobs on three sets of waves, all started at once.  Threads t < n:
+  // node t's parent and token to LDS, and the logit of its token in its
+  // parent's row (with the parent's threshold) requested; threads 256 + j:
+  // node j's row statistics (M, Z) from its chunk statistics; threads 512 + j:
+  // node j's bonus uniform.
+  float lraw = 0.f, lo_par = -INFINITY;
   int par = 0, tok = 0;
-  float2 st[8];
-  if (t < n) {
-    par = a.parents[row0 + t];
-    tok = a.draft[row0 + t];
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-      if (c < a.chunks) st[c] = a.stats[(row0 + t) * a.chunks + c];
-  }
-  __syncthreads();
-  static_assert(kWalkThreads >= TV_MAX_NODES, "one thread per node slot");
   if (t < TV_MAX_NODES) {
+    if (t < n) {
+      par = a.parents[row0 + t];
+      tok = a.draft[row0 + t];
+      s_first[t] = INT_MAX;
+      const bool ok = t == 0 ? par == -1 : (par >= 0 && par < t);
+      if (!ok) s_bad = 1;
+      // clamped indices: the load is in bounds whatever the tree holds
+      const int pc = t > 0 && par >= 0 && par < t ? par : 0;
+      const int64_t tc = tok >= 0 && (int64_t)tok < a.vocab ? tok : 0;
+      lraw = to_f32<T>(logits[(row0 + pc) * a.row_stride + tc]);
+      if (a.tau) lo_par = a.tau[row0 + pc];
+    }
     s_par[t] = t < n ? par : -2;  // slots past n match no parent
     s_tok[t] = tok;
-  }
-  if (t < n) {
-    s_first[t] = INT_MAX;
-    const bool ok = t == 0 ? par == -1 : (par >= 0 && par < t);
-    if (!ok) s_bad = 1;
-    // row statistics (M, Z) of node t's row
-    float m = -INFINITY;
+  } else if (t < 2 * TV_MAX_NODES) {
+    const int j = t - TV_MAX_NODES;
+    if (j < n) {
+      const float2* sr = a.stats + (row0 + j) * a.chunks;
+      float2 st[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-      if (c < a.chunks) m = fmaxf(m, st[c].x);
-    for (int c = 8; c < a.chunks; ++c) m = fmaxf(m, a.stats[(row0 + t) * a.chunks + c].x);
-    float z = 0.f;
+      for (int c = 0; c < 8; ++c)
+        if (c < a.chunks) st[c] = sr[c];
+      float m = -INFINITY;
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-      if (c < a.chunks) z += st[c].y * exp2f((st[c].x - m) * a.c2);
-    for (int c = 8; c < a.chunks; ++c) {
-      const float2 sc = a.stats[(row0 + t) * a.chunks + c];
-      z += sc.y * exp2f((sc.x - m) * a.c2);
+      for (int c = 0; c < 8; ++c)
+        if (c < a.chunks) m = fmaxf(m, st[c].x);
+      for (int c = 8; c < a.chunks; ++c) m = fmaxf(m, sr[c].x);
+      float z = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        if (c < a.chunks) z += st[c].y * exp2f((st[c].x - m) * a.c2);
+      for (int c = 8; c < a.chunks; ++c) z += sr[c].y * exp2f((sr[c].x - m) * a.c2);
+      s_M[j] = m;
+      s_Z[j] = z;
     }
-    s_M[t] = m;
-    s_Z[t] = z;
+  } else if (t < 3 * TV_MAX_NODES) {
+    const int j = t - 2 * TV_MAX_NODES;
+    if (j < n) s_ub[j] = philox_uniform(a.step, (uint64_t)b, (uint64_t)j, ~0ull, a.k0, a.k1);
   }
   __syncthreads();
   const bool bad = s_bad != 0;
-  // sibling links, sibling rank, the probability of each node's token at its
-  // parent and its uniform -- all nodes in parallel
-  if (t < n && t > 0 && !bad) {
-    atomicMin(&s_first[par], t);
-    // siblings before t (rank, repeated token) and the next sibling, 16
-    // slots per batch of 16-byte LDS reads
-    int nx = INT_MAX, rank = 0;
-    bool repeated = false;
-    for (int j0 = 0; j0 < n; j0 += 16) {
-      int4 pp[4], tt[4];
+  // Sibling links, rank and repeated tokens, four threads per node: thread
+  // 4t + q scans the 16-slot blocks q, q + 4, ... of the tree (16-byte LDS
+  // reads) for node t; the quad combines its counts and its first later
+  // sibling.
+  if (!bad && t < 4 * n) {
+    const int nt = t >> 2, q = t & 3;
+    const int pt = s_par[nt], kt = s_tok[nt];
+    int nx = INT_MAX, rank = 0, rep = 0;
+    if (nt > 0) {
+      for (int j0 = 16 * q; j0 < n; j0 += 64) {
+        int4 pp[4], tt[4];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        pp[q4] = *reinterpret_cast<const int4*>(&s_par[j0 + 4 * q4]);
-        tt[q4] = *reinterpret_cast<const int4*>(&s_tok[j0 + 4 * q4]);
-      }
+        for (int q4 = 0; q4 < 4; ++q4) {
+          pp[q4] = *reinterpret_cast<const int4*>(&s_par[j0 + 4 * q4]);
+          tt[q4] = *reinterpret_cast<const int4*>(&s_tok[j0 + 4 * q4]);
+        }
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int j = j0 + e;
-        const int pj = e % 4 == 0 ? pp[e / 4].x : e % 4 == 1 ? pp[e / 4].y
-                     : e % 4 == 2 ? pp[e / 4].z : pp[e / 4].w;
-        const int tj = e % 4 == 0 ? tt[e / 4].x : e % 4 == 1 ? tt[e / 4].y
-                     : e % 4 == 2 ? tt[e / 4].z : tt[e / 4].w;
-        // arithmetic, not short-circuit logic: no branches per slot
-        const int before = (pj == par) & (j < t);
-        const int after = (pj == par) & (j > t);
-        rank += before;
-        repeated |= (before & (tj == tok)) != 0;
-        nx = min(nx, after ? j : INT_MAX);
+        for (int e = 0; e < 16; ++e) {
+          const int j = j0 + e;
+          const int pj = e % 4 == 0 ? pp[e / 4].x : e % 4 == 1 ? pp[e / 4].y
+                       : e % 4 == 2 ? pp[e / 4].z : pp[e / 4].w;
+          const int tj = e % 4 == 0 ? tt[e / 4].x : e % 4 == 1 ? tt[e / 4].y
+                       : e % 4 == 2 ? tt[e / 4].z : tt[e / 4].w;
+          // arithmetic, not short-circuit logic: no branches per slot
+          const int before = (pj == pt) & (j < nt);
+          const int after = (pj == pt) & (j > nt);
+          rank += before;
+          rep |= before & (tj == kt);
+          nx = min(nx, after ? j : INT_MAX);
+        }
       }
     }
-    s_next[t] = nx;
-    const bool valid = tok >= 0 && (int64_t)tok < a.vocab && !repeated;
-    const float l = valid ? to_f32<T>(logits[(row0 + par) * a.row_stride + tok]) : 0.f;
-    const float lo = a.tau ? a.tau[row0 + par] : -INFINITY;  // filtered out below lo
-    s_p[t] = valid && l >= lo ? exp2f((l - s_M[par]) * a.c2) / s_Z[par] : 0.f;
-    s_u[t] = philox_uniform(a.step, (uint64_t)b, (uint64_t)par, (uint64_t)rank, a.k0, a.k1);
+#pragma unroll
+    for (int m = 1; m <= 2; m <<= 1) {
+      rank += __shfl_xor(rank, m);
+      rep |= __shfl_xor(rep, m);
+      nx = min(nx, __shfl_xor(nx, m));
+    }
+    if (q == 0 && nt > 0) {
+      atomicMin(&s_first[pt], nt);
+      s_next[nt] = nx;
+      s_rank[nt] = rank | (rep << 30);
+    }
   }
-  // the bonus uniforms on other waves (other SIMDs) than the acceptance ones:
-  // node j's on thread (j + 128) mod 256
-  {
-    const int j = t - 512;  // waves 8.. (other SIMD slots than the acceptance draws)
-    if (j >= 0 && j < n) s_ub[j] = philox_uniform(a.step, (uint64_t)b, (uint64_t)j, ~0ull, a.k0, a.k1);
+  __syncthreads();
+  // the probability of each node's token at its parent and its uniform
+  if (t < n && t > 0 && !bad) {
+    const int rr = s_rank[t];
+    const int rank = rr & ((1 << 30) - 1);
+    const bool repeated = (rr >> 30) != 0;
+    const bool valid = tok >= 0 && (int64_t)tok < a.vocab && !repeated;
+    s_p[t] = valid && lraw >= lo_par ? exp2f((lraw - s_M[par]) * a.c2) / s_Z[par] : 0.f;
+    s_u[t] = philox_uniform(a.step, (uint64_t)b, (uint64_t)par, (uint64_t)rank, a.k0, a.k1);
   }
   __syncthreads();
   // the walk itself, from LDS
@@ -1331,7 +1354,7 @@ __global__ __launch_bounds__(kWalkThreads) void stochastic_walk_kernel(WalkArgs 
   const float lo_u = a.tau ? a.tau[row] : -INFINITY;
 #pragma unroll
   for (int e = 0; e < kPer; ++e)
-    q[e] = my0 + e < hi && q[e] >= lo_u ? exp2f((q[e] - M) * c2) * inv_z : 0.f;
+    q[e] = my0 + e < hi && q[e] >= lo_u ? __builtin_amdgcn_exp2f((q[e] - M) * c2) * inv_z : 0.f;
   // rejected children's tokens leave the residual
   if (!bad)
     for (int k = s_first[u]; k != INT_MAX; k = s_next[k]) {
