@@ -17,7 +17,7 @@
 //     checking draft[j] == argmax[parent(j)] on every edge; the deepest
 //     accepted node (lowest index on ties) is found with one max-reduction
 //     of depth * 65536 + (65535 - i), and its root path is written out.
-#include "tv_internal.h"
+#include "tv_device.h"
 
 #include <float.h>
 

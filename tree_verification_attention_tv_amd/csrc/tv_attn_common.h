@@ -2,7 +2,7 @@
 // 16-row split kernel and the combine; tv_attn_wide.hip: the 32-row kernel).
 #pragma once
 
-#include "tv_internal.h"
+#include "tv_device.h"
 
 #include <math.h>
 

@@ -8,7 +8,7 @@
 // its copy, so with a single layer new_prefix_len may alias prefix_len (with
 // several, another layer's workgroup may start after that write, so the host
 // refuses the alias).  Layer 0 alone reports the (shared) error bits.
-#include "tv_internal.h"
+#include "tv_device.h"
 
 namespace tv {
 namespace {

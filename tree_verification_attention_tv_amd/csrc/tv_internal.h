@@ -116,12 +116,4 @@ hipError_t launch_select(const tv_select_desc& d, const SelectPlan& plan, const 
                          int32_t* n_blocks, float* scores, void* workspace, int32_t* dev_err,
                          hipStream_t stream);
 
-// ---------------------------------------------------------------------------
-// small device helpers
-// ---------------------------------------------------------------------------
-
-__device__ __forceinline__ void raise_err(int32_t* dev_err, int bits) {
-  if (dev_err) atomicOr(dev_err, bits);
-}
-
 }  // namespace tv

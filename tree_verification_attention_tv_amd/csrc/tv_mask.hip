@@ -5,7 +5,7 @@
 // validated first; then thread i walks from node i to the root, setting one
 // bit per visited node in its own LDS row, and the finished [N][W] block is
 // written out with coalesced stores.  N <= 256 keeps a row in 8 words.
-#include "tv_internal.h"
+#include "tv_device.h"
 
 namespace tv {
 namespace {

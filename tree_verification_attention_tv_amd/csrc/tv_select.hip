@@ -25,7 +25,7 @@
 //    the bits in which the candidates' keys differ (11-bit digits, LDS
 //    histograms), equal keys taken in ascending block order; the list is
 //    written ascending with workgroup prefix sums.
-#include "tv_internal.h"
+#include "tv_device.h"
 
 namespace tv {
 namespace {

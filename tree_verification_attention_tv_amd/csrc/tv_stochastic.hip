@@ -44,7 +44,7 @@
 //     finds its chunk from the chunk masses (minus the rejected tokens) and
 //     scans that chunk's logits, loaded with 16-byte loads, with a
 //     workgroup prefix sum.
-#include "tv_internal.h"
+#include "tv_device.h"
 
 #include <limits.h>
 
