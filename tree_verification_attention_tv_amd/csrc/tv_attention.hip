@@ -80,15 +80,19 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
     merge_role<D, kWaves>(a, (int)blockIdx.x - a.nsplit_wg);
     return;
   }
-  // Workgroup -> (split, unit), units varying fastest: with a multiple of 8
-  // units every split of a unit lands on the same XCD (workgroups are dealt
-  // to the XCDs in turn).
-  const int units = a.batch * a.hkv * a.row_groups;
+  // Workgroup -> (split, unit), units varying fastest and (sequence, kv
+  // head) fastest within a unit: with a multiple of 8 of them every split and
+  // every row group of a (sequence, kv head) lands on the same XCD
+  // (workgroups are dealt to the XCDs in turn), so the row groups reading one
+  // K/V chunk share its L2 lines.
+  const int bgs = a.batch * a.hkv;
+  const int units = bgs * a.row_groups;
   const int unit = (int)blockIdx.x % units;
   const int s = (int)blockIdx.x / units;
-  const int b = unit / (a.hkv * a.row_groups);
-  const int g = (unit / a.row_groups) % a.hkv;
-  const int rg = unit % a.row_groups;
+  const int bg = unit % bgs;
+  const int b = bg / a.hkv;
+  const int g = bg % a.hkv;
+  const int rg = unit / bgs;
   {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -750,7 +754,7 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
 done:
   // (every path of the split work ends here: the signal below counts the
   // workgroup's partials, empty ones included)
-  if (a.sync) split_done(a, unit / a.row_groups);
+  if (a.sync) split_done(a, bg);
 }
 
 

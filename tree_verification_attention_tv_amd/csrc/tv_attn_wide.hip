@@ -93,15 +93,18 @@ void attn_wide_kernel(AttnArgs a) {
 
   // ---- split role -----------------------------------------------------------
   auto split_role = [&]() {
-    // Workgroup -> (split, unit): units vary fastest, so with a multiple of 8
-    // units every split of a unit runs on the same XCD (workgroups are dealt
-    // to the 8 XCDs round robin) and shares its L2 for Q and the tree.
-    const int units = a.batch * a.hkv * a.row_groups;
+    // Workgroup -> (split, unit): units vary fastest and (sequence, kv head)
+    // fastest within a unit, so with a multiple of 8 of them every split and
+    // row group of a (sequence, kv head) runs on the same XCD (workgroups are
+    // dealt to the 8 XCDs round robin) and shares its L2 for Q, the tree and
+    // the K/V chunks its row groups both read.
+    const int bgs = a.batch * a.hkv;
+    const int units = bgs * a.row_groups;
     const int unit = blockIdx.x % units;
     const int s = blockIdx.x / units;
-    const int rg = unit % a.row_groups;
-    const int g = (unit / a.row_groups) % a.hkv;
-    const int b = unit / (a.row_groups * a.hkv);
+    const int rg = unit / bgs;
+    const int g = (unit % bgs) % a.hkv;
+    const int b = (unit % bgs) / a.hkv;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -802,7 +805,7 @@ void attn_wide_kernel(AttnArgs a) {
 
   };
   split_role();
-  if (a.sync) split_done(a, (int)(blockIdx.x % (a.batch * a.hkv * a.row_groups)) / a.row_groups);
+  if (a.sync) split_done(a, (int)(blockIdx.x % (a.batch * a.hkv * a.row_groups)) % (a.batch * a.hkv));
 }
 
 template <int D, int RT>
