@@ -130,7 +130,8 @@ tv_status tv_build_tree_mask(const int32_t* parents, int32_t batch, int32_t n_no
  *   out      bf16 [batch][n_nodes][n_q_heads][head_dim]
  *   lse      fp32 [batch][n_nodes][n_q_heads] or NULL
  * Supported: head_dim 64 or 128, n_q_heads % n_kv_heads == 0,
- *   n_nodes * (n_q_heads / n_kv_heads) <= 1024.
+ *   n_nodes * (n_q_heads / n_kv_heads) <= 1024, batch * n_nodes * n_q_heads
+ *   below 2^31 (query rows are indexed in 32 bits).
  * Fallbacks: a block that is invalid is skipped (TV_DERR_BAD_BLOCK); a
  *   prefix_len outside [0, min(cache_capacity, max_prefix_len)] is clamped to
  *   that range (TV_DERR_BAD_PREFIX); a row that sees no key at all (possible

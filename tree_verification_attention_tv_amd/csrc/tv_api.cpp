@@ -57,6 +57,7 @@ tv_status check_attn_desc(const tv_attn_desc* d) {
     return TV_ERR_SHAPE;
   if (d->head_dim != 64 && d->head_dim != 128) return TV_ERR_UNSUPPORTED;
   if ((int64_t)d->n_nodes * (d->n_q_heads / d->n_kv_heads) > 1024) return TV_ERR_UNSUPPORTED;
+  if ((int64_t)d->batch * d->n_nodes * d->n_q_heads > INT_MAX) return TV_ERR_UNSUPPORTED;
   if (d->cache_capacity < 0) return TV_ERR_SHAPE;
   if (d->max_blocks < 0 || d->num_splits < 0 || d->num_splits > 4096) return TV_ERR_SHAPE;
   if (d->tree_placement < TV_TREE_AUTO || d->tree_placement > TV_TREE_IN_LAST_SPLIT ||

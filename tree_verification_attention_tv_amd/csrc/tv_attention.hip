@@ -758,13 +758,19 @@ done:
 }
 
 
-// One wave per row (combine_rows in tv_attn_common.h).
-template <int D>
+// The merge of the split partials (combine_rows in tv_attn_common.h), NR
+// rows per wave (rows (b * n + i) * hq + h): with few partials per row
+// (NR = 4 when there are at most 8) every wave still has several loads in
+// flight, and one round of waves covers the rows.
+template <int D, int NR>
 __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
-  const int64_t rowid = (int64_t)blockIdx.x * (kThreads / 64) + threadIdx.x / 64;  // (b * n + i) * hq + h
-  if (rowid >= (int64_t)a.batch * a.n * a.hq) return;
-  const int64_t ids[1] = {rowid};
-  combine_rows<D, 1, false>(a, ids, threadIdx.x & 63);
+  const int64_t rows_total = (int64_t)a.batch * a.n * a.hq;
+  const int64_t r0 = ((int64_t)blockIdx.x * (kThreads / 64) + threadIdx.x / 64) * NR;
+  if (r0 >= rows_total) return;
+  int64_t ids[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) ids[r] = r0 + r < rows_total ? r0 + r : -1;
+  combine_rows<D, NR, false>(a, ids, threadIdx.x & 63);
 }
 
 template <int D, int RB>
@@ -966,12 +972,21 @@ hipError_t launch_attention(const tv_attn_desc& d, const AttnPlan& plan, const t
     if (e != hipSuccess || merge_in_launch) return e;
   }
 
-  const int64_t rows_total = (int64_t)d.batch * d.n_nodes * d.n_q_heads;  // one wave each
-  const dim3 cgrid((unsigned)((rows_total + kThreads / 64 - 1) / (kThreads / 64)));
-  if (d.head_dim == 128)
-    hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, dim3(kThreads), 0, stream, a);
+  const int64_t rows_total = (int64_t)d.batch * d.n_nodes * d.n_q_heads;
+  const int nr = a.nparts <= 8 ? 4 : 1;  // rows per wave
+  const int64_t per_wg = (int64_t)(kThreads / 64) * nr;
+  const dim3 cgrid((unsigned)((rows_total + per_wg - 1) / per_wg));
+  if (d.head_dim == 128) {
+    if (nr == 4)
+      hipLaunchKernelGGL((attn_combine_kernel<128, 4>), cgrid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_combine_kernel<128, 1>), cgrid, dim3(kThreads), 0, stream, a);
+  } else {
+    if (nr == 4)
+      hipLaunchKernelGGL((attn_combine_kernel<64, 4>), cgrid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_combine_kernel<64, 1>), cgrid, dim3(kThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -231,11 +231,14 @@ __device__ __forceinline__ void combine_rows(const AttnArgs& a, const int64_t (&
   float mx[NR], l[NR], acc[NR][8];
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
-    const int64_t id = rowid[r] < 0 ? 0 : rowid[r];
-    const int h = (int)(id % a.hq);
-    const int64_t bi = id / a.hq;
-    const int i = (int)(bi % a.n);
-    const int b = (int)(bi / a.n);
+    // 32-bit index arithmetic (the row count fits; 64-bit divisions are
+    // long instruction sequences in front of the loads)
+    const uint32_t id = rowid[r] < 0 ? 0u : (uint32_t)rowid[r];
+    const uint32_t bi = id / (uint32_t)a.hq;
+    const int h = (int)(id - bi * (uint32_t)a.hq);
+    const uint32_t bq = bi / (uint32_t)a.n;
+    const int i = (int)(bi - bq * (uint32_t)a.n);
+    const int b = (int)bq;
     const int g = h / a.grp;
     p0[r] = ((int64_t)b * a.nparts * a.hkv + g) * a.rows + i * a.grp + h % a.grp;
     mx[r] = -INFINITY;
