@@ -307,3 +307,47 @@ def test_filtered_sampling_unaligned_rows():
         got = gpu_run(parents, draft, logits, 0.7, (41, 8), 1, "bf16", stride_pad=13, filt=filt)
         assert got[3] == 0
         check_against_oracle(parents, draft, logits, 0.7, (41, 8), 1, got, filt=filt)
+
+
+# The threshold search takes two routes: top-k of at most 32 through per-slice
+# candidate lists (falling back to a whole-row search when a slice has more
+# than 256 candidates), everything else spread over 8192-element slices with
+# one launch per key digit (bf16: two digits, fp32: three).  These cases reach
+# the routes the cases above do not.
+SPREAD_CASES = [
+    # seed, batch, n_nodes, vocab, dtype, temperature, top_k, top_p, lean
+    (51, 2, 24, 70000, "f32", 0.7, 0, 0.9, (3.0, 7.0)),     # fp32 top-p: three mass digits
+    (52, 2, 16, 70000, "f32", 0.8, 200, 0.95, (3.0, 7.0)),  # fp32 count digits, then mass
+    (53, 1, 9, 600000, "bf16", 0.6, 20, 0.95, (3.0, 7.0)),  # 74 slices: top-k 20 spread
+    (54, 2, 12, 9001, "bf16", 1.0, 33, 1.0, (1.0, 3.0)),    # top-k just past the list route
+]
+
+
+@pytest.mark.parametrize("case", SPREAD_CASES, ids=lambda c: f"seed{c[0]}")
+def test_filter_routes_match_oracle(case):
+    seed, batch, n, vocab, dtype, temp, top_k, top_p, lean = case
+    _say(f"[stochastic filtered] route case seed {seed} V {vocab} {dtype} top-k {top_k} "
+         f"top-p {top_p}")
+    parents, draft, logits = W.make_sampling_case(seed, batch=batch, n_nodes=n, vocab=vocab,
+                                                  dtype=dtype, tree="random", lean=lean)
+    got = gpu_run(parents, draft, logits, temp, (seed, 1), 0, dtype, filt=(top_k, top_p))
+    assert got[3] == 0
+    check_against_oracle(parents, draft, logits, temp, (seed, 1), 0, got, filt=(top_k, top_p))
+
+
+def test_filter_heavy_ties_fall_back_to_the_row_search():
+    # rows whose values repeat so often that a slice keeps more than 256
+    # candidates at or above its bound: the per-row workgroup searches the row
+    _say("[stochastic filtered] heavy ties (candidate lists overflow)")
+    rng = np.random.default_rng(61)
+    batch, n, vocab = 2, 10, 20000
+    parents = np.stack([W.random_tree(rng, n) for _ in range(batch)]).astype(np.int32)
+    draft = rng.integers(0, vocab, size=(batch, n)).astype(np.int32)
+    # four distinct values, the top one shared by thousands of tokens
+    vals = np.array([2.0, 1.0, 0.5, -1.0], dtype=np.float32)
+    x = vals[rng.integers(0, 4, size=(batch * n, vocab))]
+    logits = W.f32_to_bf16_bits(x).reshape(batch, n, vocab)
+    for filt in ((20, 1.0), (20, 0.95), (5, 0.5)):
+        got = gpu_run(parents, draft, logits, 0.9, (61, 2), 0, "bf16", filt=filt)
+        assert got[3] == 0
+        check_against_oracle(parents, draft, logits, 0.9, (61, 2), 0, got, filt=filt)
