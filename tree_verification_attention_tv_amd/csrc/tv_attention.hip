@@ -592,16 +592,21 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
       TV_SCHED_FENCE;
     };
     // R(s): the operand reads of M(s) and the mask of S(s): LDS work and
-    // little VALU.
+    // little VALU.  The wave runs it at raised priority, so that its reads
+    // issue ahead of the other wave's softmax on the same SIMD (measured on
+    // MI355X: 5 % off the 60000-token prefix, neutral at one row block).
     auto R = [&](int s, f32x4 (&cur)[2][RB]) {
+      __builtin_amdgcn_s_setprio(1);
       read_k(s);
       read_v(s);
       TV_SCHED_FENCE;
       mask_tile(s, cur);
       TV_SCHED_FENCE;
+      __builtin_amdgcn_s_setprio(0);
     };
     // M(s): the softmax of S(s) interleaved with the QK products of tile s+1
-    // (one MFMA, then a few VALU instructions that issue while it runs), then
+    // (one MFMA, then up to six VALU instructions that issue while it runs;
+    // six measured ~1.5 % faster than four at the 60000-token prefix), then
     // the PV products of tile s.  The QK of the tile after the last one reads
     // whatever its slot holds; its result is never used.
     auto M = [&](auto track_tag, f32x4 (&cur)[2][RB], f32x4 (&nxt)[2][RB]) {
@@ -612,7 +617,7 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
 #pragma unroll
       for (int i = 0; i < 2 * RB * DC; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);  // VALU incl. transcendental
+        __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);  // VALU incl. transcendental
       }
       TV_SCHED_FENCE;
       pv();
