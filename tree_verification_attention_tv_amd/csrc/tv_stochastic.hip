@@ -12,23 +12,26 @@
 // logits, then top-p keeps, of those, the tokens whose strictly larger ones
 // hold less than p of their mass, and the kept probabilities are
 // renormalised.  Both keep every token at or above a logit threshold tau, so
-// the filter is one value per row.  Drafts are point masses: at an accepted node the children are tried in ascending node
-// index, child c (token x) is accepted with probability p_u(x) / R, R the
-// mass not yet rejected at u (a token already rejected at u has probability
-// 0).  When every child is rejected the bonus token is drawn from the
-// residual by inverse CDF in vocabulary order.
+// the filter is one value per row.  Drafts are point masses: at an accepted
+// node the children are tried in ascending node index, child c (token x) is
+// accepted with probability p_u(x) / R, R the mass not yet rejected at u (a
+// token already rejected at u has probability 0).  When every child is
+// rejected the bonus token is drawn from the residual by inverse CDF in
+// vocabulary order.
 //
 // Kernels:
 //  0. the filter's threshold tau (only with a filter), by radix selection
 //     over order-preserving 32-bit keys of the logits (11-bit digits,
 //     histograms in LDS): top-k by counts, then top-p by masses 2^((l - M) c)
 //     in 2^-40 fixed point (integer sums, so the result does not depend on
-//     the order of the atomics).  Top-k of at most 1024 goes through
-//     candidate lists: filter_threshold_kernel over four slices per row keeps
-//     each slice's elements at or above a lower bound of its top-k, then one
-//     workgroup per row selects among them.  Otherwise the selection is
-//     spread over 8192-element slices (sel_*_kernel): a launch per digit,
-//     each adding its slices' histograms into the row's in global memory.
+//     the order of the atomics).  Top-k of at most 32 goes through
+//     candidate lists: cand_collect_kernel, over 8192-element slices, keeps
+//     each slice's elements at or above a lower bound of its top-k, then
+//     filter_threshold_kernel, one workgroup per row, selects among them (or
+//     searches the whole row when ties overflow a list).  Otherwise the
+//     selection is spread over the same slices (sel_*_kernel): a launch per
+//     digit, each adding its slices' histograms into the row's in global
+//     memory.
 //  1. softmax_stats_kernel: one workgroup per (row chunk, logits row), the
 //     same streaming layout as the greedy argmax: each thread's 16-byte loads
 //     are all in flight at once.  Per chunk it writes (m, s): the chunk's max
@@ -38,9 +41,10 @@
 //     here from its last histogram).  HBM-bound: the B*N*V logits are read
 //     once.
 //  2. stochastic_walk_kernel: one workgroup per sequence.  Every input of
-//     the walk is fetched in parallel first: each node's row statistics
-//     (M, Z), the probability of its draft token at its parent and its
-//     uniform.  One thread then walks the tree out of LDS.  The bonus draw
+//     the walk is fetched in parallel first, on separate waves: each node's
+//     row statistics (M, Z), the probability of its draft token at its
+//     parent (after a sibling scan four threads per node) and its uniform.
+//     One thread then walks the tree out of LDS.  The bonus draw
 //     finds its chunk from the chunk masses (minus the rejected tokens) and
 //     scans that chunk's logits, loaded with 16-byte loads, with a
 //     workgroup prefix sum.
