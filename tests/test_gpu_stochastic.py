@@ -351,3 +351,23 @@ def test_filter_heavy_ties_fall_back_to_the_row_search():
         got = gpu_run(parents, draft, logits, 0.9, (61, 2), 0, "bf16", filt=filt)
         assert got[3] == 0
         check_against_oracle(parents, draft, logits, 0.9, (61, 2), 0, got, filt=filt)
+
+
+def test_masked_vocabulary_tail():
+    # a padded vocabulary: the last 1000 logits of every row are -inf (never
+    # kept, never drawn, never counted as mass) on every route
+    _say("[stochastic] -inf logits in every row")
+    parents, draft, logits = W.make_sampling_case(71, batch=2, n_nodes=20, vocab=20000,
+                                                  dtype="f32", tree="random", lean=(3.0, 7.0))
+    masked = logits.copy()
+    masked[:, :, -1000:] = -np.inf
+    # the oracle takes finite logits only: -1e4 has the same order and, at
+    # this temperature, an fp64 probability of exactly 0
+    finite = logits.copy()
+    finite[:, :, -1000:] = -1e4
+    for filt in (None, (20, 0.95), (0, 0.9), (500, 1.0)):
+        got = gpu_run(parents, draft, masked, 0.8, (71, 3), 0, "f32", filt=filt)
+        assert got[3] == 0
+        assert np.all(got[2] < 19000), "a masked token was drawn"
+        check_against_oracle(parents, draft, finite, 0.8, (71, 3), 0, got,
+                             filt=(0, 1.0) if filt is None else filt)
