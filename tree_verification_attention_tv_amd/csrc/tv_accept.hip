@@ -13,8 +13,10 @@
 //     result does not depend on the reduction order.  Partials go to the
 //     workspace.  This is the HBM-bound part (B*N*V logits).
 //  2. path_walk_kernel: one workgroup per sequence.  Thread i finishes row
-//     i's argmax from the partials, then walks from node i to the root
-//     checking draft[j] == argmax[parent(j)] on every edge; the deepest
+//     i's argmax from the partials and tests its own edge,
+//     draft[i] == argmax[parent(i)]; the result is packed with the parent
+//     index in LDS.  Then thread i walks from node i to the root, one LDS
+//     read per level, and stops at the first rejected edge; the deepest
 //     accepted node (lowest index on ties) is found with one max-reduction
 //     of depth * 65536 + (65535 - i), and its root path is written out.
 #include "tv_device.h"
@@ -116,6 +118,17 @@ __device__ __forceinline__ int wave_min_i(int x) {
   x = min((int)a[0], (int)a[1]);
   const auto b = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
   return min((int)b[0], (int)b[1]);
+}
+
+__device__ __forceinline__ unsigned wave_max_u(unsigned x) {
+  x = max(x, (unsigned)dpp_i<0x128>((int)x));
+  x = max(x, (unsigned)dpp_i<0x124>((int)x));
+  x = max(x, (unsigned)dpp_i<0x122>((int)x));
+  x = max(x, (unsigned)dpp_i<0x121>((int)x));
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = max(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return max(b[0], b[1]);
 }
 
 template <typename T>
@@ -246,7 +259,7 @@ __global__ __launch_bounds__(kThreads) void path_walk_kernel(
   __shared__ int s_path[TV_MAX_NODES];
   __shared__ int s_prefix, s_ok;
   __shared__ int amax[TV_MAX_NODES];
-  __shared__ int dtok[TV_MAX_NODES];
+  __shared__ int link[TV_MAX_NODES];  // node j: its parent (low 16 bits), its edge accepted (bit 16)
   __shared__ int bad;
   __shared__ unsigned red[kThreads / kWave];
 
@@ -259,10 +272,12 @@ __global__ __launch_bounds__(kThreads) void path_walk_kernel(
   if (i == 0) bad = 0;
   __syncthreads();
   int p_commit = 0;  // the commit's prefix length, loaded with the partials
+  int my_par = -1, my_tok = 0;
   if (i < n) {
     const int64_t row = (int64_t)b * n + i;
     const int p = parents[row];
-    const int dt = draft[row];
+    my_par = p;
+    my_tok = draft[row];
     if (i == 0 && cm.k_cache) p_commit = cm.prefix_len[b];
     // chunk partials in groups of 8, all loads of a group in flight at once
     float bv = -INFINITY;
@@ -286,33 +301,39 @@ __global__ __launch_bounds__(kThreads) void path_walk_kernel(
     amax[i] = bi;
     if (lead) target_argmax[row] = bi;
     par[i] = p;
-    dtok[i] = dt;
     const bool ok = (i == 0) ? (p == -1) : (p >= 0 && p < i);
     if (!ok) bad = 1;
   }
   __syncthreads();
 
+  // Each edge is tested once (node i's token against its parent's argmax)
+  // and its result packed with the parent index, so that the up-walks below
+  // take one LDS read per level.
+  const bool edge = i < n && (i == 0 || (!bad && my_tok == amax[my_par]));
+  if (i < n && !bad) link[i] = (i == 0 ? 0 : my_par) | ((int)edge << 16);
+  __syncthreads();
   // key = depth << 16 | (0xFFFF - i) for accepted nodes, 0 otherwise; the
-  // root is always accepted so the maximum is never 0.
+  // root is always accepted so the maximum is never 0.  A node is accepted
+  // when every edge on its root path is; the walk stops at the first
+  // rejected one (parents precede children, so it always ends).
   unsigned key = 0;
   if (i < n) {
     if (bad) {
       key = (i == 0) ? 0xFFFFu : 0u;
     } else {
-      bool acc = true;
-      int d = 0;
-      for (int j = i; par[j] >= 0; j = par[j]) {
-        acc = acc && (dtok[j] == amax[par[j]]);
+      bool acc = edge;
+      int d = i > 0 ? 1 : 0;
+      int j = i > 0 ? my_par : 0;
+      while (acc && j > 0) {
+        const int w = link[j];
+        acc = (w >> 16) != 0;
+        j = w & 0xFFFF;
         ++d;
       }
       if (acc) key = ((unsigned)d << 16) | (unsigned)(0xFFFF - i);
     }
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const unsigned o = __shfl_xor(key, off);
-    key = o > key ? o : key;
-  }
+  key = wave_max_u(key);
   if ((i & (kWave - 1)) == 0) red[i / kWave] = key;
   __syncthreads();
   unsigned best = red[0];
