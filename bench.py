@@ -1046,8 +1046,12 @@ def counter_summary(dirs, match="attn_", cus=256, simds_per_cu=4, shader_engines
     # per (pass, kernel, counter): the dispatch sums, averaged; a counter
     # read in several passes is averaged over them
     per = {}
+    # per kernel: (SQ_BUSY_CYCLES / shader engines, dispatch ns) of each
+    # dispatch, from the same pass (its own start and end timestamps)
+    clock = {}
     for d in dirs:
         one = {}
+        span = {}
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             with open(f) as fh:
                 for row in csv.DictReader(fh):
@@ -1056,10 +1060,17 @@ def counter_summary(dirs, match="attn_", cus=256, simds_per_cu=4, shader_engines
                     k = short_name(row["Kernel_Name"], keep_template=True)
                     c = one.setdefault(k, {}).setdefault(row["Counter_Name"], {})
                     c[row["Dispatch_Id"]] = c.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+                    if "Start_Timestamp" in row:
+                        span[(k, row["Dispatch_Id"])] = (int(row["End_Timestamp"])
+                                                         - int(row["Start_Timestamp"]))
         for k, cs in one.items():
             for n, v in cs.items():
                 if v:
                     per.setdefault(k, {}).setdefault(n, []).append(sum(v.values()) / len(v))
+            for disp, cyc in cs.get("SQ_BUSY_CYCLES", {}).items():
+                ns = span.get((k, disp), 0)
+                if ns > 0:
+                    clock.setdefault(k, []).append((cyc / shader_engines, ns))
     print(f"source_sha256_16: {source_hash()}")
     print("counter averages per dispatch; ratios below each kernel")
     simds = cus * simds_per_cu
@@ -1072,6 +1083,11 @@ def counter_summary(dirs, match="attn_", cus=256, simds_per_cu=4, shader_engines
         mfma = avg.get("SQ_VALU_MFMA_BUSY_CYCLES")
         if cyc:
             print(f"  dispatch_cycles                  {cyc:16.1f}")
+        if clock.get(k):
+            # shader clock while the dispatch ran: its busy cycles over its
+            # own duration (median over dispatches)
+            ghz = sorted(c / ns for c, ns in clock[k])[len(clock[k]) // 2]
+            print(f"  shader_clock_ghz (median)        {ghz:16.3f}")
         if mfma is not None and cyc:
             print(f"  mfma_busy_frac (of SIMD cycles)  {mfma / (simds * cyc):16.4f}")
         if mfma is not None and avg.get("SQ_BUSY_CU_CYCLES"):
