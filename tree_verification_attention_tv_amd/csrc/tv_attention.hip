@@ -770,9 +770,8 @@ done:
 
 
 // The merge of the split partials (combine_rows in tv_attn_common.h), NR
-// rows per wave (rows (b * n + i) * hq + h): with few partials per row
-// (NR = 4 when there are at most 8) every wave still has several loads in
-// flight, and one round of waves covers the rows.
+// rows per wave (rows (b * n + i) * hq + h), its lanes splitting each row's
+// partials; launched with NR = 1 for rows with more than 8 partials.
 template <int D, int NR>
 __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
   const int64_t rows_total = (int64_t)a.batch * a.n * a.hq;
@@ -782,6 +781,70 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
 #pragma unroll
   for (int r = 0; r < NR; ++r) ids[r] = r0 + r < rows_total ? r0 + r : -1;
   combine_rows<D, NR, false>(a, ids, threadIdx.x & 63);
+}
+
+// The merge for rows with at most KMAX partials: lane r * C + c of a wave
+// (C = D / 8) owns the 8 output elements of chunk c of row r, so a wave
+// covers 64 / C rows.  Each lane loads that chunk of every partial of its
+// row at once (indices clamped to the last partial, so every load is in
+// bounds and none waits on a branch), then merges them in partial order:
+// m = max_s m_s, w_s = 2^(m_s - m) l_s, o = sum_s w_s o_s / sum_s w_s,
+// lse = (m + log2 sum_s w_s) ln 2.  No value crosses lanes.  An empty
+// partial (m = -inf) weighs 0 and its output is not used.
+template <int D, int KMAX>
+__global__ __launch_bounds__(kThreads) void attn_combine_lane_kernel(AttnArgs a) {
+  constexpr int C = D / 8;
+  constexpr int RPW = kWave / C;  // rows per wave
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = lane / C, c = lane % C;
+  const int64_t rows_total = (int64_t)a.batch * a.n * a.hq;
+  const int64_t row = ((int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave) * RPW + r;
+  if (row >= rows_total) return;  // per lane: nothing below crosses lanes
+  // row = (b * n + i) * hq + h; partial rows of (b, split, g) are consecutive
+  // in m = i * grp + h % grp (32-bit: the descriptor check keeps B·N·Hq < 2^31)
+  const uint32_t id = (uint32_t)row;
+  const uint32_t bi = id / (uint32_t)a.hq;
+  const int h = (int)(id - bi * (uint32_t)a.hq);
+  const uint32_t bq = bi / (uint32_t)a.n;
+  const int i = (int)(bi - bq * (uint32_t)a.n);
+  const int g = h / a.grp;
+  const int64_t p0 = ((int64_t)bq * a.nparts * a.hkv + g) * a.rows + i * a.grp + h % a.grp;
+  const int64_t stride = (int64_t)a.hkv * a.rows;  // partial rows between splits
+  const int cnt = a.nparts;
+  float2 ml[KMAX];
+  bf16x8 ov[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    const int64_t pi = p0 + (int64_t)(k < cnt ? k : cnt - 1) * stride;
+    ml[k] = load_ml<false>(a.part_ml + pi);
+    ov[k] = load_o<false>(a.part_o + pi * D + 8 * c);
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k)
+    if (k < cnt) m = fmaxf(m, ml[k].x);
+  bf16x8 res = bf16x8{};
+  float lse_v = -INFINITY;
+  if (m != -INFINITY) {
+    float l = 0.f, acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      if (k < cnt && ml[k].x != -INFINITY) {
+        const float w = __builtin_amdgcn_exp2f(ml[k].x - m) * ml[k].y;
+        l += w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(w, (float)ov[k][e], acc[e]);
+      }
+    }
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) res[e] = (bf16)(acc[e] * inv);
+    lse_v = (m + log2f(l)) * 0.69314718055994530942f;
+  }
+  *reinterpret_cast<bf16x8*>(a.out + row * D + 8 * c) = res;
+  if (c == 0 && a.lse) a.lse[row] = lse_v;
 }
 
 template <int D, int RB>
@@ -984,20 +1047,33 @@ hipError_t launch_attention(const tv_attn_desc& d, const AttnPlan& plan, const t
   }
 
   const int64_t rows_total = (int64_t)d.batch * d.n_nodes * d.n_q_heads;
-  const int nr = a.nparts <= 8 ? 4 : 1;  // rows per wave
-  const int64_t per_wg = (int64_t)(kThreads / 64) * nr;
-  const dim3 cgrid((unsigned)((rows_total + per_wg - 1) / per_wg));
-  if (d.head_dim == 128) {
-    if (nr == 4)
-      hipLaunchKernelGGL((attn_combine_kernel<128, 4>), cgrid, dim3(kThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL((attn_combine_kernel<128, 1>), cgrid, dim3(kThreads), 0, stream, a);
-  } else {
-    if (nr == 4)
-      hipLaunchKernelGGL((attn_combine_kernel<64, 4>), cgrid, dim3(kThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL((attn_combine_kernel<64, 1>), cgrid, dim3(kThreads), 0, stream, a);
+  if (a.nparts <= 8) {
+    // Few partials per row: one lane per output chunk, all of its row's
+    // partials loaded at once, so the whole grid is one round of waves
+    // (measured on MI355X, per attention call: 11.7 -> 8.0 us for the
+    // 8-node tree over 256 tokens, 42.2 -> 35.1 us for 16 ragged
+    // sequences; with the 9 partials of the 8B layer the 16-partial form
+    // was slower, 14.0 -> 16.5 us, so more partials take the wave-per-row
+    // merge below).
+    const int64_t per_wg = (int64_t)(kThreads / 64) * (64 / (d.head_dim / 8));
+    const dim3 lgrid((unsigned)((rows_total + per_wg - 1) / per_wg));
+    const bool k4 = a.nparts <= 4;
+    if (d.head_dim == 128) {
+      if (k4) hipLaunchKernelGGL((attn_combine_lane_kernel<128, 4>), lgrid, dim3(kThreads), 0, stream, a);
+      else hipLaunchKernelGGL((attn_combine_lane_kernel<128, 8>), lgrid, dim3(kThreads), 0, stream, a);
+    } else {
+      if (k4) hipLaunchKernelGGL((attn_combine_lane_kernel<64, 4>), lgrid, dim3(kThreads), 0, stream, a);
+      else hipLaunchKernelGGL((attn_combine_lane_kernel<64, 8>), lgrid, dim3(kThreads), 0, stream, a);
+    }
+    return hipGetLastError();
   }
+  // one wave per row, its lanes splitting the partials
+  const int64_t per_wg = kThreads / 64;
+  const dim3 cgrid((unsigned)((rows_total + per_wg - 1) / per_wg));
+  if (d.head_dim == 128)
+    hipLaunchKernelGGL((attn_combine_kernel<128, 1>), cgrid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<64, 1>), cgrid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
