@@ -151,10 +151,19 @@ def test_attention_tree_placements(case, placement):
                         tree_placement=placement)
 
 
-@pytest.mark.parametrize("splits", [1, 2, 7, 31])
+@pytest.mark.parametrize("splits", [1, 2, 3, 5, 7, 31])
 def test_attention_split_counts(workloads, splits):
     _say(f"[attention] 8b_layer splits={splits}")
     _run_attention_case(workloads("8b_layer"), label=f"splits{splits}", num_splits=splits)
+
+
+@pytest.mark.parametrize("splits", [1, 3, 6, 12])
+def test_attention_split_counts_d64(splits):
+    """Head dim 64 with 1..13 partials per row: both merge forms (one lane
+    per output chunk up to 8 partials, one wave per row above) at D = 64."""
+    _say(f"[attention] d64 splits={splits}")
+    wl = W.make_random_case(41, batch=2, n_nodes=20, hq=8, hkv=2, d=64, prefix_lens=[900, 517])
+    _run_attention_case(DevWorkload(wl), label=f"d64-splits{splits}", num_splits=splits)
 
 
 def test_attention_explicit_scale(workloads):
