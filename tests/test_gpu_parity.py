@@ -166,6 +166,16 @@ def test_attention_split_counts_d64(splits):
     _run_attention_case(DevWorkload(wl), label=f"d64-splits{splits}", num_splits=splits)
 
 
+@pytest.mark.parametrize("d,splits", [(128, 40), (128, 75), (64, 75)])
+def test_attention_many_partials(d, splits):
+    """Rows with more partials than the merge keeps in flight per lane group
+    (8 per group): 38 splits of 64 tokens, and 75 splits of 32 tokens (two
+    or three rounds of loads at D = 128, two at D = 64)."""
+    _say(f"[attention] d{d} splits={splits}")
+    wl = W.make_random_case(43, batch=2, n_nodes=12, hq=8, hkv=2, d=d, prefix_lens=[2400, 2263])
+    _run_attention_case(DevWorkload(wl), label=f"d{d}-splits{splits}", num_splits=splits)
+
+
 def test_attention_explicit_scale(workloads):
     _say("[attention] explicit scale")
     _run_attention_case(workloads("tiny"), label="scale", scale=0.3)
