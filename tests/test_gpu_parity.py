@@ -126,6 +126,10 @@ ATTN_CASES = [
     (10, 4, 32, 32, 8, 128, [1000, 1600, 1203, 1377], 0, None, "random"),
     (11, 1, 3, 2, 2, 128, [5000], 0, None, "random"),
     (12, 1, 47, 4, 4, 64, [777], 48, 7, "random"),            # bs not a multiple of 32
+    # 280 and 332 rows (a second row group of 24 and 76 rows) with a grid
+    # filled by the prefix splits, full and partial mode
+    (13, 1, 70, 8, 2, 128, [9000], 0, None, "random"),
+    (14, 1, 83, 32, 8, 128, [6000], 32, 160, "random"),       # partial, 5120 listed slots
 ]
 
 
@@ -140,7 +144,7 @@ def test_attention_random(case):
 
 
 @pytest.mark.parametrize("placement", [binding.TREE_IN_LAST_SPLIT, binding.TREE_OWN_WORKGROUP])
-@pytest.mark.parametrize("case", [c for c in ATTN_CASES if c[0] in (2, 3, 4, 8, 10, 12)],
+@pytest.mark.parametrize("case", [c for c in ATTN_CASES if c[0] in (2, 3, 4, 8, 10, 12, 13)],
                          ids=lambda c: f"case{c[0]}")
 def test_attention_tree_placements(case, placement):
     seed, bsz, n, hq, hkv, d, plens, bs, bps, tree = case
@@ -604,7 +608,7 @@ def test_accept_commit_edge_cases(workloads):
         binding.DERR_BAD_PARENT
 
 
-@pytest.mark.parametrize("case", [c for c in ATTN_CASES if c[0] in (3, 4, 5, 6, 8, 12)],
+@pytest.mark.parametrize("case", [c for c in ATTN_CASES if c[0] in (3, 4, 5, 6, 8, 12, 14)],
                          ids=lambda c: f"case{c[0]}")
 def test_fused_mask_random_cases(case):
     # 1 to 4 row groups, empty prefixes, partial mode with ragged blocks
