@@ -59,8 +59,11 @@ constexpr int kThreads = 256;      // combine kernel
 constexpr int kWaves = 8;          // split kernel: 8 waves, two per SIMD
 constexpr int kSplitThreads = kWaves * 64;
 
-template <int D, int RB, bool PARTIAL>
-__global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a) {
+// OCC: waves per SIMD.  2: one workgroup per CU, the ping-pong schedule
+// below.  4: two workgroups per CU (128 VGPRs), a flat schedule with one
+// barrier per tile whose operand-read latency the other waves hide.
+template <int D, int RB, bool PARTIAL, int OCC>
+__global__ __launch_bounds__(kSplitThreads, OCC) void attn_split_kernel(AttnArgs a) {
   constexpr int ROWB = D * 2;               // bytes per row
   constexpr int DC = D / 32;                // k-steps of the QK^T product
   constexpr int DB = D / 16;                // 16-wide output blocks of PV
@@ -662,9 +665,57 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
     lds_barrier();
   };
 
+  // Flat schedule (OCC = 4): per tile, one barrier, then each wave reads
+  // its K operands, runs QK, the softmax, reads its V operands and runs
+  // PV.  Tile t lives in slot t % 4; tiles s+1 and s+2 are in flight while
+  // tile s is used, and tile s+3 is requested once every wave has passed
+  // the barrier of step s (all reads of tile s-1, in slot (s+3) % 4, done).
+  auto run_flat = [&](int skip) {
+#pragma unroll
+    for (int mb = 0; mb < RB; ++mb) {
+      lpart[mb] = 0.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[mb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+      if (t >= skip && t < ntiles) dma_tile(t, t);
+    for (int s = 0; s < ntiles; ++s) {
+      // requests are in tile order: tile s has landed once at most those
+      // of tiles s+1 and s+2 are outstanding
+      if (s + 2 < ntiles) vm_wait<2 * DPT>();
+      else if (s + 1 < ntiles) vm_wait<DPT>();
+      else vm_wait<0>();
+      lds_barrier();
+      if (s + 3 < ntiles && s + 3 >= skip) dma_tile((s + 3) % kRing, s + 3);
+      if (!active) continue;
+      f32x4 sc[2][RB];
+      qk_tile(s % kRing, sc);
+      mask_tile(s, sc);
+      bf16x8 pbl[RB];
+      if (s == 0) {
+#pragma unroll
+        for (int mb = 0; mb < RB; ++mb) pbl[mb] = softmax_block(sc, mb, std::true_type{});
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < RB; ++mb) pbl[mb] = softmax_block(sc, mb, std::false_type{});
+      }
+      const uint32_t va = ring_base + (s % kRing) * SLOT_B;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8 v = vfrag(va, db);
+#pragma unroll
+        for (int mb = 0; mb < RB; ++mb)
+          o[mb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pbl[mb], o[mb][db], 0, 0, 0);
+      }
+    }
+    lds_barrier();
+  };
+
 #pragma unroll
   for (int mb = 0; mb < RB; ++mb) mref[mb] = -INFINITY;
-  run(skip);
+  if constexpr (OCC == 4) run_flat(skip);
+  else run(skip);
 
   // ---- overflow check; exact two-pass recompute when needed --------------
   __shared__ int s_redo;
@@ -719,7 +770,8 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
       }
       lds_barrier();
     }
-    run(0);
+    if constexpr (OCC == 4) run_flat(0);
+    else run(0);
   }
   if (err) raise_err(a.dev_err, err);
 
@@ -847,20 +899,22 @@ __global__ __launch_bounds__(kThreads) void attn_combine_lane_kernel(AttnArgs a)
   if (c == 0 && a.lse) a.lse[row] = lse_v;
 }
 
-template <int D, int RB>
+template <int D, int RB, int OCC>
 void launch_split(const AttnArgs& args, dim3 grid, hipStream_t stream) {
   if (args.max_blocks)
-    hipLaunchKernelGGL((attn_split_kernel<D, RB, true>), grid, dim3(kSplitThreads), 0, stream, args);
+    hipLaunchKernelGGL((attn_split_kernel<D, RB, true, OCC>), grid, dim3(kSplitThreads), 0, stream, args);
   else
-    hipLaunchKernelGGL((attn_split_kernel<D, RB, false>), grid, dim3(kSplitThreads), 0, stream, args);
+    hipLaunchKernelGGL((attn_split_kernel<D, RB, false, OCC>), grid, dim3(kSplitThreads), 0, stream, args);
 }
 
 template <int D>
-void launch_split_rb(int rb, const AttnArgs& args, dim3 grid, hipStream_t stream) {
-  if (rb == 1)
-    launch_split<D, 1>(args, grid, stream);
+void launch_split_rb(int rb, int wg_per_cu, const AttnArgs& args, dim3 grid, hipStream_t stream) {
+  if (rb == 1 && wg_per_cu == 2)
+    launch_split<D, 1, 4>(args, grid, stream);
+  else if (rb == 1)
+    launch_split<D, 1, 2>(args, grid, stream);
   else
-    launch_split<D, 2>(args, grid, stream);
+    launch_split<D, 2, 2>(args, grid, stream);
 }
 
 }  // namespace
@@ -967,15 +1021,27 @@ AttnPlan plan_attention(const tv_attn_desc& d, int cu_count) {
     p.merge_in_launch = true;
     return p;
   }
-  // 16-row MFMA tiles, two workgroups per CU
+  // 16-row MFMA tiles, one workgroup per CU (two waves per SIMD)
   AttnPlan p2 = plan_rows(d, cu_count, 2, &crit2);
   p2.kind = TV_ATTN_KERNEL_SPLIT16;
   set_merge_shape(d, kWaves, 2 * cu_count, &p2);
-  if (p2.row_blocks == 1) return p2;
-  AttnPlan p1 = plan_rows(d, cu_count, 1, &crit1);
+  // One block per wave on the flat schedule, up to two workgroups per CU
+  // (four waves per SIMD).  Measured on MI355X against the plans above
+  // (attention call, same box): alone on its CU the flat schedule is 3-4 %
+  // faster than the ping-pong at one block per wave (8-node tree 8.0 ->
+  // 7.7 us, 8B layer 13.7 -> 13.2 us).  Two workgroups on a CU take about
+  // twice a lone one's time per tile (16 x 32-node batch: 13 tiles in
+  // 33.2 us against 25 in 31.6), i.e. ~1.15 of a two-block tile (60000-token
+  // prefix: 88.7 against 82.5 us at the same tile count), which still wins
+  // where it shortens the longest workgroup enough (83-node tree over 4096
+  // tokens: 7 tiles against 9, 21.4 against 22.6 us).
+  AttnPlan p1 = plan_rows(d, 2 * cu_count, 1, &crit1);
   p1.kind = TV_ATTN_KERNEL_SPLIT16;
+  p1.wg_per_cu = 2;
   set_merge_shape(d, kWaves, 2 * cu_count, &p1);
-  return 13 * crit1 < 20 * crit2 ? p1 : p2;
+  const bool shared = (int64_t)(p1.splits + p1.tree_sep) * d.batch * d.n_kv_heads * p1.row_groups > cu_count;
+  if (p2.row_blocks == 1) return (shared ? 2 * crit1 < crit2 : crit1 <= crit2) ? p1 : p2;
+  return (shared ? 23 * crit1 < 20 * crit2 : 13 * crit1 < 20 * crit2) ? p1 : p2;
 }
 
 hipError_t launch_attention(const tv_attn_desc& d, const AttnPlan& plan, const tv_attn_ptrs& p,
@@ -1039,9 +1105,9 @@ hipError_t launch_attention(const tv_attn_desc& d, const AttnPlan& plan, const t
     if (e != hipSuccess || merge_in_launch) return e;
   } else {
     if (d.head_dim == 128)
-      launch_split_rb<128>(plan.row_blocks, a, dim3(grid), stream);
+      launch_split_rb<128>(plan.row_blocks, plan.wg_per_cu, a, dim3(grid), stream);
     else
-      launch_split_rb<64>(plan.row_blocks, a, dim3(grid), stream);
+      launch_split_rb<64>(plan.row_blocks, plan.wg_per_cu, a, dim3(grid), stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || merge_in_launch) return e;
   }

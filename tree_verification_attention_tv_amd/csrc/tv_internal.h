@@ -31,6 +31,7 @@ struct AttnPlan {
   int tree_sep;      // 1: the tree block has a workgroup of its own (split index `splits`);
                      // 0: it runs in the last non-empty prefix split
   int chunk;         // prefix slots per split (multiple of the 32-token tile)
+  int wg_per_cu;     // 16-row schedule: 2 = one-block waves, four per SIMD; else one workgroup per CU
   int prefix_slots;  // upper bound of prefix slots per sequence
   int kind;          // TV_ATTN_KERNEL_SPLIT16 or TV_ATTN_KERNEL_WIDE
   size_t ws_o_bytes, ws_ml_bytes;
