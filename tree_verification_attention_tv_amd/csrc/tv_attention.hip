@@ -7,12 +7,15 @@
 // proposed tokens multiplies the arithmetic intensity by N).
 //
 // Design (gfx950):
-//  * One workgroup (8 waves, two per SIMD) per (sequence, kv head, row
-//    group, split).  It holds up to 256 query rows of its kv head -- the
-//    n_nodes x group rows -- so each K/V tile is read from HBM once and
-//    reused by all rows (rows FLOP/byte).  Each wave owns RB (1 or 2) blocks
-//    of 16 rows.  Two waves per SIMD are needed to keep the matrix core
-//    busy: a single wave issues dependent-free MFMAs at well under peak.
+//  * One workgroup (8 waves) per (sequence, kv head, row group, split).  It
+//    holds up to 256 query rows of its kv head -- the n_nodes x group rows
+//    -- so each K/V tile is read from HBM once and reused by all rows (rows
+//    FLOP/byte).  Each wave owns RB (1 or 2) blocks of 16 rows.  At least
+//    two waves per SIMD are needed to keep the matrix core busy: a single
+//    wave issues dependent-free MFMAs at well under peak.  Two-block plans
+//    run one workgroup per CU (two waves per SIMD, the ping-pong schedule
+//    below); one-block plans may run two per CU (four waves per SIMD, the
+//    flat schedule, 128 VGPRs).
 //  * The prefix (full rows, or the listed blocks) is cut into `splits`
 //    contiguous ranges, one workgroup each, with `splits` chosen so that the
 //    grid fits the CUs in one round.  The workgroup of the last non-empty
@@ -56,7 +59,7 @@ namespace {
 using namespace attn;
 
 constexpr int kThreads = 256;      // combine kernel
-constexpr int kWaves = 8;          // split kernel: 8 waves, two per SIMD
+constexpr int kWaves = 8;          // split kernel: 8 waves (two or four per SIMD with OCC)
 constexpr int kSplitThreads = kWaves * 64;
 
 // OCC: waves per SIMD.  2: one workgroup per CU, the ping-pong schedule
